@@ -1,0 +1,499 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotated INT4 paged KV-cache hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+kv_rotquant_write of the batch's new tokens (rotation + INT4 quantisation +
+paged store) and kv_int4_paged_decode over the cache (query rotation, page
+walk, de-quantised attention, split-K combine, inverse V rotation).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant ...]
+
+Workloads (sizes of the SAW-INT4 serving shapes; synthetic data):
+  qwen3_4b_like          (default) Hq=32, Hkv=8, 16 sequences of U{1024..4096}
+                         tokens, page 16 scattered, K block 64, V plain; a step
+                         writes every token, then decodes every sequence
+  prefill_chunk          32768-token chunk write, Hkv=8, page 64 scattered;
+                         --variant bdr (K block --k-block) | plain | bf16
+  qwen3_32b_like_decode  Hq=64, Hkv=8, 256 log-normal sequences (~2.94M
+                         tokens), page 16; a step writes 1 token per sequence
+                         and decodes all sequences over L+1
+  long_context           1M-token sequence, Hq=64, Hkv=8, page 64, blocks
+                         128/128; a step is the 64-chunk fill plus one decode
+
+Prints ONE JSON line.  ``value`` is KV tokens/s over the timed steps (tokens
+written plus tokens attended, each token = all KV heads of K and V), wall
+clock between two device synchronisations, inputs already in HBM.  The
+``roofline`` object covers the kernel with the largest share of the step
+time: algorithmic bytes per launch / its mean launch time from HIP events on
+its stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the
+same workload (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+D = 128
+CODE_ROW = 64 + 4            # bytes per (token, head) row in the INT4 cache
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_4b_like", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--variant", default="bdr", choices=["bdr", "plain", "bf16"],
+                    help="prefill_chunk only: fused BDR write, plain INT4 write, or bf16 paged copy")
+    ap.add_argument("--k-block", type=int, default=None, help="override the workload's K block")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also launch one plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--counters", default=None,
+                    help="JSON with FETCH_SIZE/WRITE_SIZE per launch (see --parse-counters)")
+    ap.add_argument("--parse-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    return ap.parse_args(argv)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "int4_kv_cache_rotquant_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ workload setup
+class Setup:
+    """Device buffers and one-step closure for a workload."""
+
+    def __init__(self, args, K, torch):
+        self.args, self.K, self.torch = args, K, torch
+        self.w = W.WORKLOADS[args.workload]()
+        self.dev = "cuda"
+        self.gen = torch.Generator(device=self.dev)
+        self.gen.manual_seed(self.w.seed)
+        self.kernels = {}          # name -> algorithmic bytes per launch
+        getattr(self, "setup_" + args.workload)()
+
+    # -- helpers
+    def rows(self, T, Hkv, out):
+        return W.make_rows_torch(self.gen, T, Hkv, out, self.dev)
+
+    def dev_i32(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(self.dev)
+
+    def write_bytes(self, T, Hkv):
+        return T * (Hkv * 2 * (2 * D + CODE_ROW) + 4)
+
+    def decode_bytes(self, lens, Hkv, Hq, P):
+        lens = np.asarray(lens, np.int64)
+        return int(lens.sum() * Hkv * 2 * CODE_ROW + len(lens) * Hq * (2 * D + 4 * D)
+                   + np.ceil(lens / P).sum() * 4 + len(lens) * 4)
+
+    # -- qwen3_4b_like: write everything, decode every sequence; 3 rotating buffer sets
+    def setup_qwen3_4b_like(self):
+        K, torch, w = self.K, self.torch, self.w
+        kb = self.args.k_block if self.args.k_block is not None else w.k_block
+        self.kb, self.vb = kb, w.v_block
+        T, Hkv, Hq = w.total_tokens, w.num_kv_heads, w.num_q_heads
+        self.sets = []
+        for i in range(3):
+            cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, w.page_size, kb, w.v_block)
+            k, v = self.rows(T, Hkv, w.k_out), self.rows(T, Hkv, w.v_out)
+            q = torch.randn((w.num_seqs, Hq, D), generator=self.gen, device=self.dev).to(torch.bfloat16)
+            self.sets.append((cache, k, v, q))
+        self.slots = self.dev_i32(w.all_slots())
+        self.tab = self.dev_i32(w.paging.page_table())
+        self.lens = self.dev_i32(w.seq_lens)
+        self.maxlen = int(w.seq_lens.max())
+        self.out = torch.empty((w.num_seqs, Hq, D), dtype=torch.float32, device=self.dev)
+        n = K.kv_int4_paged_decode_workspace(self.sets[0][0], w.num_seqs, Hq, self.maxlen,
+                                             self.args.split_tokens)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        self.kernels = {"kv_rotquant_write": self.write_bytes(T, Hkv),
+                        "kv_int4_paged_decode": self.decode_bytes(w.seq_lens, Hkv, Hq, w.page_size)}
+        self.tokens_per_step = T + int(w.seq_lens.sum())
+        self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                       "num_seqs": w.num_seqs, "tokens_written": T,
+                       "tokens_attended": int(w.seq_lens.sum()), "page_size": w.page_size,
+                       "k_block": kb, "v_block": w.v_block}
+
+    def step_qwen3_4b_like(self, i, ev):
+        K = self.K
+        cache, k, v, q = self.sets[i % len(self.sets)]
+        ev[0].record()
+        K.kv_rotquant_write(cache, k, v, self.slots)
+        ev[1].record()
+        K.kv_int4_paged_decode(cache, q, self.tab, self.lens, self.maxlen, out=self.out,
+                               split_tokens=self.args.split_tokens, workspace=self.ws)
+        ev[2].record()
+
+    # -- prefill chunk: one 32768-token write per step; 4 rotating buffer sets
+    def setup_prefill_chunk(self):
+        K, torch, w = self.K, self.torch, self.w
+        kb = self.args.k_block if self.args.k_block is not None else 128
+        variant = self.args.variant
+        if variant == "plain":
+            kb = 0
+        self.kb, self.vb = kb, 0
+        T, Hkv = w.total_tokens, w.num_kv_heads
+        self.sets = []
+        for i in range(4):
+            k, v = self.rows(T, Hkv, w.k_out), self.rows(T, Hkv, w.v_out)
+            if variant == "bf16":
+                shape = (w.paging.num_pages, Hkv, w.page_size, D)
+                cache = (torch.empty(shape, dtype=torch.bfloat16, device=self.dev),
+                         torch.empty(shape, dtype=torch.bfloat16, device=self.dev))
+            else:
+                cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, w.page_size, kb, 0)
+            self.sets.append((cache, k, v))
+        self.slots = self.dev_i32(w.all_slots())
+        self.desc = K.CacheDesc(D, Hkv, w.page_size, w.paging.num_pages, 0, 0)
+        name = "kvrq_bf16_paged_write" if variant == "bf16" else "kv_rotquant_write"
+        nbytes = T * (Hkv * 2 * (2 * D + 2 * D) + 4) if variant == "bf16" else self.write_bytes(T, Hkv)
+        self.kernels = {name: nbytes}
+        self.tokens_per_step = T
+        self.config = {"workload": w.name, "variant": variant, "num_kv_heads": Hkv, "head_dim": D,
+                       "tokens_written": T, "page_size": w.page_size, "k_block": kb, "v_block": 0}
+
+    def step_prefill_chunk(self, i, ev):
+        K = self.K
+        cache, k, v = self.sets[i % len(self.sets)]
+        ev[0].record()
+        if self.args.variant == "bf16":
+            K.kvrq_bf16_paged_write(self.desc, cache[0], cache[1], k, v, self.slots)
+        else:
+            K.kv_rotquant_write(cache, k, v, self.slots)
+        ev[1].record()
+
+    # -- high-concurrency decode: prefix filled untimed; step i writes token L+i, decodes L+i+1
+    def setup_qwen3_32b_like_decode(self):
+        K, torch, w = self.K, self.torch, self.w
+        kb = self.args.k_block if self.args.k_block is not None else w.k_block
+        self.kb, self.vb = kb, w.v_block
+        S, Hkv, Hq, P = w.num_seqs, w.num_kv_heads, w.num_q_heads, w.page_size
+        self.cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, kb, w.v_block)
+        chunk = 1 << 16
+        all_slots = w.all_slots()
+        for s0 in range(0, len(all_slots), chunk):
+            sl = all_slots[s0:s0 + chunk]
+            K.kv_rotquant_write(self.cache, self.rows(len(sl), Hkv, w.k_out),
+                                self.rows(len(sl), Hkv, w.v_out), self.dev_i32(sl))
+        n_steps = w.notes["steps"]
+        self.new_k = [self.rows(S, Hkv, w.k_out) for _ in range(min(n_steps, 8))]
+        self.new_v = [self.rows(S, Hkv, w.v_out) for _ in range(min(n_steps, 8))]
+        self.step_slots = [self.dev_i32([w.paging.slots(s, int(L) + i, 1)[0]
+                                         for s, L in enumerate(w.seq_lens)]) for i in range(n_steps)]
+        self.step_lens = [self.dev_i32(w.seq_lens + i + 1) for i in range(n_steps)]
+        self.q = torch.randn((S, Hq, D), generator=self.gen, device=self.dev).to(torch.bfloat16)
+        self.tab = self.dev_i32(w.paging.page_table())
+        self.maxlen = int(w.seq_lens.max()) + n_steps
+        self.out = torch.empty((S, Hq, D), dtype=torch.float32, device=self.dev)
+        n = K.kv_int4_paged_decode_workspace(self.cache, S, Hq, self.maxlen, self.args.split_tokens)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        mid = w.seq_lens + n_steps // 2
+        self.kernels = {"kv_rotquant_write": self.write_bytes(S, Hkv),
+                        "kv_int4_paged_decode": self.decode_bytes(mid, Hkv, Hq, P)}
+        self.tokens_per_step = S + int(mid.sum())
+        self.n_steps_max = n_steps
+        self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                       "num_seqs": S, "tokens_written": S, "tokens_attended_mid": int(mid.sum()),
+                       "page_size": P, "k_block": kb, "v_block": w.v_block}
+
+    def step_qwen3_32b_like_decode(self, i, ev):
+        K = self.K
+        j = i % self.n_steps_max
+        ev[0].record()
+        K.kv_rotquant_write(self.cache, self.new_k[j % len(self.new_k)], self.new_v[j % len(self.new_v)],
+                            self.step_slots[j])
+        ev[1].record()
+        K.kv_int4_paged_decode(self.cache, self.q, self.tab, self.step_lens[j], self.maxlen,
+                               out=self.out, split_tokens=self.args.split_tokens, workspace=self.ws)
+        ev[2].record()
+
+    # -- long context: 64 chunk writes + one decode
+    def setup_long_context(self):
+        K, torch, w = self.K, self.torch, self.w
+        Hkv, Hq, P, C = w.num_kv_heads, w.num_q_heads, w.page_size, w.notes["chunk"]
+        self.kb, self.vb = w.k_block, w.v_block
+        L = w.total_tokens
+        self.cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, w.k_block, w.v_block)
+        self.chunks_k = [self.rows(C, Hkv, w.k_out) for _ in range(4)]
+        self.chunks_v = [self.rows(C, Hkv, w.v_out) for _ in range(4)]
+        self.chunk_slots = [self.dev_i32(w.paging.slots(0, c * C, C)) for c in range(L // C)]
+        self.q = torch.randn((1, Hq, D), generator=self.gen, device=self.dev).to(torch.bfloat16)
+        self.tab = self.dev_i32(w.paging.page_table())
+        self.lens = self.dev_i32([L])
+        self.out = torch.empty((1, Hq, D), dtype=torch.float32, device=self.dev)
+        n = K.kv_int4_paged_decode_workspace(self.cache, 1, Hq, L, self.args.split_tokens)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        self.kernels = {"kv_rotquant_write": self.write_bytes(C, Hkv),
+                        "kv_int4_paged_decode": self.decode_bytes([L], Hkv, Hq, P)}
+        self.launch_count = {"kv_rotquant_write": L // C, "kv_int4_paged_decode": 1}
+        self.tokens_per_step = 2 * L
+        self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                       "context": L, "chunk": C, "page_size": P, "k_block": w.k_block,
+                       "v_block": w.v_block}
+
+    def step_long_context(self, i, ev):
+        K = self.K
+        ev[0].record()
+        for c, sl in enumerate(self.chunk_slots):
+            K.kv_rotquant_write(self.cache, self.chunks_k[c % 4], self.chunks_v[c % 4], sl)
+        ev[1].record()
+        K.kv_int4_paged_decode(self.cache, self.q, self.tab, self.lens, int(self.w.total_tokens),
+                               out=self.out, split_tokens=self.args.split_tokens, workspace=self.ws)
+        ev[2].record()
+
+    # -- tiny
+    def setup_tiny(self):
+        K, torch, w = self.K, self.torch, self.w
+        self.kb, self.vb = w.k_block, w.v_block
+        k, v = w.kv()
+        self.cache = K.PagedInt4Cache(w.paging.num_pages, 1, 16, 128, 128)
+        self.k = torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).to(self.dev)
+        self.v = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(self.dev)
+        self.q = torch.from_numpy(w.q().view(np.int16)).view(torch.bfloat16).to(self.dev)
+        self.slots = self.dev_i32(w.all_slots())
+        self.tab = self.dev_i32(w.paging.page_table())
+        self.lens = self.dev_i32(w.seq_lens)
+        self.kernels = {"kv_rotquant_write": self.write_bytes(64, 1),
+                        "kv_int4_paged_decode": self.decode_bytes([64], 1, 1, 16)}
+        self.tokens_per_step = 128
+        self.config = {"workload": w.name, "num_q_heads": 1, "num_kv_heads": 1, "head_dim": D,
+                       "tokens_written": 64, "tokens_attended": 64, "page_size": 16,
+                       "k_block": 128, "v_block": 128}
+
+    def step_tiny(self, i, ev):
+        K = self.K
+        ev[0].record()
+        K.kv_rotquant_write(self.cache, self.k, self.v, self.slots)
+        ev[1].record()
+        K.kv_int4_paged_decode(self.cache, self.q, self.tab, self.lens, 64)
+        ev[2].record()
+
+    def step(self, i, ev):
+        getattr(self, "step_" + self.args.workload)(i, ev)
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+def cpu_baseline(args):
+    """Time the oracle (as it stands) on a bounded sample of the same workload."""
+    import oracle
+    oracle.build(force=False)
+    cores = len(os.sched_getaffinity(0))
+    w = W.WORKLOADS[args.workload]()
+    kb = args.k_block if args.k_block is not None else w.k_block
+    if args.workload == "prefill_chunk" and args.variant == "plain":
+        kb = 0
+    rng = w.rng(77)
+    # sample: up to 8 sequences (long context: 65536 tokens) of the workload's own shapes
+    if args.workload == "long_context":
+        lens = np.array([65536])
+    elif args.workload == "qwen3_32b_like_decode":
+        lens = w.seq_lens[:4]
+    else:
+        lens = w.seq_lens[:8]
+    paging = W.assign_pages(rng, list(lens), w.page_size)
+    T = int(lens.sum())
+    k = W.make_rows(rng, T, w.num_kv_heads, w.k_out)
+    v = W.make_rows(rng, T, w.num_kv_heads, w.v_out)
+    slots = np.concatenate([paging.slots(s, 0, int(L)) for s, L in enumerate(lens)])
+    q = W.f32_to_bf16_bits(rng.standard_normal((len(lens), w.num_q_heads, D)).astype(np.float32))
+    tab = paging.page_table()
+    decode = args.workload != "prefill_chunk"
+    reps, t_total, tokens = 0, 0.0, 0
+    while t_total < args.cpu_seconds and reps < 1000:
+        cache = oracle.Cache(paging.num_pages, w.num_kv_heads, w.page_size)
+        t0 = time.perf_counter()
+        oracle.write(cache, k, v, slots, kb, w.v_block)
+        if decode:
+            oracle.decode(q, (cache.k_codes, cache.v_codes, cache.k_params, cache.v_params), tab,
+                          lens.astype(np.int32), w.num_kv_heads, w.page_size, kb, w.v_block)
+        t_total += time.perf_counter() - t0
+        tokens += T * (2 if decode else 1)
+        reps += 1
+    what = f"{reps} x (write {T} tokens" + (f" + decode {len(lens)} sequences)" if decode else ")")
+    return {"value": tokens / t_total, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what}, {args.workload} shapes, OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', cores)}",
+            "seconds": round(t_total, 3)}
+
+
+# ------------------------------------------------------------------ counters
+def parse_counter_dirs(fetch_dir, write_dir, out_json):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from two rocprofv3 --pmc
+    runs, plus the calibration copy's values, into ``out_json``."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        acc = {}
+        for fn in files:
+            with open(fn) as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    name = row.get("Kernel_Name", "")
+                    acc.setdefault(name, []).append(float(row["Counter_Value"]))
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+    fetch = load(fetch_dir, "FETCH_SIZE")
+    write = load(write_dir, "WRITE_SIZE")
+    out = {"kernel_hash": kernel_source_hash(), "fetch_kib": {}, "write_kib": {}}
+    for k, (m, n) in fetch.items():
+        out["fetch_kib"][k] = {"mean": m, "dispatches": n}
+    for k, (m, n) in write.items():
+        out["write_kib"][k] = {"mean": m, "dispatches": n}
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1, sort_keys=True))
+
+
+def traffic_from_counters(path, kernel_symbol, copy_bytes):
+    """HBM bytes per launch of ``kernel_symbol`` from a counters summary, scaled by the plain
+    copy kernel's counter-to-byte factor; None if absent or taken on other kernel sources."""
+    if not path or not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("kernel_hash") != kernel_source_hash():
+        return None, "stale"
+
+    def pick(table, sub):
+        for name, v in table.items():
+            if sub in name:
+                return v["mean"]
+        return None
+
+    f_k, w_k = pick(c["fetch_kib"], kernel_symbol), pick(c["write_kib"], kernel_symbol)
+    f_c, w_c = pick(c["fetch_kib"], "device_copy_kernel"), pick(c["write_kib"], "device_copy_kernel")
+    if None in (f_k, w_k, f_c, w_c):
+        return None, "incomplete"
+    fetch_factor = copy_bytes / (f_c * 1024.0)      # true bytes per counted byte (reads)
+    write_factor = copy_bytes / (w_c * 1024.0)
+    return f_k * 1024.0 * fetch_factor + w_k * 1024.0 * write_factor, \
+        {"fetch_factor": fetch_factor, "write_factor": write_factor}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    args = parse_args()
+    if args.parse_counters:
+        parse_counter_dirs(*args.parse_counters)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the rotated INT4 KV-cache path shards by KV head or by "
+              "sequence with no exchange, and this build runs on a single MI355X only "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+    import int4_kv_cache_rotquant_amd as K
+    K.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    s = Setup(args, K, torch)
+    torch.cuda.synchronize()
+
+    copy_bytes = 1 << 30
+    if args.calibrate_copy:
+        src = torch.empty(copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            K.kvrq_device_copy(dst, src)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        K.kvrq_device_copy(dst, src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * copy_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+    else:
+        copy_gbps = None
+
+    n_ev = 3
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for i in range(args.warmup):
+        s.step(i, warm)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s.step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    names = list(s.kernels)
+    per_kernel = {}
+    for j, name in enumerate(names):
+        ms = [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]
+        launches = getattr(s, "launch_count", {}).get(name, 1)
+        mean_ms = float(np.mean(ms)) / launches
+        per_kernel[name] = {"mean_us": round(mean_ms * 1e3, 3),
+                            "median_us": round(float(np.median(ms)) / launches * 1e3, 3),
+                            "algorithmic_bytes": s.kernels[name],
+                            "algorithmic_gbps": round(s.kernels[name] / (mean_ms * 1e-3) / 1e9, 1),
+                            "launches_per_step": launches}
+    dominant = max(names, key=lambda n: per_kernel[n]["mean_us"] * per_kernel[n]["launches_per_step"])
+    dk = per_kernel[dominant]
+    achieved = dk["algorithmic_gbps"]
+    symbol = {"kv_rotquant_write": "rotquant_write_kernel", "kv_int4_paged_decode": "decode_split_kernel",
+              "kvrq_bf16_paged_write": "bf16_paged_write_kernel"}[dominant]
+    traffic, traffic_note = traffic_from_counters(args.counters, symbol, copy_bytes)
+
+    ms_per_step = elapsed / args.steps * 1e3
+    value = s.tokens_per_step * args.steps / elapsed
+    result = {
+        "metric": "KV tokens/s and achieved HBM GB/s (% of peak) for rotquant write + INT4 decode",
+        "value": round(value, 1),
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 compute, int4+fp16 cache",
+        "data": "synthetic (seeded N(0,1) with outlier channels; no model weights)",
+        "config": s.config,
+        "kernels": per_kernel,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "traffic_note": traffic_note},
+        "hbm_gbps_step": round(sum(per_kernel[n]["algorithmic_bytes"] * per_kernel[n]["launches_per_step"]
+                                   for n in names) / (ms_per_step * 1e-3) / 1e9, 1),
+        "copy_probe_gbps": None if copy_gbps is None else round(copy_gbps, 1),
+        "kernel_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,233 @@
+/*
+ * kvrq.h -- C ABI of the MI355X (gfx950) rotated INT4 paged KV cache.
+ *
+ * The library implements the hot path of SAW-INT4 ("System-Aware 4-Bit
+ * KV-Cache Quantization for Real-World LLM Serving"):
+ *
+ *   kv_rotquant_write     one fused launch that rotates each K (and/or V) head
+ *                         row by a block-diagonal Walsh-Hadamard matrix,
+ *                         quantises it token-wise to INT4 and stores the codes
+ *                         and fp16 parameters straight into a paged cache
+ *                         (wispaper.ai blog, section 3: the rotation is fused
+ *                         into the KV-cache write operator, no separate
+ *                         launch; fugumt.com abstract: a fused
+ *                         rotation-quantisation kernel that writes into paged
+ *                         KV-cache layouts);
+ *   kv_int4_paged_decode  decode attention over that cache: the query is
+ *                         rotated by the same matrix (wispaper.ai blog,
+ *                         section 3, third consequence: the rotated dot
+ *                         product equals the original one), INT4 pages are
+ *                         de-quantised on the fly, the V rotation is undone on
+ *                         the output;
+ *   kvrq_pool_*           a host page allocator and page table for the fixed-
+ *                         size pages the pages insist on (wispaper.ai blog,
+ *                         section 1: PagedAttention needs uniform pages).
+ *
+ * Conventions for every call:
+ *   - Return value: kvrq_status, 0 = KVRQ_OK.  On failure a description is
+ *     available from kvrq_last_error() (thread-local, valid until the next
+ *     failing call on the same thread).  No C++ exception crosses the ABI.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call touches no device memory and makes no HIP call.
+ *   - Device pointers are plain addresses of device memory owned by the
+ *     caller.  The library never allocates or frees device memory and never
+ *     synchronises the device; hot-path calls are asynchronous on the HIP
+ *     stream passed as `stream` (a hipStream_t; NULL = the null stream).
+ *   - A launch failure is reported as KVRQ_EHIP with the HIP error string.
+ *   - head_dim must be 128.  Rotation blocks are 0 (no rotation, plain INT4)
+ *     or 16, 32, 64, 128.  Page sizes are powers of two; the decode needs a
+ *     multiple of 16.
+ *
+ * Cache layout (per layer, separate K and V pools):
+ *   codes   uint8   [num_pages][num_kv_heads][page_size][head_dim/2]
+ *           byte i of a row holds channel 2i in its low nibble and channel
+ *           2i+1 in its high nibble;
+ *   params  uint16  [num_pages][num_kv_heads][page_size][2]
+ *           binary16 bit patterns (scale, zero); a row de-quantises as
+ *           code * scale + zero in the rotated basis.
+ * A token position `pos` of a sequence lives at slot = page * page_size +
+ * pos % page_size, with page = the sequence's page for pos / page_size.
+ */
+#ifndef KVRQ_H
+#define KVRQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(KVRQ_BUILDING_LIBRARY)
+#define KVRQ_API __attribute__((visibility("default")))
+#else
+#define KVRQ_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvrq_status;
+
+enum {
+    KVRQ_OK = 0,
+    KVRQ_EINVAL = 1,        /* null pointer, negative size, bad alignment, bad shape */
+    KVRQ_EUNSUPPORTED = 2,  /* valid request outside what this build implements */
+    KVRQ_ENOPAGES = 3,      /* the page pool cannot satisfy a request */
+    KVRQ_EHIP = 4,          /* a HIP launch or runtime error */
+    KVRQ_EWORKSPACE = 5     /* workspace too small */
+};
+
+/* Static name of a status code ("KVRQ_OK", ...). Never NULL. */
+KVRQ_API const char *kvrq_status_str(kvrq_status s);
+
+/* Text of the last failure on this thread ("" if none). Never NULL. */
+KVRQ_API const char *kvrq_last_error(void);
+
+/* Geometry of one layer's cache.  k_block / v_block: rotation block of the
+ * K and V rows (0 = no rotation), the block sizes 16..128 of the pages
+ * (wispaper.ai blog, section 2, block-diagonal bullet). */
+typedef struct {
+    int32_t head_dim;      /* D, must be 128 */
+    int32_t num_kv_heads;  /* Hkv >= 1 */
+    int32_t page_size;     /* P tokens per page, power of two, 1..1024 */
+    int32_t num_pages;     /* pages in each pool, >= 1 */
+    int32_t k_block;       /* 0, 16, 32, 64 or 128 */
+    int32_t v_block;       /* 0, 16, 32, 64 or 128 */
+} kvrq_cache_desc;
+
+/* Device buffers of one layer's cache (caller-allocated, layout above).
+ * All four must be 16-byte aligned. */
+typedef struct {
+    uint8_t *k_codes;
+    uint8_t *v_codes;
+    uint16_t *k_params;
+    uint16_t *v_params;
+} kvrq_cache_buffers;
+
+/* Bytes of ONE codes pool and ONE params pool for `d` (K and V each need
+ * one of both).  Validates `d`. */
+KVRQ_API kvrq_status kvrq_cache_sizes(const kvrq_cache_desc *d, size_t *codes_bytes, size_t *params_bytes);
+
+/* ------------------------------------------------------------------------
+ * Host page pool and page table (host memory only; one pool per cache;
+ * not thread-safe).  Pages are handed out from a free list whose initial
+ * order is the identity (shuffle_seed == 0) or a permutation drawn from a
+ * 64-bit seed (scattered pages, as a long-running server would see).
+ * ------------------------------------------------------------------------ */
+typedef struct kvrq_pool kvrq_pool;
+
+/* Create a pool of num_pages pages of page_size tokens for up to max_seqs
+ * sequences of at most max_pages_per_seq pages each.  *out receives the
+ * pool; release it with kvrq_pool_destroy. */
+KVRQ_API kvrq_status kvrq_pool_create(int32_t num_pages, int32_t page_size, int32_t max_seqs,
+                             int32_t max_pages_per_seq, uint64_t shuffle_seed, kvrq_pool **out);
+
+/* Free a pool (NULL is ignored). */
+KVRQ_API void kvrq_pool_destroy(kvrq_pool *p);
+
+/* Grow sequence `seq` to hold new_len tokens, taking pages from the free
+ * list.  All or nothing: on KVRQ_ENOPAGES (pool exhausted or the sequence
+ * would exceed max_pages_per_seq) nothing changes.  new_len below the
+ * current length is KVRQ_EINVAL. */
+KVRQ_API kvrq_status kvrq_seq_extend(kvrq_pool *p, int32_t seq, int32_t new_len);
+
+/* Return all pages of `seq` to the free list and set its length to 0. */
+KVRQ_API kvrq_status kvrq_seq_release(kvrq_pool *p, int32_t seq);
+
+/* Current length of `seq` in tokens, or -1 for a bad pool or index. */
+KVRQ_API int32_t kvrq_seq_len(const kvrq_pool *p, int32_t seq);
+
+/* Slots of positions first_pos .. first_pos+count-1 of `seq` into the host
+ * array slots_out[count].  The positions must lie below the sequence's
+ * length (extend first). */
+KVRQ_API kvrq_status kvrq_slots(const kvrq_pool *p, int32_t seq, int32_t first_pos, int32_t count,
+                       int32_t *slots_out);
+
+/* Export the page table: table_out[max_seqs][max_pages_per_seq] (host,
+ * -1 beyond each sequence's pages) and seq_lens_out[max_seqs] (host; may
+ * be NULL). */
+KVRQ_API kvrq_status kvrq_page_table(const kvrq_pool *p, int32_t *table_out, int32_t *seq_lens_out);
+
+/* Number of free pages, or -1 for a NULL pool. */
+KVRQ_API int32_t kvrq_pool_free_pages(const kvrq_pool *p);
+
+/* ------------------------------------------------------------------------
+ * Hot path
+ * ------------------------------------------------------------------------ */
+
+/* Fused rotation + token-wise INT4 write (K~ = quant(K H_blk), V~ =
+ * quant(V H_blk); wispaper.ai blog, section 3 core formula).
+ *   k, v            device bf16 [num_tokens][num_kv_heads][head_dim]; token
+ *                   t of head h starts at element t*token_stride + h*head_dim;
+ *                   16-byte aligned, strides multiples of 8 elements
+ *   num_tokens      T >= 0 (T == 0 launches nothing)
+ *   slot_mapping    device int32 [T]; slot < 0 or slot >= num_pages*page_size
+ *                   skips the token; slots must be unique within a call
+ *                   (duplicates race; not checked)
+ * For every written row (token t, head h, tensor X) with block b:
+ *   y = H_b x in fp32 (butterflies of width 1, 2, ..., b/2, then * fp32(1/sqrt b)),
+ *   scale = fp16((max y - min y) / 15), zero = fp16(min y),
+ *   code_d = clamp(round_half_even((y_d - zero) / scale), 0, 15)  (0 if scale == 0).
+ * One launch on `stream`; rows are independent (no atomics). */
+KVRQ_API kvrq_status kv_rotquant_write(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
+                              const void *k, const void *v, int64_t num_tokens,
+                              int64_t k_token_stride, int64_t v_token_stride,
+                              const int32_t *slot_mapping, void *stream);
+
+/* Workspace bytes kv_int4_paged_decode needs for num_seqs sequences of at
+ * most max_seq_len tokens with num_q_heads query heads and the given
+ * split_tokens (0 = automatic, as in the decode call). */
+KVRQ_API kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t max_seq_len,
+                                           int32_t split_tokens, size_t *bytes);
+
+/* Paged INT4 decode attention (one query token per sequence).
+ *   q               device bf16 [num_seqs][num_q_heads][head_dim], unrotated
+ *   num_q_heads     multiple of num_kv_heads, at most 16 per KV head; query
+ *                   head g reads KV head g / (num_q_heads / num_kv_heads)
+ *   page_table      device int32 [num_seqs][max_pages_per_seq]; an entry
+ *                   outside [0, num_pages) is read as page 0 (garbage
+ *                   output, never an out-of-bounds access)
+ *   seq_lens        device int32 [num_seqs]; tokens 0..L-1 are attended;
+ *                   L above max_seq_len is clamped to it; L <= 0 gives a
+ *                   zero row
+ *   max_seq_len     host bound on every L, used to plan the splits
+ *   sm_scale        softmax scale; <= 0 selects 1/sqrt(head_dim)
+ *   split_tokens    tokens per split-K partition; 0 = automatic, otherwise a
+ *                   multiple of 32
+ *   out             device fp32 [num_seqs][num_q_heads][head_dim]
+ *   workspace       device scratch of workspace_bytes >= the size reported by
+ *                   kv_int4_paged_decode_workspace (16-byte aligned)
+ * Computes, per sequence s and query head g (KV head h):
+ *   q' = H_bK q,  score_t = sm_scale * q'.(code_t * scale_t + zero_t),
+ *   o' = sum_t softmax(score)_t (V code_t * scale_t + zero_t),  out = H_bV o'.
+ * Two launches on `stream` (split-K partials, then the combine). */
+KVRQ_API kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
+                                 const void *q, int32_t num_seqs, int32_t num_q_heads,
+                                 const int32_t *page_table, int32_t max_pages_per_seq,
+                                 const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
+                                 int32_t split_tokens, float *out, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement helpers (same conventions)
+ * ------------------------------------------------------------------------ */
+
+/* Unquantised reference write: bf16 rows copied into a paged bf16 cache
+ * k_cache/v_cache [num_pages][num_kv_heads][page_size][head_dim] at the same
+ * slots (the BF16 KV-cache baseline the pages compare against; wispaper.ai
+ * blog, section 4).  Only head_dim, num_kv_heads, page_size and num_pages
+ * of `d` are used. */
+KVRQ_API kvrq_status kvrq_bf16_paged_write(const kvrq_cache_desc *d, void *k_cache, void *v_cache,
+                                  const void *k, const void *v, int64_t num_tokens,
+                                  int64_t k_token_stride, int64_t v_token_stride,
+                                  const int32_t *slot_mapping, void *stream);
+
+/* Plain device copy of `bytes` bytes (multiple of 16, both pointers 16-byte
+ * aligned): the streaming kernel used to measure achievable HBM bandwidth
+ * and to calibrate byte counters. */
+KVRQ_API kvrq_status kvrq_device_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVRQ_H */

@@ -1,0 +1,258 @@
+"""ctypes binding of ``libkvrq.so`` (declared in ``include/kvrq.h``).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels.  PyTorch provides device memory and the current HIP stream.
+The functions keep the C names; tensors stand in for the raw pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libkvrq.so")
+
+KVRQ_OK, KVRQ_EINVAL, KVRQ_EUNSUPPORTED, KVRQ_ENOPAGES, KVRQ_EHIP, KVRQ_EWORKSPACE = range(6)
+HEAD_DIM = 128
+
+
+class KvrqError(RuntimeError):
+    def __init__(self, status: int, name: str, message: str):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("k_block", ctypes.c_int32), ("v_block", ctypes.c_int32)]
+
+
+class CacheBuffers(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_params", ctypes.c_void_p), ("v_params", ctypes.c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library; fails loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m int4_kv_cache_rotquant_amd.build` (there is no fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    st = ctypes.c_int32
+    sig = {
+        "kvrq_status_str": (ctypes.c_char_p, [st]),
+        "kvrq_last_error": (ctypes.c_char_p, []),
+        "kvrq_cache_sizes": (st, [P, P, P]),
+        "kvrq_pool_create": (st, [i32, i32, i32, i32, ctypes.c_uint64, P]),
+        "kvrq_pool_destroy": (None, [P]),
+        "kvrq_seq_extend": (st, [P, i32, i32]),
+        "kvrq_seq_release": (st, [P, i32]),
+        "kvrq_seq_len": (i32, [P, i32]),
+        "kvrq_slots": (st, [P, i32, i32, i32, P]),
+        "kvrq_page_table": (st, [P, P, P]),
+        "kvrq_pool_free_pages": (i32, [P]),
+        "kv_rotquant_write": (st, [P, P, P, P, i64, i64, i64, P, P]),
+        "kv_int4_paged_decode_workspace": (st, [P, i32, i32, i32, i32, P]),
+        "kv_int4_paged_decode": (st, [P, P, P, i32, i32, P, i32, P, i32, ctypes.c_float, i32, P, P,
+                                      sz, P]),
+        "kvrq_bf16_paged_write": (st, [P, P, P, P, P, i64, i64, i64, P, P]),
+        "kvrq_device_copy": (st, [P, P, sz, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != KVRQ_OK:
+        L = lib()
+        raise KvrqError(status, L.kvrq_status_str(status).decode(), L.kvrq_last_error().decode())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def status_str(status: int) -> str:
+    return lib().kvrq_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib().kvrq_last_error().decode()
+
+
+# --------------------------------------------------------------------- cache
+def kvrq_cache_sizes(desc: CacheDesc) -> Tuple[int, int]:
+    cb, pb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().kvrq_cache_sizes(ctypes.byref(desc), ctypes.byref(cb), ctypes.byref(pb)))
+    return cb.value, pb.value
+
+
+class PagedInt4Cache:
+    """One layer's INT4 cache: descriptor + four torch device tensors."""
+
+    def __init__(self, num_pages: int, num_kv_heads: int, page_size: int, k_block: int,
+                 v_block: int, device="cuda", fill: Optional[int] = None):
+        import torch
+        self.desc = CacheDesc(HEAD_DIM, num_kv_heads, page_size, num_pages, k_block, v_block)
+        codes_bytes, params_bytes = kvrq_cache_sizes(self.desc)
+        shape_c = (num_pages, num_kv_heads, page_size, HEAD_DIM // 2)
+        shape_p = (num_pages, num_kv_heads, page_size, 2)
+        self.k_codes = torch.empty(shape_c, dtype=torch.uint8, device=device)
+        self.v_codes = torch.empty(shape_c, dtype=torch.uint8, device=device)
+        self.k_params = torch.empty(shape_p, dtype=torch.int16, device=device)
+        self.v_params = torch.empty(shape_p, dtype=torch.int16, device=device)
+        if fill is not None:
+            for t in (self.k_codes, self.v_codes, self.k_params, self.v_params):
+                t.view(torch.uint8).fill_(fill)
+        assert self.k_codes.numel() == codes_bytes and self.k_params.numel() * 2 == params_bytes
+        self.buffers = CacheBuffers(self.k_codes.data_ptr(), self.v_codes.data_ptr(),
+                                    self.k_params.data_ptr(), self.v_params.data_ptr())
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.desc.num_kv_heads
+
+    @property
+    def page_size(self) -> int:
+        return self.desc.page_size
+
+
+# --------------------------------------------------------------------- hot path
+def kv_rotquant_write(cache: PagedInt4Cache, k, v, slot_mapping, stream=None) -> None:
+    """Fused BDR + token-wise INT4 write of bf16 ``k, v`` [T][Hkv][128] at int32 ``slot_mapping``."""
+    import torch
+    T = int(slot_mapping.shape[0])
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != HEAD_DIM:
+            raise ValueError(f"{name} must be bf16 [T][Hkv][128] with contiguous heads")
+        if t.shape[0] != T:
+            raise ValueError(f"{name} has {t.shape[0]} tokens, slot_mapping {T}")
+    if slot_mapping.dtype != torch.int32:
+        raise ValueError("slot_mapping must be int32")
+    _check(lib().kv_rotquant_write(ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(k),
+                                   _ptr(v), T, k.stride(0), v.stride(0), _ptr(slot_mapping),
+                                   _stream(stream)))
+
+
+def kv_int4_paged_decode_workspace(cache: PagedInt4Cache, num_seqs: int, num_q_heads: int,
+                                   max_seq_len: int, split_tokens: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().kv_int4_paged_decode_workspace(ctypes.byref(cache.desc), num_seqs, num_q_heads,
+                                                max_seq_len, split_tokens, ctypes.byref(n)))
+    return n.value
+
+
+def kv_int4_paged_decode(cache: PagedInt4Cache, q, page_table, seq_lens, max_seq_len: int,
+                         out=None, sm_scale: float = 0.0, split_tokens: int = 0, workspace=None,
+                         stream=None):
+    """Paged INT4 decode of bf16 ``q`` [S][Hq][128]; returns fp32 ``out`` [S][Hq][128]."""
+    import torch
+    S, Hq, D = q.shape
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or D != HEAD_DIM:
+        raise ValueError("q must be contiguous bf16 [S][Hq][128]")
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.shape[0] != S:
+        raise ValueError("page_table must be contiguous int32 [S][max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (S,):
+        raise ValueError("seq_lens must be int32 [S]")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = kv_int4_paged_decode_workspace(cache, S, Hq, max_seq_len, split_tokens)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().kv_int4_paged_decode(
+        ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(q), S, Hq, _ptr(page_table),
+        int(page_table.shape[1]), _ptr(seq_lens), int(max_seq_len), float(sm_scale), int(split_tokens),
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------- measurement helpers
+def kvrq_bf16_paged_write(desc: CacheDesc, k_cache, v_cache, k, v, slot_mapping, stream=None) -> None:
+    T = int(slot_mapping.shape[0])
+    _check(lib().kvrq_bf16_paged_write(ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(k),
+                                       _ptr(v), T, k.stride(0), v.stride(0), _ptr(slot_mapping),
+                                       _stream(stream)))
+
+
+def kvrq_device_copy(dst, src, nbytes: Optional[int] = None, stream=None) -> None:
+    n = nbytes if nbytes is not None else src.numel() * src.element_size()
+    _check(lib().kvrq_device_copy(_ptr(dst), _ptr(src), n, _stream(stream)))
+
+
+# --------------------------------------------------------------------- host page pool
+class Pool:
+    """Host page allocator + page table (``kvrq_pool_*``)."""
+
+    def __init__(self, num_pages: int, page_size: int, max_seqs: int, max_pages_per_seq: int,
+                 shuffle_seed: int = 0):
+        self._h = ctypes.c_void_p()
+        _check(lib().kvrq_pool_create(num_pages, page_size, max_seqs, max_pages_per_seq,
+                                      shuffle_seed, ctypes.byref(self._h)))
+        self.num_pages, self.page_size = num_pages, page_size
+        self.max_seqs, self.max_pages_per_seq = max_seqs, max_pages_per_seq
+
+    def close(self):
+        if self._h:
+            lib().kvrq_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def seq_extend(self, seq: int, new_len: int) -> None:
+        _check(lib().kvrq_seq_extend(self._h, seq, new_len))
+
+    def seq_release(self, seq: int) -> None:
+        _check(lib().kvrq_seq_release(self._h, seq))
+
+    def seq_len(self, seq: int) -> int:
+        return lib().kvrq_seq_len(self._h, seq)
+
+    def free_pages(self) -> int:
+        return lib().kvrq_pool_free_pages(self._h)
+
+    def slots(self, seq: int, first_pos: int, count: int):
+        import numpy as np
+        out = np.zeros(count, np.int32)
+        _check(lib().kvrq_slots(self._h, seq, first_pos, count, out.ctypes.data_as(ctypes.c_void_p)))
+        return out
+
+    def page_table(self):
+        import numpy as np
+        tab = np.zeros((self.max_seqs, self.max_pages_per_seq), np.int32)
+        lens = np.zeros(self.max_seqs, np.int32)
+        _check(lib().kvrq_page_table(self._h, tab.ctypes.data_as(ctypes.c_void_p),
+                                     lens.ctypes.data_as(ctypes.c_void_p)))
+        return tab, lens
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def log2_int(x: int) -> int:
+    return int(math.log2(x))

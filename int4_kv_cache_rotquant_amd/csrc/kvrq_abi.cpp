@@ -1,0 +1,496 @@
+// C-ABI layer: argument validation, error reporting, the host page pool and
+// dispatch to the HIP launchers.  No device memory is allocated here and no
+// HIP call is made before every argument has been checked.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/kvrq.h"
+#include "kvrq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvrq_status fail(kvrq_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2_exact(int64_t x)
+{
+    int l = 0;
+    while ((int64_t(1) << l) < x)
+        ++l;
+    return l;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_block(int b) { return b == 0 || b == 16 || b == 32 || b == 64 || b == 128; }
+
+kvrq_status check_desc(const kvrq_cache_desc *d)
+{
+    if (!d)
+        return fail(KVRQ_EINVAL, "cache descriptor is NULL");
+    if (d->head_dim != kvrq::kHeadDim)
+        return fail(KVRQ_EUNSUPPORTED, "head_dim %d unsupported (only 128)", d->head_dim);
+    if (d->num_kv_heads < 1)
+        return fail(KVRQ_EINVAL, "num_kv_heads must be >= 1 (got %d)", d->num_kv_heads);
+    if (!is_pow2(d->page_size) || d->page_size > 1024)
+        return fail(KVRQ_EUNSUPPORTED, "page_size %d unsupported (power of two, 1..1024)", d->page_size);
+    if (d->num_pages < 1)
+        return fail(KVRQ_EINVAL, "num_pages must be >= 1 (got %d)", d->num_pages);
+    if (!valid_block(d->k_block) || !valid_block(d->v_block))
+        return fail(KVRQ_EUNSUPPORTED, "rotation blocks (%d, %d) unsupported (0, 16, 32, 64, 128)",
+                    d->k_block, d->v_block);
+    const int64_t cells = int64_t(d->num_pages) * d->num_kv_heads * d->page_size;
+    if (cells > (int64_t(1) << 40))
+        return fail(KVRQ_EINVAL, "cache too large");
+    return KVRQ_OK;
+}
+
+kvrq_status check_buffers(const kvrq_cache_buffers *b)
+{
+    if (!b)
+        return fail(KVRQ_EINVAL, "cache buffers struct is NULL");
+    if (!b->k_codes || !b->v_codes || !b->k_params || !b->v_params)
+        return fail(KVRQ_EINVAL, "a cache buffer pointer is NULL");
+    if (!aligned(b->k_codes, 16) || !aligned(b->v_codes, 16) || !aligned(b->k_params, 16) ||
+        !aligned(b->v_params, 16))
+        return fail(KVRQ_EINVAL, "cache buffers must be 16-byte aligned");
+    return KVRQ_OK;
+}
+
+kvrq_status check_rows(const kvrq_cache_desc *d, const void *k, const void *v, int64_t T, int64_t ks,
+                       int64_t vs, const int32_t *slots)
+{
+    if (T < 0)
+        return fail(KVRQ_EINVAL, "num_tokens must be >= 0 (got %lld)", (long long)T);
+    if (T > INT32_MAX)
+        return fail(KVRQ_EUNSUPPORTED, "num_tokens %lld above 2^31-1", (long long)T);
+    if (T == 0)
+        return KVRQ_OK;
+    if (!k || !v || !slots)
+        return fail(KVRQ_EINVAL, "k, v and slot_mapping must be non-NULL");
+    const int64_t row = int64_t(d->num_kv_heads) * d->head_dim;
+    if (ks < row || vs < row)
+        return fail(KVRQ_EINVAL, "token strides (%lld, %lld) below num_kv_heads*head_dim = %lld",
+                    (long long)ks, (long long)vs, (long long)row);
+    if (ks % 8 || vs % 8)
+        return fail(KVRQ_EINVAL, "token strides must be multiples of 8 elements");
+    if (!aligned(k, 16) || !aligned(v, 16))
+        return fail(KVRQ_EINVAL, "k and v must be 16-byte aligned");
+    if (!aligned(slots, 4))
+        return fail(KVRQ_EINVAL, "slot_mapping must be 4-byte aligned");
+    return KVRQ_OK;
+}
+
+kvrq_status hip_status(int err, const char *what)
+{
+    if (err == 0)
+        return KVRQ_OK;
+    return fail(KVRQ_EHIP, "%s: %s", what, kvrq::hip_error_string(err));
+}
+
+// Decode split plan: partitions of split_tokens (a multiple of 32) chosen so
+// that an upper bound of the total work fills the chip several times over
+// while each wave still streams a few hundred tokens.
+kvrq::DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                             int32_t split_tokens)
+{
+    kvrq::DecodePlan p;
+    if (split_tokens <= 0) {
+        const int64_t work = int64_t(num_seqs) * num_kv_heads * std::max<int32_t>(max_seq_len, 1);
+        int64_t st = work / 8192;
+        st = std::max<int64_t>(256, std::min<int64_t>(2048, st));
+        st = (st + kvrq::kTile - 1) / kvrq::kTile * kvrq::kTile;
+        split_tokens = (int32_t)st;
+    }
+    p.split_tokens = split_tokens;
+    p.max_splits = std::max<int32_t>(1, (max_seq_len + split_tokens - 1) / split_tokens);
+    return p;
+}
+
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const kvrq::DecodePlan &p)
+{
+    const size_t rows = size_t(num_seqs) * num_q_heads * p.max_splits;
+    return rows * (kvrq::kHeadDim + 2) * sizeof(float);
+}
+
+kvrq_status check_decode_shape(const kvrq_cache_desc *d, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t max_seq_len, int32_t split_tokens)
+{
+    kvrq_status st = check_desc(d);
+    if (st)
+        return st;
+    if (num_seqs < 0)
+        return fail(KVRQ_EINVAL, "num_seqs must be >= 0");
+    if (num_q_heads < 1 || num_q_heads % d->num_kv_heads)
+        return fail(KVRQ_EINVAL, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                    num_q_heads, d->num_kv_heads);
+    if (num_q_heads / d->num_kv_heads > kvrq::kMaxGroup)
+        return fail(KVRQ_EUNSUPPORTED, "more than %d query heads per KV head", kvrq::kMaxGroup);
+    if (d->page_size < 16)
+        return fail(KVRQ_EUNSUPPORTED, "decode needs page_size >= 16 (got %d)", d->page_size);
+    if (max_seq_len < 0)
+        return fail(KVRQ_EINVAL, "max_seq_len must be >= 0");
+    if (split_tokens < 0 || split_tokens % kvrq::kTile)
+        return fail(KVRQ_EINVAL, "split_tokens must be 0 or a positive multiple of %d", kvrq::kTile);
+    if (num_seqs > 65535)
+        return fail(KVRQ_EUNSUPPORTED, "num_seqs above 65535");
+    return KVRQ_OK;
+}
+
+}  // namespace
+
+// --------------------------------------------------------------------------
+// host page pool
+// --------------------------------------------------------------------------
+struct kvrq_pool {
+    int32_t num_pages;
+    int32_t page_size;
+    int32_t max_seqs;
+    int32_t max_pages_per_seq;
+    std::vector<int32_t> free_list;              // back() is handed out next
+    std::vector<std::vector<int32_t>> seq_pages;
+    std::vector<int32_t> seq_len;
+};
+
+namespace {
+
+uint64_t splitmix64(uint64_t &x)
+{
+    uint64_t z = (x += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvrq_status_str(kvrq_status s)
+{
+    switch (s) {
+    case KVRQ_OK: return "KVRQ_OK";
+    case KVRQ_EINVAL: return "KVRQ_EINVAL";
+    case KVRQ_EUNSUPPORTED: return "KVRQ_EUNSUPPORTED";
+    case KVRQ_ENOPAGES: return "KVRQ_ENOPAGES";
+    case KVRQ_EHIP: return "KVRQ_EHIP";
+    case KVRQ_EWORKSPACE: return "KVRQ_EWORKSPACE";
+    default: return "KVRQ_UNKNOWN";
+    }
+}
+
+const char *kvrq_last_error(void) { return g_last_error.c_str(); }
+
+kvrq_status kvrq_cache_sizes(const kvrq_cache_desc *d, size_t *codes_bytes, size_t *params_bytes)
+{
+    kvrq_status st = check_desc(d);
+    if (st)
+        return st;
+    const size_t cells = size_t(d->num_pages) * d->num_kv_heads * d->page_size;
+    if (codes_bytes)
+        *codes_bytes = cells * (d->head_dim / 2);
+    if (params_bytes)
+        *params_bytes = cells * 2 * sizeof(uint16_t);
+    return KVRQ_OK;
+}
+
+kvrq_status kvrq_pool_create(int32_t num_pages, int32_t page_size, int32_t max_seqs,
+                             int32_t max_pages_per_seq, uint64_t shuffle_seed, kvrq_pool **out)
+{
+    if (!out)
+        return fail(KVRQ_EINVAL, "out pointer is NULL");
+    *out = nullptr;
+    if (num_pages < 1 || max_seqs < 1 || max_pages_per_seq < 1)
+        return fail(KVRQ_EINVAL, "num_pages, max_seqs and max_pages_per_seq must be >= 1");
+    if (!is_pow2(page_size) || page_size > 1024)
+        return fail(KVRQ_EUNSUPPORTED, "page_size %d unsupported (power of two, 1..1024)", page_size);
+    kvrq_pool *p = new (std::nothrow) kvrq_pool;
+    if (!p)
+        return fail(KVRQ_EINVAL, "out of host memory");
+    p->num_pages = num_pages;
+    p->page_size = page_size;
+    p->max_seqs = max_seqs;
+    p->max_pages_per_seq = max_pages_per_seq;
+    // page ids in hand-out order: identity, or a seeded Fisher-Yates permutation
+    std::vector<int32_t> order(num_pages);
+    for (int32_t i = 0; i < num_pages; ++i)
+        order[i] = i;
+    if (shuffle_seed) {
+        uint64_t st = shuffle_seed;
+        for (int32_t i = num_pages - 1; i > 0; --i) {
+            const uint64_t j = splitmix64(st) % uint64_t(i + 1);
+            std::swap(order[i], order[j]);
+        }
+    }
+    p->free_list.assign(order.rbegin(), order.rend());
+    p->seq_pages.assign(max_seqs, {});
+    p->seq_len.assign(max_seqs, 0);
+    *out = p;
+    return KVRQ_OK;
+}
+
+void kvrq_pool_destroy(kvrq_pool *p) { delete p; }
+
+kvrq_status kvrq_seq_extend(kvrq_pool *p, int32_t seq, int32_t new_len)
+{
+    if (!p)
+        return fail(KVRQ_EINVAL, "pool is NULL");
+    if (seq < 0 || seq >= p->max_seqs)
+        return fail(KVRQ_EINVAL, "sequence %d outside 0..%d", seq, p->max_seqs - 1);
+    if (new_len < p->seq_len[seq])
+        return fail(KVRQ_EINVAL, "new_len %d below current length %d", new_len, p->seq_len[seq]);
+    const int64_t need = (int64_t(new_len) + p->page_size - 1) / p->page_size;
+    const int64_t have = (int64_t)p->seq_pages[seq].size();
+    if (need > p->max_pages_per_seq)
+        return fail(KVRQ_ENOPAGES, "sequence %d would need %lld pages (max %d)", seq, (long long)need,
+                    p->max_pages_per_seq);
+    if (need - have > (int64_t)p->free_list.size())
+        return fail(KVRQ_ENOPAGES, "pool exhausted: need %lld more pages, %zu free",
+                    (long long)(need - have), p->free_list.size());
+    for (int64_t i = have; i < need; ++i) {
+        p->seq_pages[seq].push_back(p->free_list.back());
+        p->free_list.pop_back();
+    }
+    p->seq_len[seq] = new_len;
+    return KVRQ_OK;
+}
+
+kvrq_status kvrq_seq_release(kvrq_pool *p, int32_t seq)
+{
+    if (!p)
+        return fail(KVRQ_EINVAL, "pool is NULL");
+    if (seq < 0 || seq >= p->max_seqs)
+        return fail(KVRQ_EINVAL, "sequence %d outside 0..%d", seq, p->max_seqs - 1);
+    auto &pages = p->seq_pages[seq];
+    for (auto it = pages.rbegin(); it != pages.rend(); ++it)
+        p->free_list.push_back(*it);
+    pages.clear();
+    p->seq_len[seq] = 0;
+    return KVRQ_OK;
+}
+
+int32_t kvrq_seq_len(const kvrq_pool *p, int32_t seq)
+{
+    if (!p || seq < 0 || seq >= p->max_seqs)
+        return -1;
+    return p->seq_len[seq];
+}
+
+kvrq_status kvrq_slots(const kvrq_pool *p, int32_t seq, int32_t first_pos, int32_t count,
+                       int32_t *slots_out)
+{
+    if (!p)
+        return fail(KVRQ_EINVAL, "pool is NULL");
+    if (seq < 0 || seq >= p->max_seqs)
+        return fail(KVRQ_EINVAL, "sequence %d outside 0..%d", seq, p->max_seqs - 1);
+    if (count < 0 || first_pos < 0)
+        return fail(KVRQ_EINVAL, "first_pos and count must be >= 0");
+    if (count > 0 && !slots_out)
+        return fail(KVRQ_EINVAL, "slots_out is NULL");
+    if (int64_t(first_pos) + count > p->seq_len[seq])
+        return fail(KVRQ_EINVAL, "positions %d..%lld beyond sequence length %d", first_pos,
+                    (long long)first_pos + count - 1, p->seq_len[seq]);
+    if (int64_t(p->num_pages) * p->page_size > INT32_MAX)
+        return fail(KVRQ_EUNSUPPORTED, "pool too large for int32 slots");
+    const auto &pages = p->seq_pages[seq];
+    for (int32_t i = 0; i < count; ++i) {
+        const int32_t pos = first_pos + i;
+        slots_out[i] = pages[pos / p->page_size] * p->page_size + pos % p->page_size;
+    }
+    return KVRQ_OK;
+}
+
+kvrq_status kvrq_page_table(const kvrq_pool *p, int32_t *table_out, int32_t *seq_lens_out)
+{
+    if (!p)
+        return fail(KVRQ_EINVAL, "pool is NULL");
+    if (!table_out)
+        return fail(KVRQ_EINVAL, "table_out is NULL");
+    for (int32_t s = 0; s < p->max_seqs; ++s) {
+        int32_t *row = table_out + int64_t(s) * p->max_pages_per_seq;
+        const auto &pages = p->seq_pages[s];
+        for (int32_t i = 0; i < p->max_pages_per_seq; ++i)
+            row[i] = i < (int32_t)pages.size() ? pages[i] : -1;
+        if (seq_lens_out)
+            seq_lens_out[s] = p->seq_len[s];
+    }
+    return KVRQ_OK;
+}
+
+int32_t kvrq_pool_free_pages(const kvrq_pool *p) { return p ? (int32_t)p->free_list.size() : -1; }
+
+// --------------------------------------------------------------------------
+// hot path
+// --------------------------------------------------------------------------
+kvrq_status kv_rotquant_write(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, const void *k,
+                              const void *v, int64_t num_tokens, int64_t k_token_stride,
+                              int64_t v_token_stride, const int32_t *slot_mapping, void *stream)
+{
+    kvrq_status st = check_desc(d);
+    if (st)
+        return st;
+    st = check_buffers(b);
+    if (st)
+        return st;
+    st = check_rows(d, k, v, num_tokens, k_token_stride, v_token_stride, slot_mapping);
+    if (st)
+        return st;
+    if (num_tokens == 0)
+        return KVRQ_OK;
+    kvrq::WriteArgs a;
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.num_tokens = num_tokens;
+    a.k_stride = k_token_stride;
+    a.v_stride = v_token_stride;
+    a.slots = slot_mapping;
+    a.k_codes = b->k_codes;
+    a.v_codes = b->v_codes;
+    a.k_params = reinterpret_cast<uint32_t *>(b->k_params);
+    a.v_params = reinterpret_cast<uint32_t *>(b->v_params);
+    a.num_slots = int64_t(d->num_pages) * d->page_size;
+    a.num_kv_heads = d->num_kv_heads;
+    a.page_log2 = log2_exact(d->page_size);
+    return hip_status(kvrq::launch_rotquant_write(d->k_block, d->v_block, a, stream), "kv_rotquant_write");
+}
+
+kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, int32_t num_seqs,
+                                           int32_t num_q_heads, int32_t max_seq_len,
+                                           int32_t split_tokens, size_t *bytes)
+{
+    kvrq_status st = check_decode_shape(d, num_seqs, num_q_heads, max_seq_len, split_tokens);
+    if (st)
+        return st;
+    if (!bytes)
+        return fail(KVRQ_EINVAL, "bytes is NULL");
+    *bytes = decode_workspace_bytes(num_seqs, num_q_heads,
+                                    plan_decode(num_seqs, d->num_kv_heads, max_seq_len, split_tokens));
+    return KVRQ_OK;
+}
+
+kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, const void *q,
+                                 int32_t num_seqs, int32_t num_q_heads, const int32_t *page_table,
+                                 int32_t max_pages_per_seq, const int32_t *seq_lens,
+                                 int32_t max_seq_len, float sm_scale, int32_t split_tokens, float *out,
+                                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    kvrq_status st = check_decode_shape(d, num_seqs, num_q_heads, max_seq_len, split_tokens);
+    if (st)
+        return st;
+    st = check_buffers(b);
+    if (st)
+        return st;
+    if (num_seqs == 0)
+        return KVRQ_OK;
+    if (!q || !page_table || !seq_lens || !out)
+        return fail(KVRQ_EINVAL, "q, page_table, seq_lens and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4))
+        return fail(KVRQ_EINVAL, "q and out must be 16-byte aligned, page_table and seq_lens 4-byte");
+    if (max_pages_per_seq < 1)
+        return fail(KVRQ_EINVAL, "max_pages_per_seq must be >= 1");
+    if (int64_t(max_pages_per_seq) * d->page_size < max_seq_len)
+        return fail(KVRQ_EINVAL, "max_seq_len %d exceeds max_pages_per_seq*page_size", max_seq_len);
+    if (!std::isfinite(sm_scale))
+        return fail(KVRQ_EINVAL, "sm_scale must be finite");
+    const kvrq::DecodePlan plan = plan_decode(num_seqs, d->num_kv_heads, max_seq_len, split_tokens);
+    const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, plan);
+    if (!workspace || workspace_bytes < need)
+        return fail(KVRQ_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : size_t(0));
+    if (!aligned(workspace, 16))
+        return fail(KVRQ_EINVAL, "workspace must be 16-byte aligned");
+    if (plan.max_splits > 65535 * 64)
+        return fail(KVRQ_EUNSUPPORTED, "too many splits");
+
+    kvrq::DecodeArgs a;
+    a.k_codes = b->k_codes;
+    a.v_codes = b->v_codes;
+    a.k_params = reinterpret_cast<const uint32_t *>(b->k_params);
+    a.v_params = reinterpret_cast<const uint32_t *>(b->v_params);
+    a.q = static_cast<const uint16_t *>(q);
+    a.page_table = page_table;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    const size_t rows = size_t(num_seqs) * num_q_heads * plan.max_splits;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = a.part_o + rows * kvrq::kHeadDim;
+    a.num_seqs = num_seqs;
+    a.num_pages = d->num_pages;
+    a.max_seq_len = max_seq_len;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = d->num_kv_heads;
+    a.group = num_q_heads / d->num_kv_heads;
+    a.page_log2 = log2_exact(d->page_size);
+    a.max_pages = max_pages_per_seq;
+    a.split_tokens = plan.split_tokens;
+    a.max_splits = plan.max_splits;
+    const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(d->head_dim));
+    a.q_scale = scale * 1.4426950408889634f;
+    return hip_status(kvrq::launch_decode(d->k_block, d->v_block, a, stream), "kv_int4_paged_decode");
+}
+
+kvrq_status kvrq_bf16_paged_write(const kvrq_cache_desc *d, void *k_cache, void *v_cache, const void *k,
+                                  const void *v, int64_t num_tokens, int64_t k_token_stride,
+                                  int64_t v_token_stride, const int32_t *slot_mapping, void *stream)
+{
+    if (!d)
+        return fail(KVRQ_EINVAL, "cache descriptor is NULL");
+    kvrq_cache_desc dd = *d;
+    dd.k_block = dd.v_block = 0;
+    kvrq_status st = check_desc(&dd);
+    if (st)
+        return st;
+    if (!k_cache || !v_cache)
+        return fail(KVRQ_EINVAL, "bf16 cache pointers must be non-NULL");
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+        return fail(KVRQ_EINVAL, "bf16 caches must be 16-byte aligned");
+    st = check_rows(&dd, k, v, num_tokens, k_token_stride, v_token_stride, slot_mapping);
+    if (st)
+        return st;
+    if (num_tokens == 0)
+        return KVRQ_OK;
+    kvrq::CopyArgs a;
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.num_tokens = num_tokens;
+    a.k_stride = k_token_stride;
+    a.v_stride = v_token_stride;
+    a.slots = slot_mapping;
+    a.k_cache = static_cast<uint16_t *>(k_cache);
+    a.v_cache = static_cast<uint16_t *>(v_cache);
+    a.num_slots = int64_t(d->num_pages) * d->page_size;
+    a.num_kv_heads = d->num_kv_heads;
+    a.page_log2 = log2_exact(d->page_size);
+    return hip_status(kvrq::launch_bf16_paged_write(a, stream), "kvrq_bf16_paged_write");
+}
+
+kvrq_status kvrq_device_copy(void *dst, const void *src, size_t bytes, void *stream)
+{
+    if (bytes == 0)
+        return KVRQ_OK;
+    if (!dst || !src)
+        return fail(KVRQ_EINVAL, "dst and src must be non-NULL");
+    if (bytes % 16 || !aligned(dst, 16) || !aligned(src, 16))
+        return fail(KVRQ_EINVAL, "bytes must be a multiple of 16 and pointers 16-byte aligned");
+    return hip_status(kvrq::launch_device_copy(dst, src, bytes, stream), "kvrq_device_copy");
+}
+
+}  // extern "C"

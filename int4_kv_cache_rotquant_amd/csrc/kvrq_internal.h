@@ -1,0 +1,82 @@
+// Internal interface between the C-ABI layer (kvrq_abi.cpp) and the HIP
+// launchers (kvrq_write.hip, kvrq_decode.hip).  Plain types only; every
+// shape has been validated by the ABI layer before a launcher is called.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvrq {
+
+constexpr int kHeadDim = 128;       // channels per head
+constexpr int kRowCodeBytes = 64;   // packed INT4 bytes per (token, head) row
+constexpr int kTile = 32;           // decode tokens per inner step
+constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave
+
+struct WriteArgs {
+    const uint16_t *k;          // bf16 bits
+    const uint16_t *v;
+    int64_t num_tokens;
+    int64_t k_stride;           // elements between tokens
+    int64_t v_stride;
+    const int32_t *slots;
+    uint8_t *k_codes;
+    uint8_t *v_codes;
+    uint32_t *k_params;         // (scale | zero << 16) binary16 pairs
+    uint32_t *v_params;
+    int64_t num_slots;          // num_pages * page_size; slots at or above are skipped
+    int32_t num_kv_heads;
+    int32_t page_log2;
+};
+
+struct CopyArgs {
+    const uint16_t *k;
+    const uint16_t *v;
+    int64_t num_tokens;
+    int64_t k_stride;
+    int64_t v_stride;
+    const int32_t *slots;
+    uint16_t *k_cache;          // bf16 [pages][Hkv][P][128]
+    uint16_t *v_cache;
+    int64_t num_slots;
+    int32_t num_kv_heads;
+    int32_t page_log2;
+};
+
+struct DecodePlan {
+    int32_t split_tokens;       // multiple of kTile
+    int32_t max_splits;         // ceil(max_seq_len / split_tokens), >= 1
+};
+
+struct DecodeArgs {
+    const uint8_t *k_codes;
+    const uint8_t *v_codes;
+    const uint32_t *k_params;
+    const uint32_t *v_params;
+    const uint16_t *q;          // bf16 [S][Hq][128]
+    const int32_t *page_table;  // [S][max_pages]
+    const int32_t *seq_lens;    // [S]
+    float *out;                 // [S][Hq][128]
+    float *part_o;              // [S][Hq][max_splits][128]
+    float *part_ml;             // [S][Hq][max_splits][2]
+    int32_t num_seqs;
+    int32_t num_pages;          // page ids outside [0, num_pages) read page 0 instead
+    int32_t max_seq_len;        // longer seq_lens entries are clamped to it
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;              // Hq / Hkv
+    int32_t page_log2;
+    int32_t max_pages;
+    int32_t split_tokens;
+    int32_t max_splits;
+    float q_scale;              // sm_scale * log2(e)
+};
+
+// Returns a hipError_t value (0 = success).
+int launch_rotquant_write(int k_block, int v_block, const WriteArgs &a, void *stream);
+int launch_bf16_paged_write(const CopyArgs &a, void *stream);
+int launch_device_copy(void *dst, const void *src, size_t bytes, void *stream);
+int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream);
+const char *hip_error_string(int err);
+
+}  // namespace kvrq

@@ -1,0 +1,280 @@
+// Fused block-Hadamard rotation + token-wise INT4 quantisation + paged store
+// for gfx950 (SAW-INT4: K~ = quant(K H_blk), V~ = quant(V H_blk); wispaper.ai
+// blog, section 3 core formula, fused into the KV-cache write so that no
+// separate rotation launch exists and the arithmetic hides under the memory
+// time, same section, consequences 1 and 2).
+//
+// Work split: one 4-lane quad per (token, head, tensor) row of 128 channels.
+// Lane ql of the quad owns the 32 contiguous channels [32 ql, 32 ql + 32):
+//   * its bf16 input is 64 contiguous bytes (four 16-byte loads);
+//   * its INT4 output is 16 contiguous bytes (one 16-byte store);
+//   * butterfly widths 1..16 stay inside the lane (blocks of 16 and 32 need
+//     no cross-lane traffic at all); widths 32 and 64 pair lanes ql^1 and
+//     ql^2 of the quad through DPP quad permutes.
+// A workgroup of 256 lanes handles 64 consecutive tokens of one head of one
+// tensor, so its 64-byte row stores and 4-byte parameter stores land in
+// consecutive slots of a page.
+//
+// Bit-exactness: every step runs in IEEE binary32 in a fixed order --
+// butterfly widths 1, 2, 4, ... with (u+w, u-w), then * fp32(1/sqrt b); exact
+// min/max; correctly rounded (mx-mn)/15 and 1/scale; round-to-nearest-even
+// binary16 parameters; codes from the stored parameters.  Contraction is
+// disabled for this file (-ffp-contract=off) so no multiply-add is fused.
+#include <hip/hip_runtime.h>
+
+#include "kvrq_internal.h"
+
+namespace kvrq {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 value of 1/sqrt(b), the rotation's normalisation.
+template <int B> struct InvSqrt;
+template <> struct InvSqrt<16> { static constexpr float value = 0x1p-2f; };
+template <> struct InvSqrt<32> { static constexpr float value = 0x1.6a09e6p-3f; };
+template <> struct InvSqrt<64> { static constexpr float value = 0x1p-3f; };
+template <> struct InvSqrt<128> { static constexpr float value = 0x1.6a09e6p-4f; };
+
+// DPP quad permutes: value of lane ql^1 / ql^2 within the quad.
+__device__ __forceinline__ float quad_swap1(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_swap2(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4 &w, float *x)
+{
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        x[2 * m] = __uint_as_float(d[m] << 16);
+        x[2 * m + 1] = __uint_as_float(d[m] & 0xFFFF0000u);
+    }
+}
+
+// Block Walsh-Hadamard transform of the quad's 128 channels, this lane's 32.
+template <int B>
+__device__ __forceinline__ void rotate_row(float (&x)[32], int ql)
+{
+    if constexpr (B > 1) {
+        constexpr int in_lane = B < 32 ? B : 32;
+#pragma unroll
+        for (int h = 1; h < in_lane; h <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                if (i & h)
+                    continue;
+                const float u = x[i];
+                const float w = x[i + h];
+                x[i] = u + w;
+                x[i + h] = u - w;
+            }
+        }
+        if constexpr (B >= 64) {
+            // width 32: the lower lane keeps u + w, the upper lane u - w (= partner - self)
+            const float sgn = (ql & 1) ? -1.0f : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                x[i] = __builtin_fmaf(x[i], sgn, quad_swap1(x[i]));
+        }
+        if constexpr (B >= 128) {
+            const float sgn = (ql & 2) ? -1.0f : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                x[i] = __builtin_fmaf(x[i], sgn, quad_swap2(x[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            x[i] = x[i] * InvSqrt<B>::value;
+    }
+}
+
+// Rotate, quantise and store one row; called by all four lanes of a quad.
+template <int B>
+__device__ __forceinline__ void encode_row(const uint16_t *__restrict__ src, uint8_t *__restrict__ codes,
+                                           uint32_t *__restrict__ params, int64_t cell, int ql)
+{
+    float x[32];
+    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src + 32 * ql);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        bf16x8_to_f32(__builtin_nontemporal_load(s4 + j), x + 8 * j);
+
+    rotate_row<B>(x, ql);
+
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+        mn = fminf(mn, x[i]);
+        mx = fmaxf(mx, x[i]);
+    }
+    mn = fminf(mn, quad_swap1(mn));
+    mx = fmaxf(mx, quad_swap1(mx));
+    mn = fminf(mn, quad_swap2(mn));
+    mx = fmaxf(mx, quad_swap2(mx));
+    mn = mn + 0.0f;  // a zero minimum is stored as +0
+    mx = mx + 0.0f;
+
+    const float scale32 = (mx - mn) / 15.0f;
+    const _Float16 s16 = (_Float16)scale32;
+    const _Float16 z16 = (_Float16)mn;
+    const uint32_t s_bits = __builtin_bit_cast(uint16_t, s16);
+    const uint32_t z_bits = __builtin_bit_cast(uint16_t, z16);
+
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    if (s_bits != 0u) {
+        const float zf = (float)z16;
+        const float inv = 1.0f / (float)s16;
+        uint32_t pair[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            uint32_t bits[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float v = (x[2 * m + e] - zf) * inv;
+                // clamp to [0, 15], then round half to even: adding 1.5 * 2^23 leaves the
+                // nearest integer in the low mantissa bits
+                const float c = __builtin_amdgcn_fmed3f(v, 0.0f, 15.0f) + 12582912.0f;
+                bits[e] = __float_as_uint(c);
+            }
+            pair[m] = (bits[1] << 4) | bits[0];  // low byte = code(2m) | code(2m+1) << 4
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = __builtin_amdgcn_perm(pair[4 * k + 1], pair[4 * k], 0x0C0C0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(pair[4 * k + 3], pair[4 * k + 2], 0x0C0C0400u);
+            out[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+    }
+    u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + ql;
+    *dst = u32x4{out[0], out[1], out[2], out[3]};
+    if (ql == 0)
+        params[cell] = s_bits | (z_bits << 16);
+}
+
+template <int BK, int BV>
+__global__ __launch_bounds__(256) void rotquant_write_kernel(WriteArgs a)
+{
+    const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+    if (t >= a.num_tokens)
+        return;
+    const int32_t slot = a.slots[t];
+    if (slot < 0 || slot >= a.num_slots)
+        return;
+    const int h = blockIdx.y;
+    const int ql = threadIdx.x & 3;
+    const int64_t page = slot >> a.page_log2;
+    const int64_t off = slot & ((1 << a.page_log2) - 1);
+    const int64_t cell = ((page * a.num_kv_heads + h) << a.page_log2) + off;
+    if (blockIdx.z == 0)
+        encode_row<BK>(a.k + t * a.k_stride + h * kHeadDim, a.k_codes, a.k_params, cell, ql);
+    else
+        encode_row<BV>(a.v + t * a.v_stride + h * kHeadDim, a.v_codes, a.v_params, cell, ql);
+}
+
+// bf16 paged copy: the same slot scatter with no quantisation.
+__global__ __launch_bounds__(256) void bf16_paged_write_kernel(CopyArgs a)
+{
+    const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
+    if (t >= a.num_tokens)
+        return;
+    const int32_t slot = a.slots[t];
+    if (slot < 0 || slot >= a.num_slots)
+        return;
+    const int h = blockIdx.y;
+    const int ql = threadIdx.x & 3;
+    const int64_t page = slot >> a.page_log2;
+    const int64_t off = slot & ((1 << a.page_log2) - 1);
+    const int64_t cell = ((page * a.num_kv_heads + h) << a.page_log2) + off;
+    const uint16_t *src = blockIdx.z == 0 ? a.k + t * a.k_stride : a.v + t * a.v_stride;
+    uint16_t *dst = blockIdx.z == 0 ? a.k_cache : a.v_cache;
+    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src + h * kHeadDim + 32 * ql);
+    u32x4 *d4 = reinterpret_cast<u32x4 *>(dst + cell * kHeadDim + 32 * ql);
+    u32x4 w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        w[j] = __builtin_nontemporal_load(s4 + j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        d4[j] = w[j];
+}
+
+__global__ __launch_bounds__(256) void device_copy_kernel(u32x4 *__restrict__ dst,
+                                                          const u32x4 *__restrict__ src, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+template <int BK, int BV>
+hipError_t launch_bk_bv(const WriteArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)((a.num_tokens + 63) / 64), (unsigned)a.num_kv_heads, 2);
+    hipLaunchKernelGGL((rotquant_write_kernel<BK, BV>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int BK>
+hipError_t launch_bv(int v_block, const WriteArgs &a, hipStream_t s)
+{
+    switch (v_block) {
+    case 0: return launch_bk_bv<BK, 0>(a, s);
+    case 16: return launch_bk_bv<BK, 16>(a, s);
+    case 32: return launch_bk_bv<BK, 32>(a, s);
+    case 64: return launch_bk_bv<BK, 64>(a, s);
+    case 128: return launch_bk_bv<BK, 128>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int launch_rotquant_write(int k_block, int v_block, const WriteArgs &a, void *stream)
+{
+    if (a.num_tokens == 0)
+        return 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (k_block) {
+    case 0: return launch_bv<0>(v_block, a, s);
+    case 16: return launch_bv<16>(v_block, a, s);
+    case 32: return launch_bv<32>(v_block, a, s);
+    case 64: return launch_bv<64>(v_block, a, s);
+    case 128: return launch_bv<128>(v_block, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+int launch_bf16_paged_write(const CopyArgs &a, void *stream)
+{
+    if (a.num_tokens == 0)
+        return 0;
+    const dim3 grid((unsigned)((a.num_tokens + 63) / 64), (unsigned)a.num_kv_heads, 2);
+    hipLaunchKernelGGL(bf16_paged_write_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+    return hipGetLastError();
+}
+
+int launch_device_copy(void *dst, const void *src, size_t bytes, void *stream)
+{
+    const int64_t n = (int64_t)(bytes / 16);
+    if (n == 0)
+        return 0;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 256 * 16)
+        blocks = 256 * 16;
+    hipLaunchKernelGGL(device_copy_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<u32x4 *>(dst),
+                       static_cast<const u32x4 *>(src), n);
+    return hipGetLastError();
+}
+
+const char *hip_error_string(int err)
+{
+    return hipGetErrorString(static_cast<hipError_t>(err));
+}
+
+}  // namespace kvrq

@@ -1,0 +1,210 @@
+"""Host-side checks of the C-ABI library (no GPU needed, no kernel launched).
+
+* the library loads and exports exactly the functions ``include/kvrq.h`` declares;
+* every invalid argument returns the right status and a message, before any HIP call;
+* the page pool: identity and seeded orders, all-or-nothing growth, release and reuse,
+  page-table export with -1 padding, slot arithmetic.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def K():
+    import int4_kv_cache_rotquant_amd as K
+    if not os.path.exists(K.LIB_PATH):
+        from int4_kv_cache_rotquant_amd import build
+        build.build()
+    K.lib()
+    return K
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "kvrq.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^KVRQ_API [^;(]*?\b(\w+)\s*\(", text, re.M)))
+
+
+def test_exports_match_header(K):
+    names = _declared()
+    assert "kv_rotquant_write" in names and "kv_int4_paged_decode" in names
+    L = K.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    c_exports = {e for e in exported if not e.startswith("_Z") and not e.startswith("__hip")}
+    assert c_exports == set(names), c_exports ^ set(names)
+
+
+def _desc(K, **kw):
+    d = dict(head_dim=128, num_kv_heads=8, page_size=16, num_pages=64, k_block=128, v_block=0)
+    d.update(kw)
+    return K.CacheDesc(**d)
+
+
+def _bufs(K, aligned=True):
+    base = 0x10000 if aligned else 0x10004
+    return K.CacheBuffers(base, base + 0x100000, base + 0x200000, base + 0x300000)
+
+
+def _write(K, desc, bufs, k=0x40000000, v=0x50000000, T=4, ks=1024, vs=1024, slots=0x60000000):
+    L = K.lib()
+    return L.kv_rotquant_write(ctypes.byref(desc) if desc is not None else None,
+                               ctypes.byref(bufs) if bufs is not None else None, k, v, T, ks, vs,
+                               slots, None)
+
+
+def test_write_validation(K):
+    E = K
+    cases = [
+        (dict(desc=None), E.KVRQ_EINVAL, "descriptor"),
+        (dict(desc=_desc(K, head_dim=64)), E.KVRQ_EUNSUPPORTED, "head_dim"),
+        (dict(desc=_desc(K, num_kv_heads=0)), E.KVRQ_EINVAL, "num_kv_heads"),
+        (dict(desc=_desc(K, page_size=24)), E.KVRQ_EUNSUPPORTED, "page_size"),
+        (dict(desc=_desc(K, page_size=2048)), E.KVRQ_EUNSUPPORTED, "page_size"),
+        (dict(desc=_desc(K, num_pages=0)), E.KVRQ_EINVAL, "num_pages"),
+        (dict(desc=_desc(K, k_block=8)), E.KVRQ_EUNSUPPORTED, "blocks"),
+        (dict(desc=_desc(K, v_block=256)), E.KVRQ_EUNSUPPORTED, "blocks"),
+        (dict(bufs=None), E.KVRQ_EINVAL, "buffers"),
+        (dict(bufs=K.CacheBuffers(0, 0x1000, 0x2000, 0x3000)), E.KVRQ_EINVAL, "NULL"),
+        (dict(bufs=_bufs(K, aligned=False)), E.KVRQ_EINVAL, "aligned"),
+        (dict(T=-1), E.KVRQ_EINVAL, "num_tokens"),
+        (dict(T=1 << 31), E.KVRQ_EUNSUPPORTED, "num_tokens"),
+        (dict(k=0), E.KVRQ_EINVAL, "non-NULL"),
+        (dict(slots=0), E.KVRQ_EINVAL, "non-NULL"),
+        (dict(ks=1000), E.KVRQ_EINVAL, "strides"),
+        (dict(ks=1028), E.KVRQ_EINVAL, "multiples of 8"),
+        (dict(k=0x40000008), E.KVRQ_EINVAL, "aligned"),
+        (dict(slots=0x60000002), E.KVRQ_EINVAL, "aligned"),
+    ]
+    for kw, status, word in cases:
+        desc = kw.pop("desc", _desc(K))
+        bufs = kw.pop("bufs", _bufs(K))
+        st = _write(K, desc, bufs, **kw)
+        assert st == status, (kw, K.status_str(st), K.last_error())
+        assert word in K.last_error(), (word, K.last_error())
+    # an empty call is valid and launches nothing
+    assert _write(K, _desc(K), _bufs(K), T=0) == K.KVRQ_OK
+
+
+def test_decode_validation(K):
+    L = K.lib()
+    size = ctypes.c_size_t()
+
+    def ws(desc, S=4, Hq=64, maxlen=1000, split=0):
+        return L.kv_int4_paged_decode_workspace(ctypes.byref(desc), S, Hq, maxlen, split, ctypes.byref(size))
+
+    assert ws(_desc(K)) == K.KVRQ_OK and size.value > 0
+    assert ws(_desc(K), Hq=60) == K.KVRQ_EINVAL
+    assert ws(_desc(K), Hq=8 * 17) == K.KVRQ_EUNSUPPORTED
+    assert ws(_desc(K, page_size=8)) == K.KVRQ_EUNSUPPORTED
+    assert ws(_desc(K), split=48) == K.KVRQ_EINVAL
+    assert ws(_desc(K), maxlen=-1) == K.KVRQ_EINVAL
+    # workspace size grows with the number of splits
+    ws(_desc(K), split=64)
+    small = size.value
+    ws(_desc(K), split=32)
+    assert size.value > small
+
+    def dec(desc=None, q=0x1000, S=2, Hq=64, tab=0x2000, maxp=100, lens=0x3000, maxlen=1000,
+            scale=0.0, split=0, out=0x4000, wsp=0x5000, wsb=1 << 30):
+        desc = desc or _desc(K)
+        return L.kv_int4_paged_decode(ctypes.byref(desc), ctypes.byref(_bufs(K)), q, S, Hq, tab, maxp,
+                                      lens, maxlen, scale, split, out, wsp, wsb, None)
+
+    assert dec(S=0) == K.KVRQ_OK
+    assert dec(q=0) == K.KVRQ_EINVAL
+    assert dec(q=0x1004) == K.KVRQ_EINVAL
+    assert dec(maxp=10) == K.KVRQ_EINVAL            # 10 pages of 16 < 1000 tokens
+    assert dec(scale=float("nan")) == K.KVRQ_EINVAL
+    assert dec(wsb=16) == K.KVRQ_EWORKSPACE
+    assert "workspace" in K.last_error()
+    assert dec(wsp=0) == K.KVRQ_EWORKSPACE
+
+
+def test_helper_validation(K):
+    L = K.lib()
+    assert L.kvrq_device_copy(0x1000, 0x2000, 0, None) == K.KVRQ_OK
+    assert L.kvrq_device_copy(0x1000, 0x2000, 24, None) == K.KVRQ_EINVAL
+    assert L.kvrq_device_copy(0, 0x2000, 32, None) == K.KVRQ_EINVAL
+    d = _desc(K)
+    assert L.kvrq_bf16_paged_write(ctypes.byref(d), 0, 0x1000, 0x2000, 0x3000, 4, 1024, 1024,
+                                   0x4000, None) == K.KVRQ_EINVAL
+
+
+def test_status_strings(K):
+    for st, name in [(0, "KVRQ_OK"), (1, "KVRQ_EINVAL"), (2, "KVRQ_EUNSUPPORTED"), (3, "KVRQ_ENOPAGES"),
+                     (4, "KVRQ_EHIP"), (5, "KVRQ_EWORKSPACE"), (99, "KVRQ_UNKNOWN")]:
+        assert K.status_str(st) == name
+
+
+def test_cache_sizes(K):
+    cb, pb = K.kvrq_cache_sizes(_desc(K))
+    assert cb == 64 * 8 * 16 * 64 and pb == 64 * 8 * 16 * 4
+    # the footprint the pages call "a quarter of the space": 68 B vs 256 B per token-head
+    assert (cb + pb) / (64 * 8 * 16) == 68
+
+
+def test_pool_identity_order_and_slots(K):
+    p = K.Pool(num_pages=8, page_size=16, max_seqs=3, max_pages_per_seq=4)
+    p.seq_extend(0, 20)
+    p.seq_extend(1, 16)
+    tab, lens = p.page_table()
+    assert list(tab[0]) == [0, 1, -1, -1] and list(tab[1]) == [2, -1, -1, -1]
+    assert list(tab[2]) == [-1] * 4 and list(lens) == [20, 16, 0]
+    assert list(p.slots(0, 14, 4)) == [14, 15, 16, 17]
+    assert list(p.slots(1, 0, 2)) == [32, 33]
+    assert p.free_pages() == 5
+
+
+def test_pool_seeded_permutation_deterministic(K):
+    a = K.Pool(64, 16, 1, 64, shuffle_seed=1234)
+    b = K.Pool(64, 16, 1, 64, shuffle_seed=1234)
+    c = K.Pool(64, 16, 1, 64, shuffle_seed=99)
+    for p in (a, b, c):
+        p.seq_extend(0, 64 * 16)
+    ta, tb, tc = a.page_table()[0][0], b.page_table()[0][0], c.page_table()[0][0]
+    assert np.array_equal(ta, tb) and not np.array_equal(ta, tc)
+    assert sorted(ta) == list(range(64)) and not np.array_equal(ta, np.arange(64))
+
+
+def test_pool_all_or_nothing_and_reuse(K):
+    p = K.Pool(num_pages=4, page_size=16, max_seqs=2, max_pages_per_seq=3)
+    p.seq_extend(0, 40)                       # 3 pages
+    before = p.page_table()
+    with pytest.raises(K.KvrqError) as e:
+        p.seq_extend(1, 33)                   # needs 3, only 1 free
+    assert e.value.status == K.KVRQ_ENOPAGES
+    after = p.page_table()
+    assert np.array_equal(before[0], after[0]) and p.free_pages() == 1 and p.seq_len(1) == 0
+    with pytest.raises(K.KvrqError) as e:
+        p.seq_extend(0, 49)                   # beyond max_pages_per_seq
+    assert e.value.status == K.KVRQ_ENOPAGES
+    with pytest.raises(K.KvrqError) as e:
+        p.seq_extend(0, 10)                   # shrinking is not allowed
+    assert e.value.status == K.KVRQ_EINVAL
+    p.seq_release(0)
+    assert p.free_pages() == 4 and p.seq_len(0) == 0
+    p.seq_extend(1, 33)
+    assert sorted(p.page_table()[0][1][:3]) == sorted(set(p.page_table()[0][1][:3]))
+    with pytest.raises(K.KvrqError):
+        p.slots(1, 30, 4)                     # beyond the length
+    with pytest.raises(K.KvrqError):
+        p.seq_extend(5, 1)
+
+
+def test_pool_invalid_create(K):
+    with pytest.raises(K.KvrqError) as e:
+        K.Pool(0, 16, 1, 1)
+    assert e.value.status == K.KVRQ_EINVAL
+    with pytest.raises(K.KvrqError) as e:
+        K.Pool(4, 12, 1, 1)
+    assert e.value.status == K.KVRQ_EUNSUPPORTED

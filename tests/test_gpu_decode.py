@@ -1,0 +1,222 @@
+"""GPU parity of kv_int4_paged_decode against the oracle's fp64 decode (max abs error
+<= 2e-3 on fp32 outputs).  The cache the oracle reads is written by the oracle from the
+same seeded inputs (the write is bit-exact, checked in test_gpu_write.py).
+
+Covers the tiny case (G=1), the Qwen3-4B-like layer (G=4, 16 ragged sequences, page 16
+scattered), the high-concurrency shape (G=8, 256 log-normal sequences, sampled
+sequences checked), the 1M-token long context (G=8, K and V rotated, one KV head
+checked), split-count sweeps, page-table permutation invariance, GQA group sizes
+1..16, page sizes 16..128, every block pair, lengths 0, 1, 15..33 and tail tiles.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_harness import D, DECODE_ATOL, bf16_dev, decode_compare, log, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import int4_kv_cache_rotquant_amd as K
+    K.lib()
+    return K
+
+
+def _build(K, lens, Hkv, Hq, P, kb, vb, seed, permute=True, k_out=True, extra_pages=0):
+    rng = np.random.default_rng(seed)
+    prng = np.random.default_rng(seed + 999)
+    paging = W.assign_pages(prng if permute else None, list(lens), P, extra_pages=extra_pages)
+    T = int(sum(lens))
+    k = W.make_rows(rng, T, Hkv, W.OutlierSpec.random(rng, Hkv) if k_out else None)
+    v = W.make_rows(rng, T, Hkv)
+    slots = np.concatenate([paging.slots(s, 0, int(L)) for s, L in enumerate(lens)]) if T else \
+        np.zeros(0, np.int32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((len(lens), Hq, D)).astype(np.float32))
+    cache = K.PagedInt4Cache(paging.num_pages, Hkv, P, kb, vb, fill=0)
+    if T:
+        K.kv_rotquant_write(cache, bf16_dev(k), bf16_dev(v), to_dev(slots))
+    orc = oracle.Cache(paging.num_pages, Hkv, P, fill=0)
+    if T:
+        oracle.write(orc, k, v, slots, kb, vb)
+    tab = paging.page_table()
+    return cache, orc, q, tab, np.array(lens, np.int32)
+
+
+def _run(K, cache, q, tab, lens, split=0, sm_scale=0.0):
+    import torch
+    out = K.kv_int4_paged_decode(cache, bf16_dev(q), to_dev(tab), to_dev(lens),
+                                 int(max(lens.max(), 1)), sm_scale=sm_scale, split_tokens=split)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _ref(orc, q, tab, lens, Hkv, P, kb, vb, sm_scale=0.0):
+    arrays = (orc.k_codes, orc.v_codes, orc.k_params, orc.v_params)
+    return oracle.decode(q, arrays, tab, lens, Hkv, P, kb, vb, sm_scale)
+
+
+def test_tiny(K):
+    w = W.tiny()
+    k, v = w.kv()
+    cache = K.PagedInt4Cache(w.paging.num_pages, 1, 16, 128, 128, fill=0)
+    K.kv_rotquant_write(cache, bf16_dev(k), bf16_dev(v), to_dev(w.all_slots()))
+    orc = oracle.Cache(w.paging.num_pages, 1, 16, fill=0)
+    oracle.write(orc, k, v, w.all_slots(), 128, 128)
+    tab = w.paging.page_table()
+    out = _run(K, cache, w.q(), tab, w.seq_lens.astype(np.int32))
+    decode_compare(out, _ref(orc, w.q(), tab, w.seq_lens, 1, 16, 128, 128), "tiny")
+
+
+def test_qwen3_4b_like(K):
+    w = W.qwen3_4b_like()
+    k, v = w.kv()
+    cache = K.PagedInt4Cache(w.paging.num_pages, 8, 16, 64, 0, fill=0)
+    K.kv_rotquant_write(cache, bf16_dev(k), bf16_dev(v), to_dev(w.all_slots()))
+    orc = oracle.Cache(w.paging.num_pages, 8, 16, fill=0)
+    oracle.write(orc, k, v, w.all_slots(), 64, 0)
+    tab = w.paging.page_table()
+    lens = w.seq_lens.astype(np.int32)
+    q = w.q()
+    out = _run(K, cache, q, tab, lens)
+    decode_compare(out, _ref(orc, q, tab, lens, 8, 16, 64, 0), "qwen3_4b_like")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_group_sizes_and_tails(K, G):
+    lens = [1, 15, 16, 17, 31, 32, 33, 100, 257]
+    Hkv = 2
+    cache, orc, q, tab, L = _build(K, lens, Hkv, Hkv * G, 16, 128, 0, seed=G)
+    out = _run(K, cache, q, tab, L, split=64)
+    decode_compare(out, _ref(orc, q, tab, L, Hkv, 16, 128, 0), f"G{G}")
+
+
+@pytest.mark.parametrize("kb,vb", [(0, 0), (16, 16), (32, 64), (64, 128), (128, 128), (128, 32)])
+def test_block_pairs(K, kb, vb):
+    lens = [40, 300, 77]
+    cache, orc, q, tab, L = _build(K, lens, 2, 8, 16, kb, vb, seed=kb + vb)
+    out = _run(K, cache, q, tab, L)
+    decode_compare(out, _ref(orc, q, tab, L, 2, 16, kb, vb), f"blocks_{kb}_{vb}")
+
+
+@pytest.mark.parametrize("P", [16, 32, 64, 128])
+def test_page_sizes(K, P):
+    lens = [P - 3, 3 * P + 5, 500]
+    cache, orc, q, tab, L = _build(K, lens, 1, 4, P, 64, 64, seed=P)
+    out = _run(K, cache, q, tab, L, split=96 if P <= 32 else 128)
+    decode_compare(out, _ref(orc, q, tab, L, 1, P, 64, 64), f"P{P}")
+
+
+def test_split_sweep_consistent(K):
+    lens = [2049, 700, 33]
+    cache, orc, q, tab, L = _build(K, lens, 2, 16, 16, 128, 128, seed=11)
+    ref = _ref(orc, q, tab, L, 2, 16, 128, 128)
+    outs = []
+    for split in (32, 64, 256, 1024, 4096, 0):
+        out = _run(K, cache, q, tab, L, split=split)
+        decode_compare(out, ref, f"split{split}")
+        outs.append(out)
+    for o in outs[1:]:
+        # only the fp32 summation order differs between split counts
+        assert np.max(np.abs(o - outs[0])) < 1e-4
+
+
+def test_page_permutation_bit_identical(K):
+    lens = [500, 129]
+    c1, o1, q1, t1, L1 = _build(K, lens, 2, 8, 16, 128, 0, seed=12, permute=False)
+    c2, o2, q2, t2, L2 = _build(K, lens, 2, 8, 16, 128, 0, seed=12, permute=True)
+    assert np.array_equal(q1, q2)
+    a = _run(K, c1, q1, t1, L1)
+    b = _run(K, c2, q2, t2, L2)
+    assert np.array_equal(a, b)
+    decode_compare(a, _ref(o1, q1, t1, L1, 2, 16, 128, 0), "perm")
+
+
+def test_zero_length_and_scale_override(K):
+    lens = [0, 64, 1]
+    cache, orc, q, tab, L = _build(K, lens, 1, 2, 16, 32, 0, seed=13, extra_pages=1)
+    tab[0, 0] = 0  # a valid page, never read
+    out = _run(K, cache, q, tab, L, sm_scale=0.3)
+    assert np.all(out[0] == 0)
+    decode_compare(out, _ref(orc, q, tab, L, 1, 16, 32, 0, sm_scale=0.3), "len0_scale")
+
+
+def test_high_concurrency_sampled(K):
+    """256 sequences with log-normal lengths (median 8192, clip [512, 32768]), Hq=64, Hkv=8,
+    page 16 scattered over the ~3 GB pool: the full decode launch, with eight sequences
+    (shortest, longest and six more) checked against the oracle."""
+    import torch
+    w = W.qwen3_32b_like_decode()
+    lens = (w.seq_lens + 1).astype(np.int32)   # the step's new token is included
+    S, Hkv, Hq, P = w.num_seqs, 8, 64, 16
+    check = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] + list(range(0, S, 43))))[:8]
+    cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, 128, 0, fill=0)
+    host_rows = {}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    for s in range(S):
+        slots = w.paging.slots(s, 0, int(lens[s]))
+        if s in check:
+            rng = w.rng(1000 + s)
+            k = W.make_rows(rng, int(lens[s]), Hkv, w.k_out)
+            v = W.make_rows(rng, int(lens[s]), Hkv)
+            host_rows[s] = (k, v, slots)
+            kd, vd = bf16_dev(k), bf16_dev(v)
+        else:
+            kd = W.make_rows_torch(gen, int(lens[s]), Hkv, w.k_out, "cuda")
+            vd = W.make_rows_torch(gen, int(lens[s]), Hkv, None, "cuda")
+        K.kv_rotquant_write(cache, kd, vd, to_dev(slots))
+    q = W.f32_to_bf16_bits(w.rng(3).standard_normal((S, Hq, D)).astype(np.float32))
+    tab = w.paging.page_table()
+    log(f"high-concurrency: total tokens {int(lens.sum())}, checking {check}")
+    out = _run(K, cache, q, tab, lens)
+    for s in check:
+        k, v, slots = host_rows[s]
+        pages = np.unique(slots // P)
+        remap = {int(p): i for i, p in enumerate(pages)}
+        local = np.array([remap[int(x) // P] * P + int(x) % P for x in slots], np.int32)
+        orc = oracle.Cache(len(pages), Hkv, P, fill=0)
+        oracle.write(orc, k, v, local, 128, 0)
+        ltab = np.array([[remap[int(p)] for p in tab[s, :len(pages)]]], np.int32)
+        ref = _ref(orc, q[s:s + 1], ltab, lens[s:s + 1], Hkv, P, 128, 0)
+        decode_compare(out[s:s + 1], ref, f"hc_seq{s}_L{lens[s]}")
+    torch.cuda.synchronize()
+
+
+def test_long_context_one_kv_head(K):
+    """One 1,048,576-token sequence, Hq=64, Hkv=8, page 64 scattered, K and V rotated with
+    block 128, filled by 64 writes of 16384 tokens; KV head 0's eight query heads are
+    checked against the oracle."""
+    import torch
+    w = W.long_context()
+    C, L, Hkv, Hq, P = w.notes["chunk"], 1 << 20, 8, 64, 64
+    cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, 128, 128, fill=0)
+    k0 = np.empty((L, 1, D), np.uint16)
+    v0 = np.empty((L, 1, D), np.uint16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    one = W.OutlierSpec
+    for c in range(L // C):
+        # KV head 0 from the seeded host generator (it is checked), heads 1..7 on the device
+        rng = w.rng(100 + c)
+        k0[c * C:(c + 1) * C] = W.make_rows(rng, C, 1, one(w.k_out.mult[:1]))
+        v0[c * C:(c + 1) * C] = W.make_rows(rng, C, 1, one(w.v_out.mult[:1]))
+        krest = W.make_rows_torch(gen, C, Hkv - 1, one(w.k_out.mult[1:]), "cuda")
+        vrest = W.make_rows_torch(gen, C, Hkv - 1, one(w.v_out.mult[1:]), "cuda")
+        k = torch.cat([bf16_dev(k0[c * C:(c + 1) * C]), krest], dim=1)
+        v = torch.cat([bf16_dev(v0[c * C:(c + 1) * C]), vrest], dim=1)
+        K.kv_rotquant_write(cache, k, v, to_dev(w.paging.slots(0, c * C, C)))
+    q = W.f32_to_bf16_bits(w.rng(3).standard_normal((1, Hq, D)).astype(np.float32))
+    tab = w.paging.page_table()
+    lens = np.array([L], np.int32)
+    out = _run(K, cache, q, tab, lens)
+    log("long context: oracle write of KV head 0")
+    orc = oracle.Cache(w.paging.num_pages, 1, P, fill=0)
+    oracle.write(orc, k0, v0, w.paging.slots(0, 0, L), 128, 128)
+    ref = _ref(orc, q[:, :8].copy(), tab, lens, 1, P, 128, 128)
+    decode_compare(out[:, :8], ref, "long_context_h0")
+    torch.cuda.synchronize()
