@@ -191,8 +191,8 @@ KVRQ_API kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, in
  *                   zero row
  *   max_seq_len     host bound on every L, used to plan the splits
  *   sm_scale        softmax scale; <= 0 selects 1/sqrt(head_dim)
- *   split_tokens    tokens per split-K partition; 0 = automatic, otherwise a
- *                   multiple of 32
+ *   split_tokens    tokens per split-K partition (one workgroup of four
+ *                   waves); 0 = automatic, otherwise a multiple of 128
  *   out             device fp32 [num_seqs][num_q_heads][head_dim]
  *   workspace       device scratch of workspace_bytes >= the size reported by
  *                   kv_int4_paged_decode_workspace (16-byte aligned)

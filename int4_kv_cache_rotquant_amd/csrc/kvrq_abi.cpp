@@ -106,19 +106,23 @@ kvrq_status hip_status(int err, const char *what)
     return fail(KVRQ_EHIP, "%s: %s", what, kvrq::hip_error_string(err));
 }
 
-// Decode split plan: partitions of split_tokens (a multiple of 32) chosen so
-// that an upper bound of the total work fills the chip several times over
-// while each wave still streams a few hundred tokens.
+// Decode split plan.  A workgroup of kDecodeWaves waves takes split_tokens
+// consecutive tokens of one (sequence, KV head), each wave a quarter.  The
+// automatic size gives every wave split_tokens/4 = clamp(S * Hkv * max_len /
+// 8192, 64, 1024) tokens (a multiple of 32): an upper bound of the work spread
+// over ~8192 waves, several per SIMD, while each wave still streams enough
+// tiles to hide its prologue and the split partials stay a few percent of the
+// cache bytes.
 kvrq::DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                              int32_t split_tokens)
 {
     kvrq::DecodePlan p;
     if (split_tokens <= 0) {
         const int64_t work = int64_t(num_seqs) * num_kv_heads * std::max<int32_t>(max_seq_len, 1);
-        int64_t st = work / 8192;
-        st = std::max<int64_t>(256, std::min<int64_t>(2048, st));
-        st = (st + kvrq::kTile - 1) / kvrq::kTile * kvrq::kTile;
-        split_tokens = (int32_t)st;
+        int64_t wt = work / 8192;
+        wt = std::max<int64_t>(64, std::min<int64_t>(1024, wt));
+        wt = (wt + kvrq::kTile - 1) / kvrq::kTile * kvrq::kTile;
+        split_tokens = (int32_t)(wt * kvrq::kDecodeWaves);
     }
     p.split_tokens = split_tokens;
     p.max_splits = std::max<int32_t>(1, (max_seq_len + split_tokens - 1) / split_tokens);
@@ -148,8 +152,9 @@ kvrq_status check_decode_shape(const kvrq_cache_desc *d, int32_t num_seqs, int32
         return fail(KVRQ_EUNSUPPORTED, "decode needs page_size >= 16 (got %d)", d->page_size);
     if (max_seq_len < 0)
         return fail(KVRQ_EINVAL, "max_seq_len must be >= 0");
-    if (split_tokens < 0 || split_tokens % kvrq::kTile)
-        return fail(KVRQ_EINVAL, "split_tokens must be 0 or a positive multiple of %d", kvrq::kTile);
+    if (split_tokens < 0 || split_tokens % (kvrq::kTile * kvrq::kDecodeWaves))
+        return fail(KVRQ_EINVAL, "split_tokens must be 0 or a positive multiple of %d",
+                    kvrq::kTile * kvrq::kDecodeWaves);
     if (num_seqs > 65535)
         return fail(KVRQ_EUNSUPPORTED, "num_seqs above 65535");
     return KVRQ_OK;

@@ -11,7 +11,10 @@ namespace kvrq {
 constexpr int kHeadDim = 128;       // channels per head
 constexpr int kRowCodeBytes = 64;   // packed INT4 bytes per (token, head) row
 constexpr int kTile = 32;           // decode tokens per inner step
+constexpr int kWriteTile = 32;      // write tokens per wave step (two lanes per row)
+constexpr int kWriteWgsPerCu = 3;   // resident write workgroups per CU (3 waves per SIMD)
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave
+constexpr int kDecodeWaves = 4;     // waves per decode workgroup, each on its own token range
 
 struct WriteArgs {
     const uint16_t *k;          // bf16 bits
@@ -44,7 +47,7 @@ struct CopyArgs {
 };
 
 struct DecodePlan {
-    int32_t split_tokens;       // multiple of kTile
+    int32_t split_tokens;       // tokens per workgroup, multiple of kTile * kDecodeWaves
     int32_t max_splits;         // ceil(max_seq_len / split_tokens), >= 1
 };
 

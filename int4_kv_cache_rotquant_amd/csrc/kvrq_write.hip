@@ -4,16 +4,19 @@
 // separate rotation launch exists and the arithmetic hides under the memory
 // time, same section, consequences 1 and 2).
 //
-// Work split: one 4-lane quad per (token, head, tensor) row of 128 channels.
-// Lane ql of the quad owns the 32 contiguous channels [32 ql, 32 ql + 32):
-//   * its bf16 input is 64 contiguous bytes (four 16-byte loads);
-//   * its INT4 output is 16 contiguous bytes (one 16-byte store);
-//   * butterfly widths 1..16 stay inside the lane (blocks of 16 and 32 need
-//     no cross-lane traffic at all); widths 32 and 64 pair lanes ql^1 and
-//     ql^2 of the quad through DPP quad permutes.
-// A workgroup of 256 lanes handles 64 consecutive tokens of one head of one
-// tensor, so its 64-byte row stores and 4-byte parameter stores land in
-// consecutive slots of a page.
+// Work split: two lanes per (token, head, tensor) row of 128 channels; lane
+// half hl of the pair owns the 64 contiguous channels [64 hl, 64 hl + 64):
+//   * its bf16 input is 128 contiguous bytes (eight 16-byte loads);
+//   * its INT4 output is 32 contiguous bytes (two 16-byte stores);
+//   * butterfly widths 1..32 stay inside the lane (blocks of 16, 32 and 64
+//     need no cross-lane traffic); width 64 (block 128) pairs the two lanes
+//     through one DPP quad permute.
+// A wave encodes tiles of 32 consecutive tokens of one head, the K tile and then
+// the V tile, so its 64-byte row stores and 4-byte parameter stores land in
+// consecutive slots of a page.  Waves are persistent: each walks the tile
+// pairs with a stride of the grid's wave count and keeps the next tile's loads
+// in flight while it encodes the current one, so memory time and arithmetic
+// overlap.
 //
 // Bit-exactness: every step runs in IEEE binary32 in a fixed order --
 // butterfly widths 1, 2, 4, ... with (u+w, u-w), then * fp32(1/sqrt b); exact
@@ -56,16 +59,16 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4 &w, float *x)
     }
 }
 
-// Block Walsh-Hadamard transform of the quad's 128 channels, this lane's 32.
+// Block Walsh-Hadamard transform of a row, this lane's 64 channels.
 template <int B>
-__device__ __forceinline__ void rotate_row(float (&x)[32], int ql)
+__device__ __forceinline__ void rotate_row(float (&x)[64], int hl)
 {
     if constexpr (B > 1) {
-        constexpr int in_lane = B < 32 ? B : 32;
+        constexpr int in_lane = B < 64 ? B : 64;
 #pragma unroll
         for (int h = 1; h < in_lane; h <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
+            for (int i = 0; i < 64; ++i) {
                 if (i & h)
                     continue;
                 const float u = x[i];
@@ -74,48 +77,58 @@ __device__ __forceinline__ void rotate_row(float (&x)[32], int ql)
                 x[i + h] = u - w;
             }
         }
-        if constexpr (B >= 64) {
-            // width 32: the lower lane keeps u + w, the upper lane u - w (= partner - self)
-            const float sgn = (ql & 1) ? -1.0f : 1.0f;
+        if constexpr (B >= 128) {
+            // width 64: the lower lane keeps u + w, the upper lane u - w (= partner - self)
+            const float sgn = hl ? -1.0f : 1.0f;
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
+            for (int i = 0; i < 64; ++i)
                 x[i] = __builtin_fmaf(x[i], sgn, quad_swap1(x[i]));
         }
-        if constexpr (B >= 128) {
-            const float sgn = (ql & 2) ? -1.0f : 1.0f;
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-                x[i] = __builtin_fmaf(x[i], sgn, quad_swap2(x[i]));
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
+        for (int i = 0; i < 64; ++i)
             x[i] = x[i] * InvSqrt<B>::value;
     }
 }
 
-// Rotate, quantise and store one row; called by all four lanes of a quad.
-template <int B>
-__device__ __forceinline__ void encode_row(const uint16_t *__restrict__ src, uint8_t *__restrict__ codes,
-                                           uint32_t *__restrict__ params, int64_t cell, int ql)
-{
-    float x[32];
-    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src + 32 * ql);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        bf16x8_to_f32(__builtin_nontemporal_load(s4 + j), x + 8 * j);
+// The raw input of one tile as this lane holds it.
+struct RowLoad {
+    u32x4 raw[8];     // 64 bf16 channels
+    int32_t slot;     // < 0: nothing to store
+};
 
-    rotate_row<B>(x, ql);
+__device__ __forceinline__ void load_row(RowLoad &R, const uint16_t *src_base, int64_t stride,
+                                         const int32_t *slots, int64_t t, int64_t num_tokens, int hl)
+{
+    if (t < num_tokens) {
+        R.slot = slots[t];
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src_base + t * stride + 64 * hl);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            R.raw[j] = s4[j];
+    } else {
+        R.slot = -1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            R.raw[j] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Rotate, quantise and store one row held in x; called by both lanes of the pair.
+template <int B>
+__device__ __forceinline__ void encode_row(float (&x)[64], int32_t slot, uint8_t *__restrict__ codes,
+                                           uint32_t *__restrict__ params, int64_t num_slots,
+                                           int num_kv_heads, int page_log2, int h, int hl)
+{
+    rotate_row<B>(x, hl);
 
     float mn = x[0], mx = x[0];
 #pragma unroll
-    for (int i = 1; i < 32; ++i) {
+    for (int i = 1; i < 64; ++i) {
         mn = fminf(mn, x[i]);
         mx = fmaxf(mx, x[i]);
     }
     mn = fminf(mn, quad_swap1(mn));
     mx = fmaxf(mx, quad_swap1(mx));
-    mn = fminf(mn, quad_swap2(mn));
-    mx = fmaxf(mx, quad_swap2(mx));
     mn = mn + 0.0f;  // a zero minimum is stored as +0
     mx = mx + 0.0f;
 
@@ -125,55 +138,96 @@ __device__ __forceinline__ void encode_row(const uint16_t *__restrict__ src, uin
     const uint32_t s_bits = __builtin_bit_cast(uint16_t, s16);
     const uint32_t z_bits = __builtin_bit_cast(uint16_t, z16);
 
-    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     if (s_bits != 0u) {
         const float zf = (float)z16;
         const float inv = 1.0f / (float)s16;
-        uint32_t pair[16];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            uint32_t bits[2];
+        for (int k = 0; k < 8; ++k) {
+            uint32_t pair[4];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float v = (x[2 * m + e] - zf) * inv;
-                // clamp to [0, 15], then round half to even: adding 1.5 * 2^23 leaves the
-                // nearest integer in the low mantissa bits
-                const float c = __builtin_amdgcn_fmed3f(v, 0.0f, 15.0f) + 12582912.0f;
-                bits[e] = __float_as_uint(c);
+            for (int m = 0; m < 4; ++m) {
+                uint32_t bits[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float v = (x[8 * k + 2 * m + e] - zf) * inv;
+                    // clamp to [0, 15], then round half to even: adding 1.5 * 2^23 leaves
+                    // the nearest integer in the low mantissa bits
+                    const float c = __builtin_amdgcn_fmed3f(v, 0.0f, 15.0f) + 12582912.0f;
+                    bits[e] = __float_as_uint(c);
+                }
+                pair[m] = (bits[1] << 4) | bits[0];  // low byte = code(2m) | code(2m+1) << 4
             }
-            pair[m] = (bits[1] << 4) | bits[0];  // low byte = code(2m) | code(2m+1) << 4
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = __builtin_amdgcn_perm(pair[4 * k + 1], pair[4 * k], 0x0C0C0400u);
-            const uint32_t hi = __builtin_amdgcn_perm(pair[4 * k + 3], pair[4 * k + 2], 0x0C0C0400u);
+            const uint32_t lo = __builtin_amdgcn_perm(pair[1], pair[0], 0x0C0C0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(pair[3], pair[2], 0x0C0C0400u);
             out[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
         }
     }
-    u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + ql;
-    *dst = u32x4{out[0], out[1], out[2], out[3]};
-    if (ql == 0)
-        params[cell] = s_bits | (z_bits << 16);
+    if (slot >= 0 && slot < num_slots) {
+        const int64_t page = slot >> page_log2;
+        const int64_t off = slot & ((1 << page_log2) - 1);
+        const int64_t cell = ((page * num_kv_heads + h) << page_log2) + off;
+        u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + 2 * hl;
+        dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+        dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+        if (hl == 0)
+            params[cell] = s_bits | (z_bits << 16);
+    }
 }
 
+// Each wave walks tile pairs: the K tile and the V tile of the same 32 tokens of one
+// head, pair i covering head i % num_kv_heads, so waves that run side by side read all
+// heads of the same tokens (whole 2 KB-per-token input rows at once).  The loop is unrolled over the two
+// tensors, so each half is compiled for its own block size, and K and V work is spread
+// evenly over the waves.
 template <int BK, int BV>
-__global__ __launch_bounds__(256) void rotquant_write_kernel(WriteArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void rotquant_write_kernel(WriteArgs a)
 {
-    const int64_t t = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);
-    if (t >= a.num_tokens)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hl = lane & 1;
+    const int row = lane >> 1;
+    const int64_t tiles_per_head = (a.num_tokens + kWriteTile - 1) / kWriteTile;
+    const int64_t num_pairs = tiles_per_head * a.num_kv_heads;
+    const int64_t stride_w = (int64_t)gridDim.x * (blockDim.x >> 6);
+    int64_t pair = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+    if (pair >= num_pairs)
         return;
-    const int32_t slot = a.slots[t];
-    if (slot < 0 || slot >= a.num_slots)
-        return;
-    const int h = blockIdx.y;
-    const int ql = threadIdx.x & 3;
-    const int64_t page = slot >> a.page_log2;
-    const int64_t off = slot & ((1 << a.page_log2) - 1);
-    const int64_t cell = ((page * a.num_kv_heads + h) << a.page_log2) + off;
-    if (blockIdx.z == 0)
-        encode_row<BK>(a.k + t * a.k_stride + h * kHeadDim, a.k_codes, a.k_params, cell, ql);
-    else
-        encode_row<BV>(a.v + t * a.v_stride + h * kHeadDim, a.v_codes, a.v_params, cell, ql);
+
+    auto issue = [&](RowLoad &R, const uint16_t *src, int64_t stride, int64_t pr) {
+        const int64_t tt = pr / a.num_kv_heads;
+        const int64_t h = pr - tt * a.num_kv_heads;
+        const int64_t t0 = tt * kWriteTile;
+        load_row(R, src + h * kHeadDim, stride, a.slots, t0 + row, a.num_tokens, hl);
+    };
+
+    // One register set: once a tile's bf16 input is widened to fp32, the same registers
+    // take the next tile's loads, which then fly while this tile is encoded.
+    RowLoad R;
+    issue(R, a.k, a.k_stride, pair);
+    while (true) {
+        const int h = (int)(pair % a.num_kv_heads);
+        float x[64];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            bf16x8_to_f32(R.raw[j], x + 8 * j);
+        int32_t slot = R.slot;
+        issue(R, a.v, a.v_stride, pair);
+        encode_row<BK>(x, slot, a.k_codes, a.k_params, a.num_slots, a.num_kv_heads, a.page_log2, h, hl);
+
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            bf16x8_to_f32(R.raw[j], x + 8 * j);
+        slot = R.slot;
+        const int64_t next = pair + stride_w;
+        if (next < num_pairs)
+            issue(R, a.k, a.k_stride, next);
+        encode_row<BV>(x, slot, a.v_codes, a.v_params, a.num_slots, a.num_kv_heads, a.page_log2, h, hl);
+        if (next >= num_pairs)
+            break;
+        pair = next;
+    }
 }
 
 // bf16 paged copy: the same slot scatter with no quantisation.
@@ -197,7 +251,7 @@ __global__ __launch_bounds__(256) void bf16_paged_write_kernel(CopyArgs a)
     u32x4 w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        w[j] = __builtin_nontemporal_load(s4 + j);
+        w[j] = s4[j];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         d4[j] = w[j];
@@ -208,14 +262,31 @@ __global__ __launch_bounds__(256) void device_copy_kernel(u32x4 *__restrict__ ds
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-        dst[i] = __builtin_nontemporal_load(src + i);
+        dst[i] = src[i];
+}
+
+// Persistent grid: enough workgroups for a few resident waves per SIMD, each wave
+// then walks several tiles so its next loads overlap its current arithmetic.
+unsigned write_grid(const WriteArgs &a)
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+    }
+    // one wave per (K, V) tile pair at most, four waves per workgroup
+    const int64_t pairs = (a.num_tokens + kWriteTile - 1) / kWriteTile * a.num_kv_heads;
+    const int64_t wgs = (pairs + 3) / 4;
+    const int64_t cap = (int64_t)cus * kWriteWgsPerCu;
+    return (unsigned)(wgs < cap ? wgs : cap);
 }
 
 template <int BK, int BV>
 hipError_t launch_bk_bv(const WriteArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)((a.num_tokens + 63) / 64), (unsigned)a.num_kv_heads, 2);
-    hipLaunchKernelGGL((rotquant_write_kernel<BK, BV>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((rotquant_write_kernel<BK, BV>), dim3(write_grid(a)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -107,11 +107,12 @@ def test_decode_validation(K):
     assert ws(_desc(K), Hq=8 * 17) == K.KVRQ_EUNSUPPORTED
     assert ws(_desc(K, page_size=8)) == K.KVRQ_EUNSUPPORTED
     assert ws(_desc(K), split=48) == K.KVRQ_EINVAL
+    assert ws(_desc(K), split=96) == K.KVRQ_EINVAL
     assert ws(_desc(K), maxlen=-1) == K.KVRQ_EINVAL
     # workspace size grows with the number of splits
-    ws(_desc(K), split=64)
+    ws(_desc(K), split=256)
     small = size.value
-    ws(_desc(K), split=32)
+    ws(_desc(K), split=128)
     assert size.value > small
 
     def dec(desc=None, q=0x1000, S=2, Hq=64, tab=0x2000, maxp=100, lens=0x3000, maxlen=1000,

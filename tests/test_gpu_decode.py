@@ -91,7 +91,7 @@ def test_group_sizes_and_tails(K, G):
     lens = [1, 15, 16, 17, 31, 32, 33, 100, 257]
     Hkv = 2
     cache, orc, q, tab, L = _build(K, lens, Hkv, Hkv * G, 16, 128, 0, seed=G)
-    out = _run(K, cache, q, tab, L, split=64)
+    out = _run(K, cache, q, tab, L, split=128)
     decode_compare(out, _ref(orc, q, tab, L, Hkv, 16, 128, 0), f"G{G}")
 
 
@@ -107,7 +107,7 @@ def test_block_pairs(K, kb, vb):
 def test_page_sizes(K, P):
     lens = [P - 3, 3 * P + 5, 500]
     cache, orc, q, tab, L = _build(K, lens, 1, 4, P, 64, 64, seed=P)
-    out = _run(K, cache, q, tab, L, split=96 if P <= 32 else 128)
+    out = _run(K, cache, q, tab, L, split=128 if P <= 32 else 256)
     decode_compare(out, _ref(orc, q, tab, L, 1, P, 64, 64), f"P{P}")
 
 
@@ -116,7 +116,7 @@ def test_split_sweep_consistent(K):
     cache, orc, q, tab, L = _build(K, lens, 2, 16, 16, 128, 128, seed=11)
     ref = _ref(orc, q, tab, L, 2, 16, 128, 128)
     outs = []
-    for split in (32, 64, 256, 1024, 4096, 0):
+    for split in (128, 256, 512, 1024, 4096, 8192, 0):
         out = _run(K, cache, q, tab, L, split=split)
         decode_compare(out, ref, f"split{split}")
         outs.append(out)
