@@ -110,6 +110,10 @@ __device__ __forceinline__ uint32_t centred_codes(uint32_t masked, bool upper)
 // query quantised to 22 bits (three int8 slices), exact in the int32 accumulators.
 constexpr uint32_t kNibBytes = 0x0F0F0F0Fu;
 
+// Lazy softmax maximum (base 2): weights exp2(score - m) may grow to 2^kLazyMax before
+// the reference max m moves and the accumulators are rescaled.
+constexpr float kLazyMax = 8.0f;
+
 __device__ __forceinline__ i32x4 mfma_i8(const i32x4 &a, const i32x4 &b, const i32x4 &c)
 {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
@@ -253,13 +257,16 @@ struct WaveState {
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
         tmax = fmaxf(tmax, wave_xor(tmax, 16));
         tmax = fmaxf(tmax, wave_xor(tmax, 32));
-        const float m_new = fmaxf(m, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);   // softmax rescale of l, z, acc
-        const bool moved = m_new > m;
+        // The reference max moves only when a score exceeds it by more than kLazyMax (base
+        // 2), so the accumulators are rarely rescaled; weights stay below 2^kLazyMax.
+        const bool moved = tmax > m + kLazyMax;
+        const float m_new = moved ? tmax : m;
+        const float alpha = moved ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
         m = m_new;
         // Weight exponent: the f16 high and low parts of p * scale_V * 2^E keep ~22 bits only
         // while the low part stays a normal f16, so E puts the tile's largest possible weight
-        // (p <= 1) just below 2^14.  E only decreases; the accumulators follow exactly.
+        // (p <= 2^kLazyMax) just below 2^14.  E only decreases; the accumulators follow
+        // exactly.
         float smax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                            fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
         smax = fmaxf(smax, wave_xor(smax, 16));
@@ -269,7 +276,7 @@ struct WaveState {
         if (smax > 0.0f) {
             int ex;
             frexpf(smax, &ex);
-            const int e_tile = 14 - ex;
+            const int e_tile = 14 - (int)kLazyMax - ex;
             if (e_tile < E) {                      // uniform across the wave
                 acc_f = ldexpf(alpha, e_tile - E);
                 E = e_tile;

@@ -11,8 +11,9 @@ namespace kvrq {
 constexpr int kHeadDim = 128;       // channels per head
 constexpr int kRowCodeBytes = 64;   // packed INT4 bytes per (token, head) row
 constexpr int kTile = 32;           // decode tokens per inner step
-constexpr int kWriteTile = 32;      // write tokens per wave step (two lanes per row)
-constexpr int kWriteWgsPerCu = 3;   // resident write workgroups per CU (3 waves per SIMD)
+constexpr int kWriteTile = 16;      // write tokens per wave step (four lanes per row)
+constexpr int kWriteWavesPerSimd = 5;  // occupancy target (the kernel fits six)
+constexpr int kWriteWgsPerCu = 6;      // 256-lane workgroups per CU: one wave per SIMD each
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave
 constexpr int kDecodeWaves = 4;     // waves per decode workgroup, each on its own token range
 

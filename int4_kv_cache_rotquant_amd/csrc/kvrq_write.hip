@@ -4,19 +4,19 @@
 // separate rotation launch exists and the arithmetic hides under the memory
 // time, same section, consequences 1 and 2).
 //
-// Work split: two lanes per (token, head, tensor) row of 128 channels; lane
-// half hl of the pair owns the 64 contiguous channels [64 hl, 64 hl + 64):
-//   * its bf16 input is 128 contiguous bytes (eight 16-byte loads);
-//   * its INT4 output is 32 contiguous bytes (two 16-byte stores);
-//   * butterfly widths 1..32 stay inside the lane (blocks of 16, 32 and 64
-//     need no cross-lane traffic); width 64 (block 128) pairs the two lanes
-//     through one DPP quad permute.
-// A wave encodes tiles of 32 consecutive tokens of one head, the K tile and then
+// Work split: four lanes (a quad) per (token, head, tensor) row of 128 channels;
+// lane ql of the quad owns the 32 contiguous channels [32 ql, 32 ql + 32):
+//   * its bf16 input is 64 contiguous bytes (four 16-byte loads);
+//   * its INT4 output is 16 contiguous bytes (one 16-byte store);
+//   * butterfly widths 1..16 stay inside the lane (blocks of 16 and 32 need no
+//     cross-lane traffic); widths 32 and 64 pair lanes ql^1 and ql^2 of the
+//     quad through DPP quad permutes.
+// A wave encodes tiles of 16 consecutive tokens of one head, the K tile and then
 // the V tile, so its 64-byte row stores and 4-byte parameter stores land in
-// consecutive slots of a page.  Waves are persistent: each walks the tile
-// pairs with a stride of the grid's wave count and keeps the next tile's loads
-// in flight while it encodes the current one, so memory time and arithmetic
-// overlap.
+// consecutive slots of a page.  Waves are persistent: each walks the tile pairs
+// with a stride of the grid's wave count and keeps the next tile's loads in
+// flight while it encodes the current one.  The small per-lane footprint keeps
+// five waves per SIMD resident, enough to cover memory latency with arithmetic.
 //
 // Bit-exactness: every step runs in IEEE binary32 in a fixed order --
 // butterfly widths 1, 2, 4, ... with (u+w, u-w), then * fp32(1/sqrt b); exact
@@ -59,16 +59,16 @@ __device__ __forceinline__ void bf16x8_to_f32(const u32x4 &w, float *x)
     }
 }
 
-// Block Walsh-Hadamard transform of a row, this lane's 64 channels.
+// Block Walsh-Hadamard transform of a row, this lane's 32 channels.
 template <int B>
-__device__ __forceinline__ void rotate_row(float (&x)[64], int hl)
+__device__ __forceinline__ void rotate_row(float (&x)[32], int ql)
 {
     if constexpr (B > 1) {
-        constexpr int in_lane = B < 64 ? B : 64;
+        constexpr int in_lane = B < 32 ? B : 32;
 #pragma unroll
         for (int h = 1; h < in_lane; h <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 64; ++i) {
+            for (int i = 0; i < 32; ++i) {
                 if (i & h)
                     continue;
                 const float u = x[i];
@@ -77,58 +77,66 @@ __device__ __forceinline__ void rotate_row(float (&x)[64], int hl)
                 x[i + h] = u - w;
             }
         }
-        if constexpr (B >= 128) {
-            // width 64: the lower lane keeps u + w, the upper lane u - w (= partner - self)
-            const float sgn = hl ? -1.0f : 1.0f;
+        if constexpr (B >= 64) {
+            // width 32: the lower lane keeps u + w, the upper lane u - w (= partner - self)
+            const float sgn = (ql & 1) ? -1.0f : 1.0f;
 #pragma unroll
-            for (int i = 0; i < 64; ++i)
+            for (int i = 0; i < 32; ++i)
                 x[i] = __builtin_fmaf(x[i], sgn, quad_swap1(x[i]));
         }
+        if constexpr (B >= 128) {
+            const float sgn = (ql & 2) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 64; ++i)
+            for (int i = 0; i < 32; ++i)
+                x[i] = __builtin_fmaf(x[i], sgn, quad_swap2(x[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
             x[i] = x[i] * InvSqrt<B>::value;
     }
 }
 
 // The raw input of one tile as this lane holds it.
 struct RowLoad {
-    u32x4 raw[8];     // 64 bf16 channels
+    u32x4 raw[4];     // 32 bf16 channels
     int32_t slot;     // < 0: nothing to store
 };
 
 __device__ __forceinline__ void load_row(RowLoad &R, const uint16_t *src_base, int64_t stride,
-                                         const int32_t *slots, int64_t t, int64_t num_tokens, int hl)
+                                         const int32_t *slots, int64_t t, int64_t num_tokens, int ql)
 {
     if (t < num_tokens) {
         R.slot = slots[t];
-        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src_base + t * stride + 64 * hl);
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src_base + t * stride + 32 * ql);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
             R.raw[j] = s4[j];
     } else {
         R.slot = -1;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
             R.raw[j] = u32x4{0u, 0u, 0u, 0u};
     }
 }
 
-// Rotate, quantise and store one row held in x; called by both lanes of the pair.
+// Rotate, quantise and store one row held in x; called by all four lanes of the quad.
 template <int B>
-__device__ __forceinline__ void encode_row(float (&x)[64], int32_t slot, uint8_t *__restrict__ codes,
+__device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t *__restrict__ codes,
                                            uint32_t *__restrict__ params, int64_t num_slots,
-                                           int num_kv_heads, int page_log2, int h, int hl)
+                                           int num_kv_heads, int page_log2, int h, int ql)
 {
-    rotate_row<B>(x, hl);
+    rotate_row<B>(x, ql);
 
     float mn = x[0], mx = x[0];
 #pragma unroll
-    for (int i = 1; i < 64; ++i) {
+    for (int i = 1; i < 32; ++i) {
         mn = fminf(mn, x[i]);
         mx = fmaxf(mx, x[i]);
     }
     mn = fminf(mn, quad_swap1(mn));
     mx = fmaxf(mx, quad_swap1(mx));
+    mn = fminf(mn, quad_swap2(mn));
+    mx = fmaxf(mx, quad_swap2(mx));
     mn = mn + 0.0f;  // a zero minimum is stored as +0
     mx = mx + 0.0f;
 
@@ -138,12 +146,12 @@ __device__ __forceinline__ void encode_row(float (&x)[64], int32_t slot, uint8_t
     const uint32_t s_bits = __builtin_bit_cast(uint16_t, s16);
     const uint32_t z_bits = __builtin_bit_cast(uint16_t, z16);
 
-    uint32_t out[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
     if (s_bits != 0u) {
         const float zf = (float)z16;
         const float inv = 1.0f / (float)s16;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < 4; ++k) {
             uint32_t pair[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -167,27 +175,26 @@ __device__ __forceinline__ void encode_row(float (&x)[64], int32_t slot, uint8_t
         const int64_t page = slot >> page_log2;
         const int64_t off = slot & ((1 << page_log2) - 1);
         const int64_t cell = ((page * num_kv_heads + h) << page_log2) + off;
-        u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + 2 * hl;
-        dst[0] = u32x4{out[0], out[1], out[2], out[3]};
-        dst[1] = u32x4{out[4], out[5], out[6], out[7]};
-        if (hl == 0)
+        u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + ql;
+        *dst = u32x4{out[0], out[1], out[2], out[3]};
+        if (ql == 0)
             params[cell] = s_bits | (z_bits << 16);
     }
 }
 
-// Each wave walks tile pairs: the K tile and the V tile of the same 32 tokens of one
+// Each wave walks tile pairs: the K tile and the V tile of the same 16 tokens of one
 // head, pair i covering head i % num_kv_heads, so waves that run side by side read all
-// heads of the same tokens (whole 2 KB-per-token input rows at once).  The loop is unrolled over the two
-// tensors, so each half is compiled for its own block size, and K and V work is spread
-// evenly over the waves.
+// heads of the same tokens (whole 2 KB-per-token input rows at once).  The loop is
+// unrolled over the two tensors, so each half is compiled for its own block size, and
+// K and V work is spread evenly over the waves.
 template <int BK, int BV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWriteWavesPerSimd)))
 void rotquant_write_kernel(WriteArgs a)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int hl = lane & 1;
-    const int row = lane >> 1;
+    const int ql = lane & 3;
+    const int row = lane >> 2;
     const int64_t tiles_per_head = (a.num_tokens + kWriteTile - 1) / kWriteTile;
     const int64_t num_pairs = tiles_per_head * a.num_kv_heads;
     const int64_t stride_w = (int64_t)gridDim.x * (blockDim.x >> 6);
@@ -198,8 +205,7 @@ void rotquant_write_kernel(WriteArgs a)
     auto issue = [&](RowLoad &R, const uint16_t *src, int64_t stride, int64_t pr) {
         const int64_t tt = pr / a.num_kv_heads;
         const int64_t h = pr - tt * a.num_kv_heads;
-        const int64_t t0 = tt * kWriteTile;
-        load_row(R, src + h * kHeadDim, stride, a.slots, t0 + row, a.num_tokens, hl);
+        load_row(R, src + h * kHeadDim, stride, a.slots, tt * kWriteTile + row, a.num_tokens, ql);
     };
 
     // One register set: once a tile's bf16 input is widened to fp32, the same registers
@@ -208,22 +214,22 @@ void rotquant_write_kernel(WriteArgs a)
     issue(R, a.k, a.k_stride, pair);
     while (true) {
         const int h = (int)(pair % a.num_kv_heads);
-        float x[64];
+        float x[32];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
             bf16x8_to_f32(R.raw[j], x + 8 * j);
         int32_t slot = R.slot;
         issue(R, a.v, a.v_stride, pair);
-        encode_row<BK>(x, slot, a.k_codes, a.k_params, a.num_slots, a.num_kv_heads, a.page_log2, h, hl);
+        encode_row<BK>(x, slot, a.k_codes, a.k_params, a.num_slots, a.num_kv_heads, a.page_log2, h, ql);
 
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
             bf16x8_to_f32(R.raw[j], x + 8 * j);
         slot = R.slot;
         const int64_t next = pair + stride_w;
         if (next < num_pairs)
             issue(R, a.k, a.k_stride, next);
-        encode_row<BV>(x, slot, a.v_codes, a.v_params, a.num_slots, a.num_kv_heads, a.page_log2, h, hl);
+        encode_row<BV>(x, slot, a.v_codes, a.v_params, a.num_slots, a.num_kv_heads, a.page_log2, h, ql);
         if (next >= num_pairs)
             break;
         pair = next;
