@@ -65,23 +65,93 @@ def parse_args(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also launch one plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--counters", default=None,
-                    help="JSON with FETCH_SIZE/WRITE_SIZE per launch (see --parse-counters)")
+                    help="JSON with FETCH_SIZE/WRITE_SIZE per launch (see --parse-counters); "
+                         "default: profiles/hbm_counters.<workload>[.<variant>].json if present")
     ap.add_argument("--parse-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
-    return ap.parse_args(argv)
+    ap.add_argument("--profiled-args", default="",
+                    help="with --parse-counters: the bench.py arguments the two --pmc runs used")
+    args = ap.parse_args(argv)
+    if args.counters is None:
+        args.counters = os.path.join(ROOT, "profiles", f"hbm_counters.{workload_tag(args)}.json")
+    return args
+
+
+def workload_tag(args) -> str:
+    """Name of the measured configuration, used for the counter summary files."""
+    tag = args.workload
+    if args.variant != "bdr":
+        tag += "." + args.variant
+    elif args.k_block is not None:
+        tag += f".k{args.k_block}"
+    return tag
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed: counter figures
+    taken on other code are not reported as this code's traffic."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "int4_kv_cache_rotquant_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+            with open(os.path.join(csrc, name)) as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", "", text)
+            h.update(name.encode() + re.sub(r"\s+", " ", text).strip().encode())
     return h.hexdigest()[:16]
 
 
-# ------------------------------------------------------------------ workload setup
+class HipEvent:
+    """A HIP timing event recorded on the stream the kernels are launched on (torch's
+    current stream, which the bindings use by default).
+
+    Created with hipEventDisableSystemFence: a default event performs a system-scope
+    release (an L2 write-back) when it is recorded, which adds several microseconds to
+    every bracketed kernel; a fence-free event times the kernel, not the fence."""
+    FLAGS = 0x20000000          # hipEventDisableSystemFence
+    _hip = None
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            h = ctypes.CDLL("libamdhip64.so")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self, torch):
+        import ctypes
+        self.torch = torch
+        self.ev = ctypes.c_void_p()
+        st = self.hip().hipEventCreateWithFlags(ctypes.byref(self.ev), self.FLAGS)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {st}")
+
+    def record(self):
+        st = self.hip().hipEventRecord(self.ev, self.torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed: {st}")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        st = self.hip().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {st}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
 class Setup:
     """Device buffers and one-step closure for a workload."""
 
@@ -339,7 +409,7 @@ def cpu_baseline(args):
 
 
 # ------------------------------------------------------------------ counters
-def parse_counter_dirs(fetch_dir, write_dir, out_json):
+def parse_counter_dirs(fetch_dir, write_dir, out_json, profiled_args=""):
     """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from two rocprofv3 --pmc
     runs, plus the calibration copy's values, into ``out_json``."""
     import csv
@@ -354,12 +424,18 @@ def parse_counter_dirs(fetch_dir, write_dir, out_json):
                     if row.get("Counter_Name") != counter:
                         continue
                     name = row.get("Kernel_Name", "")
+                    if "kvrq::" not in name:          # torch's set-up kernels are not ours
+                        continue
                     acc.setdefault(name, []).append(float(row["Counter_Value"]))
         return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
     fetch = load(fetch_dir, "FETCH_SIZE")
     write = load(write_dir, "WRITE_SIZE")
-    out = {"kernel_hash": kernel_source_hash(), "fetch_kib": {}, "write_kib": {}}
+    out = {"kernel_hash": kernel_source_hash(), "fetch_kib": {}, "write_kib": {},
+           "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <{c}_DIR> -o run -- "
+                        f"python bench.py {profiled_args}".rstrip() for c in ("FETCH_SIZE", "WRITE_SIZE")]
+           + [f"python bench.py --parse-counters <FETCH_SIZE_DIR> <WRITE_SIZE_DIR> <OUT> "
+              f"--profiled-args '{profiled_args}'"]}
     for k, (m, n) in fetch.items():
         out["fetch_kib"][k] = {"mean": m, "dispatches": n}
     for k, (m, n) in write.items():
@@ -399,7 +475,7 @@ def traffic_from_counters(path, kernel_symbol, copy_bytes):
 def main():
     args = parse_args()
     if args.parse_counters:
-        parse_counter_dirs(*args.parse_counters)
+        parse_counter_dirs(*args.parse_counters, profiled_args=args.profiled_args)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the rotated INT4 KV-cache path shards by KV head or by "
@@ -422,7 +498,7 @@ def main():
         for _ in range(3):
             K.kvrq_device_copy(dst, src)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = HipEvent(torch), HipEvent(torch)
         e0.record()
         K.kvrq_device_copy(dst, src)
         e1.record()
@@ -433,8 +509,8 @@ def main():
         copy_gbps = None
 
     n_ev = 3
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    warm = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    evs = [[HipEvent(torch) for _ in range(n_ev)] for _ in range(args.steps)]
+    warm = [HipEvent(torch) for _ in range(n_ev)]
     for i in range(args.warmup):
         s.step(i, warm)
     torch.cuda.synchronize()

@@ -9,22 +9,23 @@
 // rotated, so the output is rotated back once at the end (H is symmetric and
 // orthonormal, hence its own inverse).
 //
-// Launch 1 -- decode_split_kernel, one 64-lane wave per (split, KV head,
-// sequence).  The wave walks its token range in 32-token tiles:
-//   QK^T  S[t][g] = sum_d (code_K[t][d] - 8) q''[d][g] on MFMA 16x16x32 (f16
-//         in, f32 accumulate): A = the INT4 codes of 16 tokens turned into
-//         exact centred f16 integers, B = the G (<= 16) rotated queries split
-//         into f16 high and low parts (two MFMAs) so the product keeps ~22
-//         mantissa bits; score = scale_t * S + (zero_t + 8 scale_t) * sum(q')
+// Launch 1 -- decode_split_kernel, one workgroup of four 64-lane waves per
+// (split, KV head, sequence); each wave walks a quarter of the split's tokens
+// in 32-token tiles, the next tile's loads in flight while one is consumed:
+//   QK^T  S[t][g] = sum_d code_K[t][d] q[d][g] on int8 MFMA 16x16x64: A = the
+//         INT4 codes as bytes, B = the G (<= 16) rotated queries rounded to a
+//         21-bit integer grid and cut into three int8 digits, so the products
+//         are exact integers; score = scale_t * 2^-f * S + zero_t * sum(q')
 //         (de-quantisation factored out of the dot product);
-//   softmax online, in base 2 (log2 e is folded into q');
+//   softmax online, in base 2 (log2 e is folded into q'), with a lazy maximum;
 //   PV    O'[d][g] += sum_t (code_V[t][d] - 8) (p_t scale_t), plus
-//         sum_t p_t (zero_t + 8 scale_t), again on MFMA with the weights split
-//         into f16 high and low parts.
-// Each lane keeps one query head g = lane % 16, so the softmax state and the
-// 32 output channels a lane accumulates never need a cross-lane exchange
-// except for the per-tile maximum.
-// Launch 2 -- decode_combine_kernel, one wave per (query head, sequence):
+//         sum_t p_t (zero_t + 8 scale_t), on f16 MFMA 16x16x32 with the codes
+//         as exact centred f16 integers and the weights split into f16 high
+//         and low parts.
+// Lane (n16, kq) keeps query head g = n16, so the softmax state needs no
+// cross-lane exchange except for the per-tile maxima.  The four waves' states
+// are merged in LDS into one split partial (o, m, l).
+// Launch 2 -- decode_combine_kernel, one workgroup per (query head, sequence):
 // log-sum-exp combine of the splits, then the inverse V rotation.
 #include <hip/hip_runtime.h>
 
