@@ -91,29 +91,65 @@ __device__ __forceinline__ void rotate_query(float (&x)[32], int ql)
     }
 }
 
-// V codes become f16 MFMA operands: a nibble masked in place and OR-ed into the
-// f16 pattern 0x6400 (= 1024) is the exact f16 integer 1024 + code (bits 0-3) or
-// 1024 + 16 code (bits 4-7); one packed subtraction centres it to code - 8 (times
-// 16 for the upper nibble).  Normal f16 operands keep the matrix cores' full
-// accumulation precision, and centred codes keep the weighted sums small.
-constexpr uint32_t kLoNib = 0x000F000Fu;
-constexpr uint32_t kHiNib = 0x00F000F0u;
-
-__device__ __forceinline__ uint32_t centred_codes(uint32_t masked, bool upper)
+__device__ __forceinline__ float wave_xor(float x, int m)
 {
-    const f16x2 v = __builtin_bit_cast(f16x2, masked | 0x64006400u);
-    const _Float16 c = upper ? (_Float16)1152.0f : (_Float16)1032.0f;
-    return __builtin_bit_cast(uint32_t, v - f16x2{c, c});
+    return __shfl_xor(x, m, 64);
 }
 
-// K codes become int8 MFMA operands: the even and the odd nibbles of a dword, masked
-// in place, are four bytes each.  Scores are integer dot products of codes with the
-// query quantised to 22 bits (three int8 slices), exact in the int32 accumulators.
+// Maximum and sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48, which hold the 16
+// tokens of one MFMA column between them (gfx950 row permutes: swap the upper 32
+// lanes, then the odd 16-lane rows, with the same register).
+__device__ __forceinline__ float max_raw(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ __forceinline__ float col_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float col_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+    return r;
+}
+
+// V codes become f16 MFMA operands: a nibble moved into mantissa bits 6..9 under the
+// exponent of 1.0 is the exact f16 value 1 + code / 16 (a high nibble left in bits 4..7:
+// 1 + code / 64); one packed subtraction centres it to (code - 8) / 16 (or / 64), exact,
+// so the accumulators hold small centred sums and keep their precision.  The zero point
+// then becomes zero + 8 scale: sum_t p_t (c_t s_t + z_t) = sum_t p_t s_t (c_t - 8)
+// + sum_t p_t z_t + 8 sum_t p_t s_t.
+constexpr uint32_t kOne2 = 0x3C003C00u;     // f16x2 {1, 1}
+constexpr uint32_t kMant69 = 0x03C003C0u;   // mantissa bits 6..9 of both halves
+constexpr uint32_t kMant47 = 0x00F000F0u;   // mantissa bits 4..7 of both halves
+
+// K codes become int8 MFMA operands: the even and the odd nibbles of a dword, masked in
+// place, are four bytes each.  Scores are integer dot products of codes with the query
+// rounded to a 21-bit grid (three int8 digits), exact in the int32 accumulators.
 constexpr uint32_t kNibBytes = 0x0F0F0F0Fu;
 
 // Lazy softmax maximum (base 2): weights exp2(score - m) may grow to 2^kLazyMax before
 // the reference max m moves and the accumulators are rescaled.
 constexpr float kLazyMax = 8.0f;
+
+// Running maximum before any score has been seen (finite, far below any real score).
+constexpr float kNoScore = -1.0e30f;
 
 __device__ __forceinline__ i32x4 mfma_i8(const i32x4 &a, const i32x4 &b, const i32x4 &c)
 {
@@ -125,210 +161,279 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const f16x8 &a, const f16x8 &b, co
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_xor(float x, int m)
-{
-    return __shfl_xor(x, m, 64);
-}
-
-// One 32-token tile of one (sequence, KV head) as this lane loads it.
-//   kc[hf]  16 code bytes of token t0 + 16 hf + n16, channels [32 kq, 32 kq + 32)
-//   vc      code dword n16 (channels 8 n16 .. 8 n16 + 7) of tokens t0 + 16 hf + 4 kq + r
-//   par     lanes 0..31: (scale, zero) of K for token t0 + lane; lanes 32..63: the same
-//           for V (token t0 + lane - 32); redistributed through LDS when the tile is used
+// Tokens are handled in tiles of 32.  Two layouts of the QK^T product:
+//   F = 1 (9..16 query heads per KV head): a 16x16x64 MFMA covers 16 tokens x 16 heads
+//         x 64 k (32 channels, one nibble parity); lane (n16, kq) ends with the scores of
+//         head n16 for tokens 16 hf + 4 kq + r (8 per lane);
+//   F = 2 (up to 8 heads): the k range is split between two tokens: k < 32 belongs to
+//         token n16, k >= 32 to token n16 + 16, and B columns 0..7 / 8..15 read only
+//         their half, so one MFMA covers 32 tokens x 8 heads; lane (n16, kq) ends with
+//         the scores of head n16 % 8 for tokens 4 kq + r + 16 (n16 / 8) (4 per lane) and
+//         keeps its own softmax state for that half of the tile (merged at the end).
+// One 32-token tile as this lane loads it:
+//   kc[j]   F = 1: 16 code bytes of token 16 j + n16, bytes [16 kq, 16 kq + 16)
+//           F = 2: 16 code bytes of token n16 + 16 (kq / 2), bytes 32 (kq % 2) + 16 j
+//   vc[j]   code dword n16 (channels 8 n16 .. 8 n16 + 7) of token 16 (j / 4) + 4 kq + j % 4
+//   par     lanes 0..31: (scale, zero) of K of token lane; lanes 32..63: V of token
+//           lane - 32; converted and shared through LDS when the tile is consumed
 struct Tile {
     u32x4 kc[2];
     uint32_t vc[8];
     uint32_t par;
 };
 
-// Lane byte offsets inside one 16-token half tile of a (page, head): constant for the
-// whole loop, so the loads are a scalar (uniform) base plus a 32-bit lane offset.
-struct LaneOffsets {
-    uint32_t kc;   // n16 * 64 + 16 kq into the K codes
-    uint32_t vc;   // 4 kq * 64 + 4 n16 into the V codes; + 64 r for token 4 kq + r
-    uint32_t par;  // 4 (lane % 16) into the parameters of the lane's half tile
-};
-
+// Issues the loads of the tile starting at t0 (< t_end).  A half tile that starts past
+// the end re-reads the first half's rows: every load is in bounds and unconditional, and
+// tokens past the end are removed by their parameters (zero) and score bias (-inf).
+template <int F>
 __device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const int32_t *ptab, int h,
-                                          int t0, int t_end, const LaneOffsets &o, int lane)
+                                          int t0, int t_end, int lane)
 {
     const int P = 1 << a.page_log2;
-    const bool v_lane = lane >= 32;
-    const int my_half = (lane >> 4) & 1;
-    T.par = 0u;
+    const int n16 = lane & 15, kq = lane >> 4;
+    // (page, head) row bases of the two 16-token halves; uniform, so on the scalar unit
+    const uint8_t *kb[2], *vb[2];
+    const uint32_t *kp[2], *vp[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-        const int tb = t0 + 16 * hf;
-        if (tb < t_end) {
-            int page = ptab[tb >> a.page_log2];
-            page = (unsigned)page < (unsigned)a.num_pages ? page : 0;
-            const int64_t cell0 = ((int64_t)page * a.num_kv_heads + h) * P + (tb & (P - 1));
-            const uint8_t *kc = a.k_codes + cell0 * kRowCodeBytes;
-            const uint8_t *vc = a.v_codes + cell0 * kRowCodeBytes;
-            T.kc[hf] = *reinterpret_cast<const u32x4 *>(kc + o.kc);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                T.vc[4 * hf + r] = *reinterpret_cast<const uint32_t *>(vc + o.vc + 64 * r);
-            if (my_half == hf) {
-                const uint32_t *pp = v_lane ? a.v_params + cell0 : a.k_params + cell0;
-                T.par = *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(pp) + o.par);
-            }
-        } else {
-            T.kc[hf] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                T.vc[4 * hf + r] = 0u;
-        }
+        const int tb = hf && t0 + 16 >= t_end ? t0 : t0 + 16 * hf;
+        int page = ptab[tb >> a.page_log2];
+        page = (unsigned)page < (unsigned)a.num_pages ? page : 0;
+        const int64_t cell0 = ((int64_t)page * a.num_kv_heads + h) * P + (tb & (P - 1));
+        kb[hf] = a.k_codes + cell0 * kRowCodeBytes;
+        vb[hf] = a.v_codes + cell0 * kRowCodeBytes;
+        kp[hf] = a.k_params + cell0;
+        vp[hf] = a.v_params + cell0;
     }
+    if constexpr (F == 1) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            T.kc[hf] = *reinterpret_cast<const u32x4 *>(kb[hf] + n16 * kRowCodeBytes + 16 * kq);
+    } else {
+        const uint8_t *src = (kq >> 1 ? kb[1] : kb[0]) + n16 * kRowCodeBytes + 32 * (kq & 1);
+        T.kc[0] = *reinterpret_cast<const u32x4 *>(src);
+        T.kc[1] = *reinterpret_cast<const u32x4 *>(src + 16);
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            T.vc[4 * hf + r] =
+                *reinterpret_cast<const uint32_t *>(vb[hf] + (4 * kq + r) * kRowCodeBytes + 4 * n16);
+    }
+    const int ph = (lane >> 4) & 1;
+    T.par = *((lane < 32 ? (ph ? kp[1] : kp[0]) : (ph ? vp[1] : vp[0])) + (lane & 15));
 }
 
-// B operand of QK^T in lane order: the query quantised to int32 q = round(q' * 2^f)
-// (|q| < 2^21) and cut into int8 digits q = 2^16 hi + 2^8 mid + lo.  Element e of
-// k-step ks for lane (n16, kq) is the digit of channel 32 kq + 8 (e / 4) + 2 (e % 4) + ks.
+// B operands of QK^T in lane order: the query rounded to integers q = round(q' 2^f)
+// (|q| <= 2^20, one f per KV head) and cut into int8 digits q = 2^16 hi + 2^8 mid + lo.
+//   F = 1: v[par][digit][lane], element byte e of lane (n16, kq): channel 32 kq + 2 e + par
+//          of head n16;
+//   F = 2: v[2 j + par][digit][lane]: channel 64 (kq % 2) + 32 j + 2 e + par of head n16 % 8
+//          for lanes with (n16 / 8) == (kq / 2), zero for the others.
 struct QOperand {
-    i32x4 v[2][3][64];   // [k-step][hi, mid, lo][lane]
+    i32x4 v[4][3][64];
 };
 
-// Online-softmax state of one wave: lane (n16, kq) keeps query head g = n16.
+// Parameters of one tile in fp32, per wave: [0] scale (K: times 2^-f), [1] zero,
+// [2] score bias (0, or -inf past the end); K of token j at j, V at 32 + j.
+struct ParLds {
+    float v[3][64];
+};
+
+// Online-softmax state of one lane: the MFMA column it belongs to (head n16, or head
+// n16 % 8 over one half of each tile when F = 2).
 struct WaveState {
-    float kscale;               // 2^-f: integer dot products back to the query's scale
     float qsum;                 // sum of the rotated, scaled query (for the zero points)
-    float m, l, z;              // running max (base 2), partial sums of p and p * zero_V
-    int E;                      // weights enter the PV product as p * scale_V * 2^E
-    f32x4 acc[8];               // O'[d][g] * 2^E, d = 8 (4 kq + r) + b, centred codes
-                                // (x16 for odd b)
+    float m, l, z;              // running max (base 2), sums of p and p * zero_V
+    float wsum;                 // sum of the PV weights w, scaled like acc
+    int E;                      // weights enter the PV product as w = p * scale_V * 2^E
+    float slim;                 // 2^(6 - E): a V scale this large needs a smaller E
+    f32x4 acc[8];               // sum_t w_t (code - 8) / u_b, d = 8 (4 kq + r) + b,
+                                // u_b = 16 (even b) or 64 (odd b)
 
-    __device__ __forceinline__ void consume(const Tile &T, int t0, int t_end, int lane,
-                                            const QOperand &qop, uint32_t *par_lds)
+    template <int F>
+    __device__ __forceinline__ void consume(const Tile &T, int t0, int t_end, int lane, float kscale,
+                                            const QOperand &qop, ParLds &pl)
     {
-        const int kq = lane >> 4;
-        const bool full = t0 + kTile <= t_end;   // uniform: no masking inside full tiles
-        // parameters of the lane's 8 tokens, K then V: [0..31] K of tokens 0..31, [32..63] V
-        // (lanes of one wave exchange through LDS; LDS operations of a wave complete in order)
-        par_lds[lane] = T.par;
-        __builtin_amdgcn_wave_barrier();
-        const u32x4 kp0 = *reinterpret_cast<const u32x4 *>(par_lds + 4 * kq);
-        const u32x4 kp1 = *reinterpret_cast<const u32x4 *>(par_lds + 16 + 4 * kq);
-        const u32x4 vp0 = *reinterpret_cast<const u32x4 *>(par_lds + 32 + 4 * kq);
-        const u32x4 vp1 = *reinterpret_cast<const u32x4 *>(par_lds + 48 + 4 * kq);
+        constexpr int NS = 8 / F;            // scores per lane
+        const int n16 = lane & 15, kq = lane >> 4;
+        const int sub = F == 2 ? (n16 >> 3) : 0;
 
-        // ---- a8: scores of tokens t0 + 16 hf + 4 kq + r ---------------------------------
-        float Sd[8];
+        // parameters: each lane converts one (scale, zero) pair (zero past the end of the
+        // range, where the bias also removes the token from the softmax)
+        {
+            const bool valid = t0 + (lane & 31) < t_end;
+            const f16x2 pr = __builtin_bit_cast(f16x2, valid ? T.par : 0u);
+            pl.v[0][lane] = (float)pr.x * kscale;
+            pl.v[1][lane] = (float)pr.y;
+            pl.v[2][lane] = valid ? 0.0f : -INFINITY;
+        }
+        __builtin_amdgcn_wave_barrier();
+        float sk[NS], zk[NS], bk[NS], sv[NS], zv[NS];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const u32x4 w = T.kc[hf];
-            const i32x4 ev = {int32_t(w.x & kNibBytes), int32_t(w.y & kNibBytes),
-                              int32_t(w.z & kNibBytes), int32_t(w.w & kNibBytes)};
-            const i32x4 od = {int32_t((w.x >> 4) & kNibBytes), int32_t((w.y >> 4) & kNibBytes),
-                              int32_t((w.z >> 4) & kNibBytes), int32_t((w.w >> 4) & kNibBytes)};
-            i32x4 dg[3];
+        for (int j = 0; j < NS / 4; ++j) {
+            const int base = 4 * kq + 16 * (F == 2 ? sub : j);
+            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&pl.v[0][base]);
+            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&pl.v[1][base]);
+            const f32x4 a2 = *reinterpret_cast<const f32x4 *>(&pl.v[2][base]);
+            const f32x4 a3 = *reinterpret_cast<const f32x4 *>(&pl.v[0][32 + base]);
+            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&pl.v[1][32 + base]);
 #pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                dg[j] = mfma_i8(ev, qop.v[0][j][lane], i32x4{0, 0, 0, 0});
-                dg[j] = mfma_i8(od, qop.v[1][j][lane], dg[j]);
+            for (int r = 0; r < 4; ++r) {
+                sk[4 * j + r] = a0[r];
+                zk[4 * j + r] = a1[r];
+                bk[4 * j + r] = a2[r];
+                sv[4 * j + r] = a3[r];
+                zv[4 * j + r] = a4[r];
+            }
+        }
+
+        // ---- a8: integer scores -----------------------------------------------------------
+        float sc[NS];
+        if constexpr (F == 1) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const u32x4 w = T.kc[hf];
+                const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
+                const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
+                i32x4 dg[3];
+#pragma unroll
+                for (int d = 0; d < 3; ++d) {
+                    dg[d] = mfma_i8(ev, qop.v[0][d][lane], i32x4{0, 0, 0, 0});
+                    dg[d] = mfma_i8(od, qop.v[1][d][lane], dg[d]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sc[4 * hf + r] = (float)((((dg[0][r] << 8) + dg[1][r]) << 8) + dg[2][r]);
+            }
+        } else {
+            i32x4 dg[3] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const u32x4 w = T.kc[j];
+                const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
+                const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
+#pragma unroll
+                for (int d = 0; d < 3; ++d) {
+                    dg[d] = mfma_i8(ev, qop.v[2 * j][d][lane], dg[d]);
+                    dg[d] = mfma_i8(od, qop.v[2 * j + 1][d][lane], dg[d]);
+                }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Sd[4 * hf + r] = (float)(dg[0][r] * 256 + dg[1][r]) * 256.0f + (float)dg[2][r];
+                sc[r] = (float)((((dg[0][r] << 8) + dg[1][r]) << 8) + dg[2][r]);
         }
-        float sc[8], sv[8], zv[8];
-        const uint32_t kpw[8] = {kp0.x, kp0.y, kp0.z, kp0.w, kp1.x, kp1.y, kp1.z, kp1.w};
-        const uint32_t vpw[8] = {vp0.x, vp0.y, vp0.z, vp0.w, vp1.x, vp1.y, vp1.z, vp1.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const f16x2 kpar = __builtin_bit_cast(f16x2, kpw[i]);
-            const f16x2 vpar = __builtin_bit_cast(f16x2, vpw[i]);
-            const float score = Sd[i] * ((float)kpar.x * kscale) + (float)kpar.y * qsum;
-            const float vs = (float)vpar.x;
-            const float vz = (float)vpar.y + 8.0f * vs;   // zero point of the centred codes
-            if (full) {
-                sc[i] = score;
-                sv[i] = vs;
-                zv[i] = vz;
-            } else {
-                const bool ok = t0 + 16 * (i >> 2) + 4 * kq + (i & 3) < t_end;
-                sc[i] = ok ? score : -INFINITY;
-                sv[i] = ok ? vs : 0.0f;
-                zv[i] = ok ? vz : 0.0f;
-            }
-        }
+        for (int i = 0; i < NS; ++i)
+            sc[i] = fmaf(sc[i], sk[i], fmaf(zk[i], qsum, bk[i]));
 
-        // ---- a9: online softmax (base 2); accumulators rescaled only when a max moved ------
-        float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        tmax = fmaxf(tmax, wave_xor(tmax, 16));
-        tmax = fmaxf(tmax, wave_xor(tmax, 32));
-        // The reference max moves only when a score exceeds it by more than kLazyMax (base
-        // 2), so the accumulators are rarely rescaled; weights stay below 2^kLazyMax.
-        const bool moved = tmax > m + kLazyMax;
-        const float m_new = moved ? tmax : m;
-        const float alpha = moved ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
-        m = m_new;
-        // Weight exponent: the f16 high and low parts of p * scale_V * 2^E keep ~22 bits only
-        // while the low part stays a normal f16, so E puts the tile's largest possible weight
-        // (p <= 2^kLazyMax) just below 2^14.  E only decreases; the accumulators follow
-        // exactly.
-        float smax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                           fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        smax = fmaxf(smax, wave_xor(smax, 16));
-        smax = fmaxf(smax, wave_xor(smax, 32));
-        float acc_f = alpha;
-        bool e_moved = false;
-        if (smax > 0.0f) {
-            int ex;
-            frexpf(smax, &ex);
-            const int e_tile = 14 - (int)kLazyMax - ex;
-            if (e_tile < E) {                      // uniform across the wave
+        // ---- a9: online softmax (base 2), lazy maximum ------------------------------------
+        // Most tiles change nothing: the maximum moves only when a score exceeds it by more
+        // than kLazyMax, the weight exponent only when a V scale reaches slim = 2^(6 - E).
+        // Lanes test their own scores; the column reductions run only when some lane asks.
+        float tmax = sc[0], smax = sv[0];
+#pragma unroll
+        for (int i = 1; i < NS; ++i) {
+            tmax = fmaxf(tmax, sc[i]);
+            smax = max_raw(smax, sv[i]);
+        }
+        float alpha = 1.0f;
+        if (__builtin_amdgcn_ballot_w64(tmax > m + kLazyMax || smax >= slim)) {
+            tmax = col_max(tmax);
+            smax = col_max(smax);
+            const bool moved = tmax > m + kLazyMax;
+            const float m_new = moved ? tmax : m;
+            alpha = moved ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
+            m = m_new;
+            // weight exponent: the f16 high and low parts of w keep ~22 bits while the low
+            // part is a normal f16, so E puts the largest possible weight of the tile
+            // (p <= 2^8) just below 2^14; E only decreases, and the accumulators follow
+            float acc_f = alpha;
+            if (smax >= slim) {
+                int ex;
+                frexpf(smax, &ex);
+                const int e_tile = 14 - (int)kLazyMax - ex;
                 acc_f = ldexpf(alpha, e_tile - E);
                 E = e_tile;
-                e_moved = true;
+                slim = ldexpf(1.0f, 14 - (int)kLazyMax - E);
             }
-        }
-        float psum = 0.0f, pz = 0.0f;
-        f16x8 pb_hi, pb_lo;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = __builtin_amdgcn_exp2f(sc[i] - m_new);
-            psum += p;
-            pz += p * zv[i];
-            const float w = p * ldexpf(sv[i], E);
-            const _Float16 hi = (_Float16)w;
-            pb_hi[i] = hi;
-            pb_lo[i] = (_Float16)(w - (float)hi);
-        }
-        l = l * alpha + psum;
-        z = z * alpha + pz;
-        if (__builtin_amdgcn_ballot_w64(moved) || e_moved) {
+            l *= alpha;
+            z *= alpha;
+            wsum *= acc_f;
 #pragma unroll
             for (int b = 0; b < 8; ++b)
                 acc[b] *= acc_f;
         }
-
-        // ---- PV: A = V codes (rows: channel 8 n16 + b, k: the 8 tokens), B = p * scale -----
-        uint32_t src[4][4];   // [lo bytes, lo >> 8, hi bytes, hi >> 8][token pair]
+        const float m_new = m;
+        // p 2^E = exp2(score - (m - E)): the weights come out scaled, the sums of p are
+        // scaled back once per tile
+        const float mE = m_new - (float)E;
+        float psum = 0.0f, pz = 0.0f, ws = 0.0f;
+        float w[NS];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            src[0][p] = __builtin_amdgcn_perm(T.vc[2 * p + 1], T.vc[2 * p], 0x05040100u);
-            src[2][p] = __builtin_amdgcn_perm(T.vc[2 * p + 1], T.vc[2 * p], 0x07060302u);
-            src[1][p] = src[0][p] >> 8;
-            src[3][p] = src[2][p] >> 8;
+        for (int i = 0; i < NS; ++i) {
+            const float pe = __builtin_amdgcn_exp2f(sc[i] - mE);
+            psum += pe;
+            pz = fmaf(pe, zv[i], pz);
+            w[i] = pe * sv[i];
+            ws += w[i];
         }
+        const float uE = ldexpf(1.0f, -E);
+        l = fmaf(psum, uE, l);
+        z = fmaf(pz, uE, z);
+        wsum += ws;
+        // B operand of PV, f16 high and low parts (high rounded toward zero, so the low
+        // part keeps the rest): k slot e of lane (n16, kq) is token 16 (e / 4) + 4 kq + e % 4
+        uint32_t hp[NS / 2], lp[NS / 2];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const uint32_t *sp = src[b >> 1];
-            const bool upper = b & 1;
-            const uint32_t mask = upper ? kHiNib : kLoNib;
-            const u32x4 r = {centred_codes(sp[0] & mask, upper), centred_codes(sp[1] & mask, upper),
-                             centred_codes(sp[2] & mask, upper), centred_codes(sp[3] & mask, upper)};
-            const f16x8 va = __builtin_bit_cast(f16x8, r);
-            acc[b] = mfma16x16x32(va, pb_hi, acc[b]);
-            acc[b] = mfma16x16x32(va, pb_lo, acc[b]);
+        for (int j = 0; j < NS / 2; ++j) {
+            const auto h = __builtin_amdgcn_cvt_pkrtz(w[2 * j], w[2 * j + 1]);
+            const auto r = __builtin_amdgcn_cvt_pkrtz(w[2 * j] - (float)h[0], w[2 * j + 1] - (float)h[1]);
+            hp[j] = __builtin_bit_cast(uint32_t, h);
+            lp[j] = __builtin_bit_cast(uint32_t, r);
+        }
+        u32x4 bhu, blu;
+        if constexpr (F == 1) {
+            bhu = u32x4{hp[0], hp[1], hp[2], hp[3]};
+            blu = u32x4{lp[0], lp[1], lp[2], lp[3]};
+        } else {
+            bhu = sub ? u32x4{0u, 0u, hp[0], hp[1]} : u32x4{hp[0], hp[1], 0u, 0u};
+            blu = sub ? u32x4{0u, 0u, lp[0], lp[1]} : u32x4{lp[0], lp[1], 0u, 0u};
+        }
+        const f16x8 bh = __builtin_bit_cast(f16x8, bhu);
+        const f16x8 bl = __builtin_bit_cast(f16x8, blu);
+
+        // ---- PV: A = V codes (rows: channel 8 n16 + b, k: the 8 tokens), B = weights -------
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t src[4];   // byte k of tokens (2p, 2p + 1) in bits 0..7 and 16..23
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                src[p] = __builtin_amdgcn_perm(T.vc[2 * p + 1], T.vc[2 * p],
+                                               0x0C000C00u | ((4u + k) << 16) | (uint32_t)k);
+            f16x8 al, ah;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f16x2 lo = __builtin_bit_cast(f16x2, and_or(src[p] << 6, kMant69, kOne2));
+                const f16x2 hi = __builtin_bit_cast(f16x2, and_or(src[p], kMant47, kOne2));
+                const f16x2 cl = lo - f16x2{(_Float16)1.5f, (_Float16)1.5f};
+                const f16x2 ch = hi - f16x2{(_Float16)1.125f, (_Float16)1.125f};
+                al[2 * p] = cl[0];
+                al[2 * p + 1] = cl[1];
+                ah[2 * p] = ch[0];
+                ah[2 * p + 1] = ch[1];
+            }
+            acc[2 * k] = mfma16x16x32(al, bh, acc[2 * k]);
+            acc[2 * k] = mfma16x16x32(al, bl, acc[2 * k]);
+            acc[2 * k + 1] = mfma16x16x32(ah, bh, acc[2 * k + 1]);
+            acc[2 * k + 1] = mfma16x16x32(ah, bl, acc[2 * k + 1]);
         }
     }
 };
 
-template <int BK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+template <int BK, int F>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? 3 : 2)))
 void decode_split_kernel(DecodeArgs a)
 {
     const int split = blockIdx.x;
@@ -348,14 +453,14 @@ void decode_split_kernel(DecodeArgs a)
     const int t_begin = wg_begin + wave * wave_tokens;
     const int t_end = min(L, t_begin + wave_tokens);
 
-    // rotated query rows in the prologue, the four waves' states in the epilogue
-    __shared__ float lds_o[kDecodeWaves][kMaxGroup][kHeadDim + 4];
+    // rotated query rows in the prologue, the waves' partial states in the epilogue
+    __shared__ float lds_o[kDecodeWaves][16][kHeadDim + 4];
     __shared__ QOperand qop;
-    __shared__ uint32_t lds_par[kDecodeWaves][64];
-    __shared__ float lds_m[kDecodeWaves][kMaxGroup];
-    __shared__ float lds_l[kDecodeWaves][kMaxGroup];
+    __shared__ ParLds lds_par[kDecodeWaves];
+    __shared__ float lds_m[kDecodeWaves][16];
+    __shared__ float lds_l[kDecodeWaves][16];
     __shared__ float lds_qsum[kMaxGroup];
-    __shared__ float lds_kscale[kMaxGroup];
+    __shared__ float lds_kscale;
     float(*q_lds)[kHeadDim + 4] = lds_o[0];
 
     // ---- a6: wave 0 rotates the G queries of this KV head, folds sm_scale * log2(e) ---------
@@ -388,57 +493,71 @@ void decode_split_kernel(DecodeArgs a)
             amax = fmaxf(amax, fabsf(x[i]));
             sum += x[i];
         }
-        amax = fmaxf(amax, dpp_quad_swap1(amax));
-        amax = fmaxf(amax, dpp_quad_swap2(amax));
         sum += dpp_quad_swap1(sum);
         sum += dpp_quad_swap2(sum);
-        // power-of-two factor 2^f placing the largest |q' * 2^f| in [2^20, 2^21)
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1)
+            amax = fmaxf(amax, wave_xor(amax, o));
+        // one power-of-two factor 2^f for the whole group: max |q' 2^f| in [2^19, 2^20)
         int e = 0;
         if (amax > 0.0f)
             frexpf(amax, &e);
 #pragma unroll
         for (int i = 0; i < 32; ++i)
-            q_lds[g][32 * ql + i] = ldexpf(x[i], 21 - e);
-        if (ql == 0) {
+            q_lds[g][32 * ql + i] = ldexpf(x[i], 20 - e);
+        if (ql == 0 && g < kMaxGroup)
             lds_qsum[g] = sum;
-            lds_kscale[g] = ldexpf(1.0f, e - 21);
-        }
+        if (lane == 0)
+            lds_kscale = ldexpf(1.0f, e - 20);
     }
     __syncthreads();
 
-    // B operands of QK^T: int8 digits of the quantised query in lane order
-    for (int i = tid; i < 2 * 64; i += 64 * kDecodeWaves) {
-        const int ks = i >> 6, ln = i & 63;
+    // B operands of QK^T: int8 digits of the integer query in lane order
+    for (int i = tid; i < 2 * F * 64; i += 64 * kDecodeWaves) {
+        const int slot = i >> 6, ln = i & 63;     // slot = 2 j + par (F = 2) or par (F = 1)
         const int n = ln & 15, q4 = ln >> 4;
+        const int par = slot & 1, jj = slot >> 1;
+        const int g = F == 2 ? (n & 7) : n;
+        const bool live = g < G && (F == 1 || (n >> 3) == (q4 >> 1));
+        const int ch0 = F == 2 ? 64 * (q4 & 1) + 32 * jj + par : 32 * q4 + par;
         uint32_t dig[3][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             dig[0][j] = dig[1][j] = dig[2][j] = 0u;
+        if (live) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int32_t q = (int32_t)rintf(q_lds[n][32 * q4 + 8 * (e >> 2) + 2 * (e & 3) + ks]);
-            const int32_t lo = ((q + 128) & 255) - 128;
-            const int32_t r1 = (q - lo) >> 8;
-            const int32_t mid = ((r1 + 128) & 255) - 128;
-            const int32_t hi = (r1 - mid) >> 8;
-            const int sh = 8 * (e & 3);
-            dig[0][e >> 2] |= uint32_t(hi & 255) << sh;
-            dig[1][e >> 2] |= uint32_t(mid & 255) << sh;
-            dig[2][e >> 2] |= uint32_t(lo & 255) << sh;
+            for (int e = 0; e < 16; ++e) {
+                const int32_t q = (int32_t)rintf(q_lds[g][ch0 + 2 * e]);
+                const int32_t lo = ((q + 128) & 255) - 128;
+                const int32_t r1 = (q - lo) >> 8;
+                const int32_t mid = ((r1 + 128) & 255) - 128;
+                const int32_t hi = (r1 - mid) >> 8;
+                const int sh = 8 * (e & 3);
+                dig[0][e >> 2] |= uint32_t(hi & 255) << sh;
+                dig[1][e >> 2] |= uint32_t(mid & 255) << sh;
+                dig[2][e >> 2] |= uint32_t(lo & 255) << sh;
+            }
         }
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
-            qop.v[ks][j][ln] = i32x4{int32_t(dig[j][0]), int32_t(dig[j][1]), int32_t(dig[j][2]), int32_t(dig[j][3])};
+        for (int d = 0; d < 3; ++d)
+            qop.v[slot][d][ln] = i32x4{int32_t(dig[d][0]), int32_t(dig[d][1]), int32_t(dig[d][2]),
+                                       int32_t(dig[d][3])};
     }
     const int n16 = lane & 15;
     const int kq = lane >> 4;
+    const int gl = F == 2 ? (n16 & 7) : n16;   // this lane's query head
     WaveState st;
-    st.qsum = lds_qsum[n16];
-    st.kscale = lds_kscale[n16];
-    st.m = -INFINITY;
+    st.qsum = lds_qsum[gl];
+    // K lanes scale by 2^-f (the integer query's grid), V lanes by 1
+    const float kscale = lane < 32 ? lds_kscale : 1.0f;
+    // a finite start: with F = 2 half a tile may hold no valid token while nothing has been
+    // seen yet, and exp2(-inf - (-inf)) would poison the sums
+    st.m = kNoScore;
     st.l = 0.0f;
     st.z = 0.0f;
+    st.wsum = 0.0f;
     st.E = 64;
+    st.slim = 0x1p-58f;   // 2^(6 - E)
 #pragma unroll
     for (int b = 0; b < 8; ++b)
         st.acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -447,42 +566,48 @@ void decode_split_kernel(DecodeArgs a)
     // ---- a7: page walk, one tile ahead of the math --------------------------------------
     const int32_t *ptab = a.page_table + (int64_t)s * a.max_pages;
     if (t_begin < t_end) {
-        const LaneOffsets off = {uint32_t(n16 * kRowCodeBytes + 16 * kq),
-                                 uint32_t(4 * kq * kRowCodeBytes + 4 * n16), uint32_t(4 * (lane & 15))};
-        uint32_t *par_lds = lds_par[wave];
-        Tile A, B;
-        load_tile(A, a, ptab, h, t_begin, t_end, off, lane);
+        ParLds &pl = lds_par[wave];
+        // three register tiles: two are in flight while the third is consumed
+        Tile A, B, C;
+        load_tile<F>(A, a, ptab, h, t_begin, t_end, lane);
+        if (t_begin + kTile < t_end)
+            load_tile<F>(B, a, ptab, h, t_begin + kTile, t_end, lane);
         int t0 = t_begin;
         while (true) {
-            bool more = t0 + kTile < t_end;
-            if (more)
-                load_tile(B, a, ptab, h, t0 + kTile, t_end, off, lane);
-            st.consume(A, t0, t_end, lane, qop, par_lds);
+            if (t0 + 2 * kTile < t_end)
+                load_tile<F>(C, a, ptab, h, t0 + 2 * kTile, t_end, lane);
+            st.template consume<F>(A, t0, t_end, lane, kscale, qop, pl);
             t0 += kTile;
-            if (!more)
+            if (t0 >= t_end)
                 break;
-            more = t0 + kTile < t_end;
-            if (more)
-                load_tile(A, a, ptab, h, t0 + kTile, t_end, off, lane);
-            st.consume(B, t0, t_end, lane, qop, par_lds);
+            if (t0 + 2 * kTile < t_end)
+                load_tile<F>(A, a, ptab, h, t0 + 2 * kTile, t_end, lane);
+            st.template consume<F>(B, t0, t_end, lane, kscale, qop, pl);
             t0 += kTile;
-            if (!more)
+            if (t0 >= t_end)
+                break;
+            if (t0 + 2 * kTile < t_end)
+                load_tile<F>(B, a, ptab, h, t0 + 2 * kTile, t_end, lane);
+            st.template consume<F>(C, t0, t_end, lane, kscale, qop, pl);
+            t0 += kTile;
+            if (t0 >= t_end)
                 break;
         }
     }
 
-    // ---- combine the four waves' states of this split -------------------------------------
-    st.l += wave_xor(st.l, 16);
-    st.l += wave_xor(st.l, 32);
-    st.z += wave_xor(st.z, 16);
-    st.z += wave_xor(st.z, 32);
-    if (n16 < G) {
+    // ---- the waves' (and, for F = 2, the two halves') partial states of this split -------
+    st.l = col_sum(st.l);
+    st.z = col_sum(st.z);
+    st.wsum = col_sum(st.wsum);
+    if (gl < G) {
+        const float u_even = ldexpf(16.0f, -st.E), u_odd = ldexpf(64.0f, -st.E);
+        const float zero = fmaf(8.0f, ldexpf(st.wsum, -st.E), st.z);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
-            const float unit = ldexpf((b & 1) ? 0.0625f : 1.0f, -st.E);
+            const float unit = (b & 1) ? u_odd : u_even;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                lds_o[wave][n16][32 * kq + 8 * r + b] = st.acc[b][r] * unit + st.z;
+                lds_o[wave][n16][32 * kq + 8 * r + b] = fmaf(st.acc[b][r], unit, zero);
         }
         if (kq == 0) {
             lds_m[wave][n16] = st.m;
@@ -492,16 +617,22 @@ void decode_split_kernel(DecodeArgs a)
     __syncthreads();
     for (int i = tid; i < G * kHeadDim; i += 64 * kDecodeWaves) {
         const int g = i >> 7, d = i & (kHeadDim - 1);
-        float M = lds_m[0][g];
+        float M = -INFINITY;
 #pragma unroll
-        for (int w = 1; w < kDecodeWaves; ++w)
-            M = fmaxf(M, lds_m[w][g]);
+        for (int w = 0; w < kDecodeWaves; ++w)
+#pragma unroll
+            for (int hf = 0; hf < F; ++hf)
+                M = fmaxf(M, lds_m[w][g + 8 * hf]);
         float o = 0.0f, lsum = 0.0f;
 #pragma unroll
         for (int w = 0; w < kDecodeWaves; ++w) {
-            const float f = lds_m[w][g] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lds_m[w][g] - M);
-            o += f * lds_o[w][g][d];
-            lsum += f * lds_l[w][g];
+#pragma unroll
+            for (int hf = 0; hf < F; ++hf) {
+                const int sl = g + 8 * hf;
+                const float f = lds_m[w][sl] == kNoScore ? 0.0f : __builtin_amdgcn_exp2f(lds_m[w][sl] - M);
+                o += f * lds_o[w][sl][d];
+                lsum += f * lds_l[w][sl];
+            }
         }
         const int64_t row = ((int64_t)s * a.num_q_heads + h * G + g) * a.max_splits + split;
         a.part_o[row * kHeadDim + d] = o;
@@ -603,7 +734,10 @@ template <int BK>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
 {
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    hipLaunchKernelGGL(decode_split_kernel<BK>, grid, dim3(64 * kDecodeWaves), 0, s, a);
+    if (a.group <= 8)
+        hipLaunchKernelGGL((decode_split_kernel<BK, 2>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<BK, 1>), grid, dim3(64 * kDecodeWaves), 0, s, a);
     return hipGetLastError();
 }
 
