@@ -50,6 +50,10 @@ __device__ __forceinline__ float dpp_quad_swap1(float x)
 {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
 }
+__device__ __forceinline__ float dpp_row_ror8(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float dpp_quad_swap2(float x)
 {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
@@ -129,12 +133,14 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c)
     return r;
 }
 
-// V codes become f16 MFMA operands: a nibble moved into mantissa bits 6..9 under the
-// exponent of 1.0 is the exact f16 value 1 + code / 16 (a high nibble left in bits 4..7:
-// 1 + code / 64); one packed subtraction centres it to (code - 8) / 16 (or / 64), exact,
-// so the accumulators hold small centred sums and keep their precision.  The zero point
-// then becomes zero + 8 scale: sum_t p_t (c_t s_t + z_t) = sum_t p_t s_t (c_t - 8)
+// V codes become f16 MFMA operands without arithmetic: a nibble moved into mantissa bits
+// 6..9 under the exponent of 1.0 is the exact f16 value 1 + code / 16 (a high nibble left
+// in bits 4..7: 1 + code / 64).  The accumulators are re-centred every kRecentre tiles by
+// the weight sum of those tiles (1 + c / 16 - 1.5 = (c - 8) / 16, 1 + c / 64 - 1.125 =
+// (c - 8) / 64), so they hold small centred sums and keep their precision.  The zero
+// point then becomes zero + 8 scale: sum_t p_t (c_t s_t + z_t) = sum_t p_t s_t (c_t - 8)
 // + sum_t p_t z_t + 8 sum_t p_t s_t.
+constexpr int kRecentre = 4;
 constexpr uint32_t kOne2 = 0x3C003C00u;     // f16x2 {1, 1}
 constexpr uint32_t kMant69 = 0x03C003C0u;   // mantissa bits 6..9 of both halves
 constexpr uint32_t kMant47 = 0x00F000F0u;   // mantissa bits 4..7 of both halves
@@ -185,8 +191,28 @@ struct Tile {
 // Issues the loads of the tile starting at t0 (< t_end).  A half tile that starts past
 // the end re-reads the first half's rows: every load is in bounds and unconditional, and
 // tokens past the end are removed by their parameters (zero) and score bias (-inf).
+// Page ids of up to 64 consecutive pages of a sequence, one per lane, so a tile's pages
+// come from readlane instead of a scalar load whose latency every tile would wait for.
+struct PageIds {
+    int first;   // page index held by lane 0 (uniform)
+    int id;      // lane j: page id of page index first + j (out-of-range ids read as 0)
+
+    __device__ __forceinline__ void fill(const DecodeArgs &a, const int32_t *ptab, int first_page,
+                                         int lane)
+    {
+        first = first_page;
+        const int k = first_page + lane;
+        const int v = k < a.max_pages ? ptab[k] : 0;
+        id = (unsigned)v < (unsigned)a.num_pages ? v : 0;
+    }
+    __device__ __forceinline__ int page(int page_index) const
+    {
+        return __builtin_amdgcn_readlane(id, page_index - first);
+    }
+};
+
 template <int F>
-__device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const int32_t *ptab, int h,
+__device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const PageIds &pid, int h,
                                           int t0, int t_end, int lane)
 {
     const int P = 1 << a.page_log2;
@@ -197,8 +223,7 @@ __device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const in
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
         const int tb = hf && t0 + 16 >= t_end ? t0 : t0 + 16 * hf;
-        int page = ptab[tb >> a.page_log2];
-        page = (unsigned)page < (unsigned)a.num_pages ? page : 0;
+        const int page = pid.page(tb >> a.page_log2);
         const int64_t cell0 = ((int64_t)page * a.num_kv_heads + h) * P + (tb & (P - 1));
         kb[hf] = a.k_codes + cell0 * kRowCodeBytes;
         vb[hf] = a.v_codes + cell0 * kRowCodeBytes;
@@ -231,8 +256,9 @@ __device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const in
 //          of head n16;
 //   F = 2: v[2 j + par][digit][lane]: channel 64 (kq % 2) + 32 j + 2 e + par of head n16 % 8
 //          for lanes with (n16 / 8) == (kq / 2), zero for the others.
+template <int F>
 struct QOperand {
-    i32x4 v[4][3][64];
+    i32x4 v[2 * F][3][64];
 };
 
 // Parameters of one tile in fp32, per wave: [0] scale (K: times 2^-f), [1] zero,
@@ -249,12 +275,32 @@ struct WaveState {
     float wsum;                 // sum of the PV weights w, scaled like acc
     int E;                      // weights enter the PV product as w = p * scale_V * 2^E
     float slim;                 // 2^(6 - E): a V scale this large needs a smaller E
+    float wpend;                // this lane's weights since the last re-centring
+    int nt;                     // tiles since the last re-centring
     f32x4 acc[8];               // sum_t w_t (code - 8) / u_b, d = 8 (4 kq + r) + b,
-                                // u_b = 16 (even b) or 64 (odd b)
+                                // u_b = 16 (even b) or 64 (odd b), once re-centred
+
+    // take the constant parts 1.5 w (even b) and 1.125 w (odd b) out of the accumulators
+    __device__ __forceinline__ void recentre()
+    {
+        const float W = col_sum(wpend);
+        const float we = -1.5f * W, wo = -1.125f * W;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            acc[b] += (b & 1) ? wo : we;
+        wpend = 0.0f;
+        nt = 0;
+    }
+
+    __device__ __forceinline__ void tick()
+    {
+        if (++nt == kRecentre)
+            recentre();
+    }
 
     template <int F>
     __device__ __forceinline__ void consume(const Tile &T, int t0, int t_end, int lane, float kscale,
-                                            const QOperand &qop, ParLds &pl)
+                                            const QOperand<F> &qop, ParLds &pl)
     {
         constexpr int NS = 8 / F;            // scores per lane
         const int n16 = lane & 15, kq = lane >> 4;
@@ -361,6 +407,7 @@ struct WaveState {
             l *= alpha;
             z *= alpha;
             wsum *= acc_f;
+            wpend *= acc_f;
 #pragma unroll
             for (int b = 0; b < 8; ++b)
                 acc[b] *= acc_f;
@@ -383,13 +430,15 @@ struct WaveState {
         l = fmaf(psum, uE, l);
         z = fmaf(pz, uE, z);
         wsum += ws;
-        // B operand of PV, f16 high and low parts (high rounded toward zero, so the low
-        // part keeps the rest): k slot e of lane (n16, kq) is token 16 (e / 4) + 4 kq + e % 4
+        wpend += ws;
+        // B operand of PV, f16 high and low parts, both rounded to nearest (an unbiased
+        // split: the removed constant part of the V operands then adds no drift):
+        // k slot e of lane (n16, kq) is token 16 (e / 4) + 4 kq + e % 4
         uint32_t hp[NS / 2], lp[NS / 2];
 #pragma unroll
         for (int j = 0; j < NS / 2; ++j) {
-            const auto h = __builtin_amdgcn_cvt_pkrtz(w[2 * j], w[2 * j + 1]);
-            const auto r = __builtin_amdgcn_cvt_pkrtz(w[2 * j] - (float)h[0], w[2 * j + 1] - (float)h[1]);
+            const f16x2 h = {(_Float16)w[2 * j], (_Float16)w[2 * j + 1]};
+            const f16x2 r = {(_Float16)(w[2 * j] - (float)h[0]), (_Float16)(w[2 * j + 1] - (float)h[1])};
             hp[j] = __builtin_bit_cast(uint32_t, h);
             lp[j] = __builtin_bit_cast(uint32_t, r);
         }
@@ -412,18 +461,14 @@ struct WaveState {
             for (int p = 0; p < 4; ++p)
                 src[p] = __builtin_amdgcn_perm(T.vc[2 * p + 1], T.vc[2 * p],
                                                0x0C000C00u | ((4u + k) << 16) | (uint32_t)k);
-            f16x8 al, ah;
+            u32x4 lo, hi;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const f16x2 lo = __builtin_bit_cast(f16x2, and_or(src[p] << 6, kMant69, kOne2));
-                const f16x2 hi = __builtin_bit_cast(f16x2, and_or(src[p], kMant47, kOne2));
-                const f16x2 cl = lo - f16x2{(_Float16)1.5f, (_Float16)1.5f};
-                const f16x2 ch = hi - f16x2{(_Float16)1.125f, (_Float16)1.125f};
-                al[2 * p] = cl[0];
-                al[2 * p + 1] = cl[1];
-                ah[2 * p] = ch[0];
-                ah[2 * p + 1] = ch[1];
+                lo[p] = and_or(src[p] << 6, kMant69, kOne2);
+                hi[p] = and_or(src[p], kMant47, kOne2);
             }
+            const f16x8 al = __builtin_bit_cast(f16x8, lo);
+            const f16x8 ah = __builtin_bit_cast(f16x8, hi);
             acc[2 * k] = mfma16x16x32(al, bh, acc[2 * k]);
             acc[2 * k] = mfma16x16x32(al, bl, acc[2 * k]);
             acc[2 * k + 1] = mfma16x16x32(ah, bh, acc[2 * k + 1]);
@@ -433,7 +478,7 @@ struct WaveState {
 };
 
 template <int BK, int F>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? 3 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? 4 : 2)))
 void decode_split_kernel(DecodeArgs a)
 {
     const int split = blockIdx.x;
@@ -454,14 +499,17 @@ void decode_split_kernel(DecodeArgs a)
     const int t_end = min(L, t_begin + wave_tokens);
 
     // rotated query rows in the prologue, the waves' partial states in the epilogue
-    __shared__ float lds_o[kDecodeWaves][16][kHeadDim + 4];
-    __shared__ QOperand qop;
+    // (F = 2: the two halves of each column are merged inside the wave first, so one slot
+    // per query head and wave)
+    constexpr int kSlots = F == 2 ? 8 : 16;
+    __shared__ float lds_o[kDecodeWaves][kSlots][kHeadDim + 4];
+    __shared__ QOperand<F> qop;
     __shared__ ParLds lds_par[kDecodeWaves];
-    __shared__ float lds_m[kDecodeWaves][16];
-    __shared__ float lds_l[kDecodeWaves][16];
+    __shared__ float lds_m[kDecodeWaves][kSlots];
+    __shared__ float lds_l[kDecodeWaves][kSlots];
     __shared__ float lds_qsum[kMaxGroup];
     __shared__ float lds_kscale;
-    float(*q_lds)[kHeadDim + 4] = lds_o[0];
+    float(*q_lds)[kHeadDim + 4] = reinterpret_cast<float(*)[kHeadDim + 4]>(&lds_o[0][0][0]);
 
     // ---- a6: wave 0 rotates the G queries of this KV head, folds sm_scale * log2(e) ---------
     if (wave == 0) {
@@ -558,6 +606,8 @@ void decode_split_kernel(DecodeArgs a)
     st.wsum = 0.0f;
     st.E = 64;
     st.slim = 0x1p-58f;   // 2^(6 - E)
+    st.wpend = 0.0f;
+    st.nt = 0;
 #pragma unroll
     for (int b = 0; b < 8; ++b)
         st.acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -565,77 +615,95 @@ void decode_split_kernel(DecodeArgs a)
 
     // ---- a7: page walk, one tile ahead of the math --------------------------------------
     const int32_t *ptab = a.page_table + (int64_t)s * a.max_pages;
-    if (t_begin < t_end) {
-        ParLds &pl = lds_par[wave];
-        // three register tiles: two are in flight while the third is consumed
-        Tile A, B, C;
-        load_tile<F>(A, a, ptab, h, t_begin, t_end, lane);
-        if (t_begin + kTile < t_end)
-            load_tile<F>(B, a, ptab, h, t_begin + kTile, t_end, lane);
-        int t0 = t_begin;
+    ParLds &pl = lds_par[wave];
+    // the range in chunks of at most 1024 tokens: starting 32-aligned, a chunk spans at most
+    // 64 pages of 16 tokens, whose ids one register holds
+    for (int cb = t_begin; cb < t_end; cb += 1024) {
+        const int ce = min(t_end, cb + 1024);
+        PageIds pid;
+        pid.fill(a, ptab, cb >> a.page_log2, lane);
+        // two register tiles, each refilled with the tile two ahead right after it is
+        // consumed (at most 128 VGPRs, so four waves share a SIMD).  The loads are
+        // unconditional (a prefetch past the end re-reads the last tile, an L2 hit), so the
+        // same loads are in flight at every point of the loop and the wait before a tile
+        // covers only that tile's loads.
+        const int t_last = cb + (ce - 1 - cb) / kTile * kTile;
+        Tile A, B;
+        load_tile<F>(A, a, pid, h, cb, ce, lane);
+        load_tile<F>(B, a, pid, h, min(cb + kTile, t_last), ce, lane);
+        int t0 = cb;
         while (true) {
-            if (t0 + 2 * kTile < t_end)
-                load_tile<F>(C, a, ptab, h, t0 + 2 * kTile, t_end, lane);
-            st.template consume<F>(A, t0, t_end, lane, kscale, qop, pl);
-            t0 += kTile;
-            if (t0 >= t_end)
+            st.template consume<F>(A, t0, ce, lane, kscale, qop, pl);
+            st.tick();
+            if (t0 + kTile >= ce)
                 break;
-            if (t0 + 2 * kTile < t_end)
-                load_tile<F>(A, a, ptab, h, t0 + 2 * kTile, t_end, lane);
-            st.template consume<F>(B, t0, t_end, lane, kscale, qop, pl);
+            load_tile<F>(A, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
             t0 += kTile;
-            if (t0 >= t_end)
+            st.template consume<F>(B, t0, ce, lane, kscale, qop, pl);
+            st.tick();
+            if (t0 + kTile >= ce)
                 break;
-            if (t0 + 2 * kTile < t_end)
-                load_tile<F>(B, a, ptab, h, t0 + 2 * kTile, t_end, lane);
-            st.template consume<F>(C, t0, t_end, lane, kscale, qop, pl);
+            load_tile<F>(B, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
             t0 += kTile;
-            if (t0 >= t_end)
-                break;
         }
     }
 
     // ---- the waves' (and, for F = 2, the two halves') partial states of this split -------
+    st.recentre();
     st.l = col_sum(st.l);
     st.z = col_sum(st.z);
     st.wsum = col_sum(st.wsum);
-    if (gl < G) {
+    float o[8][4];
+    {
         const float u_even = ldexpf(16.0f, -st.E), u_odd = ldexpf(64.0f, -st.E);
         const float zero = fmaf(8.0f, ldexpf(st.wsum, -st.E), st.z);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const float unit = (b & 1) ? u_odd : u_even;
+        for (int b = 0; b < 8; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                lds_o[wave][n16][32 * kq + 8 * r + b] = fmaf(st.acc[b][r], unit, zero);
-        }
+                o[b][r] = fmaf(st.acc[b][r], (b & 1) ? u_odd : u_even, zero);
+    }
+    float m_w = st.m, l_w = st.l;
+    if constexpr (F == 2) {
+        // lanes n16 and n16 ^ 8 (one 16-lane row) hold the two halves of head n16 % 8
+        const float m_o = dpp_row_ror8(st.m);
+        const float M = fmaxf(st.m, m_o);
+        const float fa = __builtin_amdgcn_exp2f(st.m - M), fb = __builtin_amdgcn_exp2f(m_o - M);
+        l_w = st.l * fa + dpp_row_ror8(st.l) * fb;
+        m_w = M;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                o[b][r] = o[b][r] * fa + dpp_row_ror8(o[b][r]) * fb;
+    }
+    if (n16 < kSlots && gl < G) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                lds_o[wave][n16][32 * kq + 8 * r + b] = o[b][r];
         if (kq == 0) {
-            lds_m[wave][n16] = st.m;
-            lds_l[wave][n16] = st.l;
+            lds_m[wave][n16] = m_w;
+            lds_l[wave][n16] = l_w;
         }
     }
     __syncthreads();
     for (int i = tid; i < G * kHeadDim; i += 64 * kDecodeWaves) {
         const int g = i >> 7, d = i & (kHeadDim - 1);
-        float M = -INFINITY;
+        float M = lds_m[0][g];
 #pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w)
-#pragma unroll
-            for (int hf = 0; hf < F; ++hf)
-                M = fmaxf(M, lds_m[w][g + 8 * hf]);
-        float o = 0.0f, lsum = 0.0f;
+        for (int w = 1; w < kDecodeWaves; ++w)
+            M = fmaxf(M, lds_m[w][g]);
+        float acc = 0.0f, lsum = 0.0f;
 #pragma unroll
         for (int w = 0; w < kDecodeWaves; ++w) {
-#pragma unroll
-            for (int hf = 0; hf < F; ++hf) {
-                const int sl = g + 8 * hf;
-                const float f = lds_m[w][sl] == kNoScore ? 0.0f : __builtin_amdgcn_exp2f(lds_m[w][sl] - M);
-                o += f * lds_o[w][sl][d];
-                lsum += f * lds_l[w][sl];
-            }
+            const float f = __builtin_amdgcn_exp2f(lds_m[w][g] - M);
+            acc += f * lds_o[w][g][d];
+            lsum += f * lds_l[w][g];
         }
         const int64_t row = ((int64_t)s * a.num_q_heads + h * G + g) * a.max_splits + split;
-        a.part_o[row * kHeadDim + d] = o;
+        a.part_o[row * kHeadDim + d] = acc;
         if (d == 0) {
             a.part_ml[2 * row] = M;
             a.part_ml[2 * row + 1] = lsum;
