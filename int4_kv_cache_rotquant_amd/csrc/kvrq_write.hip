@@ -99,24 +99,24 @@ __device__ __forceinline__ void rotate_row(float (&x)[32], int ql)
 // The raw input of one tile as this lane holds it.
 struct RowLoad {
     u32x4 raw[4];     // 32 bf16 channels
-    int32_t slot;     // < 0: nothing to store
+    int32_t slot;     // slot of the row's token
+    bool valid;       // false past the last token: nothing is stored
 };
 
+// Issues the loads of one row.  Rows past the last token re-read the last token and are
+// marked invalid: every load is unconditional, so the loads of the next tile stay in
+// flight while the current one is encoded (a conditional load would make the compiler
+// wait for all outstanding loads where the paths join).
 __device__ __forceinline__ void load_row(RowLoad &R, const uint16_t *src_base, int64_t stride,
                                          const int32_t *slots, int64_t t, int64_t num_tokens, int ql)
 {
-    if (t < num_tokens) {
-        R.slot = slots[t];
-        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src_base + t * stride + 32 * ql);
+    R.valid = t < num_tokens;
+    const int64_t tc = R.valid ? t : num_tokens - 1;
+    R.slot = slots[tc];
+    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src_base + tc * stride + 32 * ql);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            R.raw[j] = s4[j];
-    } else {
-        R.slot = -1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            R.raw[j] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int j = 0; j < 4; ++j)
+        R.raw[j] = s4[j];
 }
 
 // Rotate, quantise and store one row held in x; called by all four lanes of the quad.
@@ -208,29 +208,32 @@ void rotquant_write_kernel(WriteArgs a)
         load_row(R, src + h * kHeadDim, stride, a.slots, tt * kWriteTile + row, a.num_tokens, ql);
     };
 
-    // One register set: once a tile's bf16 input is widened to fp32, the same registers
-    // take the next tile's loads, which then fly while this tile is encoded.
-    RowLoad R;
-    issue(R, a.k, a.k_stride, pair);
+    // Two register sets, K and V: each is refilled with the next pair's tile as soon as
+    // its bf16 input is widened to fp32, so up to two tiles are in flight while one is
+    // encoded.
+    RowLoad RK, RV;
+    issue(RK, a.k, a.k_stride, pair);
+    issue(RV, a.v, a.v_stride, pair);
     while (true) {
         const int h = (int)(pair % a.num_kv_heads);
+        const int64_t next = pair + stride_w;
+        const bool more = next < num_pairs;
+        const int64_t pf = more ? next : pair;   // past the end: re-read this pair (no store)
         float x[32];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            bf16x8_to_f32(R.raw[j], x + 8 * j);
-        int32_t slot = R.slot;
-        issue(R, a.v, a.v_stride, pair);
+            bf16x8_to_f32(RK.raw[j], x + 8 * j);
+        int32_t slot = RK.valid ? RK.slot : -1;
+        issue(RK, a.k, a.k_stride, pf);
         encode_row<BK>(x, slot, a.k_codes, a.k_params, a.num_slots, a.num_kv_heads, a.page_log2, h, ql);
 
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            bf16x8_to_f32(R.raw[j], x + 8 * j);
-        slot = R.slot;
-        const int64_t next = pair + stride_w;
-        if (next < num_pairs)
-            issue(R, a.k, a.k_stride, next);
+            bf16x8_to_f32(RV.raw[j], x + 8 * j);
+        slot = RV.valid ? RV.slot : -1;
+        issue(RV, a.v, a.v_stride, pf);
         encode_row<BV>(x, slot, a.v_codes, a.v_params, a.num_slots, a.num_kv_heads, a.page_log2, h, ql);
-        if (next >= num_pairs)
+        if (!more)
             break;
         pair = next;
     }
