@@ -140,7 +140,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c)
 // (c - 8) / 64), so they hold small centred sums and keep their precision.  The zero
 // point then becomes zero + 8 scale: sum_t p_t (c_t s_t + z_t) = sum_t p_t s_t (c_t - 8)
 // + sum_t p_t z_t + 8 sum_t p_t s_t.
-constexpr int kRecentre = 4;
+constexpr int kRecentre = 8;
 constexpr uint32_t kOne2 = 0x3C003C00u;     // f16x2 {1, 1}
 constexpr uint32_t kMant69 = 0x03C003C0u;   // mantissa bits 6..9 of both halves
 constexpr uint32_t kMant47 = 0x00F000F0u;   // mantissa bits 4..7 of both halves
@@ -243,8 +243,8 @@ __device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const Pa
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            T.vc[4 * hf + r] =
-                *reinterpret_cast<const uint32_t *>(vb[hf] + (4 * kq + r) * kRowCodeBytes + 4 * n16);
+            T.vc[4 * hf + r] = *reinterpret_cast<const uint32_t *>(
+                vb[hf] + (uint32_t)((4 * kq + r) * kRowCodeBytes + 4 * n16));
     }
     const int ph = (lane >> 4) & 1;
     T.par = *((lane < 32 ? (ph ? kp[1] : kp[0]) : (ph ? vp[1] : vp[0])) + (lane & 15));
