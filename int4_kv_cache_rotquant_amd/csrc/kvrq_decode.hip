@@ -25,8 +25,9 @@
 // Lane (n16, kq) keeps query head g = n16, so the softmax state needs no
 // cross-lane exchange except for the per-tile maxima.  The four waves' states
 // are merged in LDS into one split partial (o, m, l).
-// Launch 2 -- decode_combine_kernel, one workgroup per (query head, sequence):
-// log-sum-exp combine of the splits, then the inverse V rotation.
+// Launch 2 -- log-sum-exp combine of the splits, then the inverse V rotation:
+// decode_combine_wave_kernel (one wave per (query head, sequence)) for up to 64 splits,
+// decode_combine_kernel (one workgroup per (query head, sequence)) beyond.
 #include <hip/hip_runtime.h>
 
 #include "kvrq_internal.h"
@@ -711,6 +712,28 @@ void decode_split_kernel(DecodeArgs a)
     }
 }
 
+// Inverse V rotation of one output row held as channels (2 lane, 2 lane + 1) by the
+// 64 lanes of a wave: width 1 in-lane, widths 2.. across lanes.
+template <int BV>
+__device__ __forceinline__ void inverse_rotate_pair(float &o0, float &o1, int lane)
+{
+    if constexpr (BV > 1) {
+        const float u = o0 + o1, w = o0 - o1;
+        o0 = u;
+        o1 = w;
+#pragma unroll
+        for (int hw = 2; hw < BV; hw <<= 1) {
+            const int m = hw >> 1;
+            const float p0 = wave_xor(o0, m), p1 = wave_xor(o1, m);
+            const bool upper = lane & m;
+            o0 = upper ? p0 - o0 : o0 + p0;
+            o1 = upper ? p1 - o1 : o1 + p1;
+        }
+        o0 *= InvSqrtF<BV>::value;
+        o1 *= InvSqrtF<BV>::value;
+    }
+}
+
 // ---- a10: combine the splits of one (sequence, query head), undo the V rotation ---------
 template <int BV>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a)
@@ -779,22 +802,70 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a)
     o0 *= inv_l;
     o1 *= inv_l;
     const int lane = tid;
-    if constexpr (BV > 1) {
-        // lane holds channels 2 lane, 2 lane + 1: width 1 in-lane, widths 2.. across lanes
-        float u = o0 + o1, w = o0 - o1;
-        o0 = u;
-        o1 = w;
-#pragma unroll
-        for (int hw = 2; hw < BV; hw <<= 1) {
-            const int m = hw >> 1;
-            const float p0 = wave_xor(o0, m), p1 = wave_xor(o1, m);
-            const bool upper = lane & m;
-            o0 = upper ? p0 - o0 : o0 + p0;
-            o1 = upper ? p1 - o1 : o1 + p1;
-        }
-        o0 *= InvSqrtF<BV>::value;
-        o1 *= InvSqrtF<BV>::value;
+    inverse_rotate_pair<BV>(o0, o1, lane);
+    *reinterpret_cast<float2 *>(out + 2 * lane) = make_float2(o0, o1);
+}
+
+// ---- a10 for up to 64 splits: one wave per (sequence, query head) ---------------------
+// Lane j holds split j's maximum and normaliser, so the log-sum-exp weights come from
+// two wave reductions; the partial outputs are then summed with each split's weight
+// broadcast from its lane.  No barrier, four query heads per workgroup.
+template <int BV>
+__global__ __launch_bounds__(256) void decode_combine_wave_kernel(DecodeArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int s = blockIdx.y;
+    if (g >= a.num_q_heads)
+        return;
+    const int L = min(a.seq_lens[s], a.max_seq_len);
+    float *out = a.out + ((int64_t)s * a.num_q_heads + g) * kHeadDim;
+    if (L <= 0) {
+        *reinterpret_cast<float2 *>(out + 2 * lane) = make_float2(0.0f, 0.0f);
+        return;
     }
+    const int n = (L + a.split_tokens - 1) / a.split_tokens;   // 1..64
+    const int64_t row0 = ((int64_t)s * a.num_q_heads + g) * a.max_splits;
+    float m = -INFINITY, l = 0.0f;
+    if (lane < n) {
+        const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * (row0 + lane));
+        m = ml.x;
+        l = ml.y;
+    }
+    float M = m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        M = fmaxf(M, wave_xor(M, o));
+    const float wj = lane < n ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+    float lsum = wj * l;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        lsum += wave_xor(lsum, o);
+    const float *po = a.part_o + row0 * kHeadDim + 2 * lane;
+    float o0 = 0.0f, o1 = 0.0f;
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {
+        float2 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            v[k] = *reinterpret_cast<const float2 *>(po + (int64_t)(i + k) * kHeadDim);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), i + k));
+            o0 = fmaf(w, v[k].x, o0);
+            o1 = fmaf(w, v[k].y, o1);
+        }
+    }
+    for (; i < n; ++i) {
+        const float2 v = *reinterpret_cast<const float2 *>(po + (int64_t)i * kHeadDim);
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), i));
+        o0 = fmaf(w, v.x, o0);
+        o1 = fmaf(w, v.y, o1);
+    }
+    const float inv_l = 1.0f / lsum;
+    o0 *= inv_l;
+    o1 *= inv_l;
+    inverse_rotate_pair<BV>(o0, o1, lane);
     *reinterpret_cast<float2 *>(out + 2 * lane) = make_float2(o0, o1);
 }
 
@@ -812,8 +883,13 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
 template <int BV>
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
-    hipLaunchKernelGGL(decode_combine_kernel<BV>, grid, dim3(256), 0, s, a);
+    if (a.max_splits <= 64) {
+        const dim3 grid((unsigned)((a.num_q_heads + 3) / 4), (unsigned)a.num_seqs);
+        hipLaunchKernelGGL(decode_combine_wave_kernel<BV>, grid, dim3(256), 0, s, a);
+    } else {
+        const dim3 grid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
+        hipLaunchKernelGGL(decode_combine_kernel<BV>, grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -125,6 +125,26 @@ def test_split_sweep_consistent(K):
         assert np.max(np.abs(o - outs[0])) < 1e-4
 
 
+def test_combine_split_counts_around_64(K):
+    """64 splits is the largest count combined one wave per query head; 65 takes the
+    workgroup-per-head combine.  Both must agree with the oracle and with each other."""
+    lens = [8192, 8191, 129]
+    cache, orc, q, tab, L = _build(K, lens, 1, 8, 16, 64, 32, seed=21)
+    ref = _ref(orc, q, tab, L, 1, 16, 64, 32)
+    # one more (unused) page-table column so that max_seq_len 8193 is a valid bound
+    tab = np.concatenate([tab, np.full((tab.shape[0], 1), -1, np.int32)], axis=1)
+    outs = []
+    for split, maxlen in ((128, 8192), (128, 8193)):   # 64 and 65 splits
+        import torch
+        out = K.kv_int4_paged_decode(cache, bf16_dev(q), to_dev(tab), to_dev(L), maxlen,
+                                     split_tokens=split)
+        torch.cuda.synchronize()
+        out = out.cpu().numpy()
+        decode_compare(out, ref, f"split{split}/maxlen{maxlen}")
+        outs.append(out)
+    assert np.max(np.abs(outs[0] - outs[1])) < 1e-5
+
+
 def test_page_permutation_bit_identical(K):
     lens = [500, 129]
     c1, o1, q1, t1, L1 = _build(K, lens, 2, 8, 16, 128, 0, seed=12, permute=False)
