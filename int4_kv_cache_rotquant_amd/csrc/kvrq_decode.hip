@@ -27,7 +27,7 @@
 // are merged in LDS into one split partial (o, m, l).
 // Launch 2 -- log-sum-exp combine of the splits, then the inverse V rotation:
 // decode_combine_wave_kernel (one wave per (query head, sequence)) for up to 64 splits,
-// decode_combine_kernel (one workgroup per (query head, sequence)) beyond.
+// decode_combine_kernel (a 16-wave workgroup per (query head, sequence)) beyond.
 #include <hip/hip_runtime.h>
 
 #include "kvrq_internal.h"
@@ -736,11 +736,13 @@ __device__ __forceinline__ void inverse_rotate_pair(float &o0, float &o1, int la
 
 // ---- a10: combine the splits of one (sequence, query head), undo the V rotation ---------
 template <int BV>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a)
+__global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a)
 {
+    // one workgroup of 16 waves per (query head, sequence), for many splits
     const int g = blockIdx.x;
     const int s = blockIdx.y;
     const int tid = threadIdx.x;
+    const int wave = tid >> 6;
     const int L = min(a.seq_lens[s], a.max_seq_len);
     float *out = a.out + ((int64_t)s * a.num_q_heads + g) * kHeadDim;
     if (L <= 0) {
@@ -752,37 +754,38 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a)
     const int64_t row0 = ((int64_t)s * a.num_q_heads + g) * a.max_splits;
     const float *ml = a.part_ml + 2 * row0;
 
-    __shared__ float red[8];
-    __shared__ float part[8][kHeadDim];
+    __shared__ float red[32];
+    __shared__ float part[32][kHeadDim];
 
     // global max and normaliser over the splits
     float M = -INFINITY;
-    for (int i = tid; i < n; i += 256)
+    for (int i = tid; i < n; i += 1024)
         M = fmaxf(M, ml[2 * i]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         M = fmaxf(M, wave_xor(M, o));
     if ((tid & 63) == 0)
-        red[tid >> 6] = M;
+        red[wave] = M;
     __syncthreads();
-    M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    M = red[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w)
+        M = fmaxf(M, red[w]);
     float l = 0.0f;
-    for (int i = tid; i < n; i += 256)
+    for (int i = tid; i < n; i += 1024)
         l += __builtin_amdgcn_exp2f(ml[2 * i] - M) * ml[2 * i + 1];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1)
         l += wave_xor(l, o);
-    __syncthreads();
     if ((tid & 63) == 0)
-        red[4 + (tid >> 6)] = l;
-    __syncthreads();
-    l = red[4] + red[5] + red[6] + red[7];
+        red[16 + wave] = l;
 
-    // weighted sum of the partial outputs: thread = (split residue sub, 4 channels)
+    // weighted sum of the partial outputs: thread = (split residue sub of 32, 4 channels)
     const int sub = tid >> 5, dq = tid & 31;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     const float *po = a.part_o + row0 * kHeadDim + 4 * dq;
-    for (int i = sub; i < n; i += 8) {
+#pragma unroll 4
+    for (int i = sub; i < n; i += 32) {
         const float w = __builtin_amdgcn_exp2f(ml[2 * i] - M);
         acc += w * *reinterpret_cast<const f32x4 *>(po + (int64_t)i * kHeadDim);
     }
@@ -792,10 +795,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a)
     __syncthreads();
     if (tid >= 64)
         return;
+    l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w)
+        l += red[16 + w];
     const float inv_l = 1.0f / l;
     float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
         o0 += part[k][2 * tid];
         o1 += part[k][2 * tid + 1];
     }
@@ -888,7 +895,7 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t s)
         hipLaunchKernelGGL(decode_combine_wave_kernel<BV>, grid, dim3(256), 0, s, a);
     } else {
         const dim3 grid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
-        hipLaunchKernelGGL(decode_combine_kernel<BV>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(decode_combine_kernel<BV>, grid, dim3(1024), 0, s, a);
     }
     return hipGetLastError();
 }
