@@ -73,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.kvrq_oracle_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, i32, P,
                                          f64, P, P, P, P, P]
         L.kvrq_oracle_decode.restype = i32
+        L.kvrq_oracle_extend.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, i32, P,
+                                         ctypes.c_double, P, P, P, P, P]
+        L.kvrq_oracle_extend.restype = i32
         _lib = L
     return _lib
 
@@ -188,6 +191,33 @@ def decode(q: np.ndarray, cache_arrays, page_table: np.ndarray, seq_lens: np.nda
                                   float(sm_scale), _p(kc), _p(vc), _p(kp), _p(vp), _p(out))
     if rc == 1:
         raise ValueError("bad decode shapes")
+    if rc == 2:
+        raise ValueError("page id outside the pool")
+    return out
+
+
+def extend(q: np.ndarray, cache_arrays, qo_start: np.ndarray, page_table: np.ndarray,
+           seq_lens: np.ndarray, num_kv_heads: int, page_size: int, k_block: int, v_block: int,
+           sm_scale: float = 0.0) -> np.ndarray:
+    """fp64 causal extend attention: ``q`` [total_q][Hq][D] bf16 bits; the rows
+    qo_start[s]..qo_start[s+1]-1 are the last tokens of sequence s (of seq_lens[s])."""
+    q = np.ascontiguousarray(q, np.uint16)
+    total_q, Hq, D = q.shape
+    kc, vc, kp, vp = [np.ascontiguousarray(a) for a in cache_arrays]
+    num_pages = kc.shape[0]
+    qo_start = np.ascontiguousarray(qo_start, np.int32)
+    page_table = np.ascontiguousarray(page_table, np.int32)
+    seq_lens = np.ascontiguousarray(seq_lens, np.int32)
+    S = seq_lens.shape[0]
+    if qo_start.shape != (S + 1,) or qo_start[-1] != total_q:
+        raise ValueError("qo_start must have S+1 entries ending at total_q")
+    out = np.zeros((total_q, Hq, D), np.float64)
+    rc = lib().kvrq_oracle_extend(S, Hq, num_kv_heads, D, page_size, num_pages, k_block,
+                                  v_block, _p(q), _p(qo_start), _p(page_table),
+                                  page_table.shape[1], _p(seq_lens), float(sm_scale), _p(kc),
+                                  _p(vc), _p(kp), _p(vp), _p(out))
+    if rc == 1:
+        raise ValueError("bad extend shapes")
     if rc == 2:
         raise ValueError("page id outside the pool")
     return out

@@ -118,3 +118,36 @@ def decode(q_bf16: np.ndarray, cache_arrays, page_table: np.ndarray, seq_lens, n
             p /= p.sum(axis=1, keepdims=True)
             out[s, h * G:(h + 1) * G] = (p @ V) @ HV.T    # back to the unrotated basis
     return out
+
+
+def extend(q_bf16: np.ndarray, cache_arrays, qo_start, page_table: np.ndarray, seq_lens,
+           num_kv_heads: int, page_size: int, k_block: int, v_block: int,
+           sm_scale: float = 0.0) -> np.ndarray:
+    """fp64 causal extend attention with explicit matrices and an explicit mask: the n
+    query rows of sequence s are its last n positions; row i sees tokens 0..L-n+i."""
+    q = bf16_to_f32(q_bf16).astype(np.float64)
+    total_q, Hq, D = q.shape
+    G = Hq // num_kv_heads
+    if sm_scale <= 0:
+        sm_scale = 1.0 / np.sqrt(D)
+    HK = hadamard_blockdiag(D, k_block)
+    HV = hadamard_blockdiag(D, v_block)
+    out = np.zeros((total_q, Hq, D))
+    for s in range(len(seq_lens)):
+        r0, r1 = int(qo_start[s]), int(qo_start[s + 1])
+        n, L = r1 - r0, int(seq_lens[s])
+        if n == 0:
+            continue
+        pos = L - n + np.arange(n)                              # query positions
+        mask = np.arange(L)[None, :] <= pos[:, None]            # [n][L], causal
+        for h in range(num_kv_heads):
+            K, V = gather_seq(cache_arrays, page_table[s], L, page_size, h)
+            for g in range(h * G, (h + 1) * G):
+                qs = q[r0:r1, g] @ HK.T                         # [n][D]
+                scores = sm_scale * (qs @ K.T)
+                scores = np.where(mask, scores, -np.inf)
+                scores -= scores.max(axis=1, keepdims=True)
+                p = np.exp(scores)
+                p /= p.sum(axis=1, keepdims=True)
+                out[r0:r1, g] = (p @ V) @ HV.T
+    return out

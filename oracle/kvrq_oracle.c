@@ -296,6 +296,79 @@ ORACLE_API int kvrq_oracle_write(int T, int Hkv, int D, int P, int num_pages, in
 /* decode (fp64, plain definition)                                          */
 /* ---------------------------------------------------------------------- */
 
+/* Softmax attention of one query row over tokens 0..L-1 of KV head h of one
+ * sequence, written from its definition (wispaper.ai blog, section 3: the query is
+ * rotated by the K block matrix; V is stored rotated and the output is rotated back):
+ *   q' = H_K q;  k_t = c_t s_t + z_t, v_t likewise (read from the stored codes and
+ *   fp16 parameters at page_row[t / P], offset t % P);
+ *   p_t = exp(sm_scale q'.k_t - max);  o = H_V (sum_t p_t v_t / sum_t p_t).
+ * qrow: bf16 bits [D]; o: fp64 [D]; L <= 0 gives zeros.  Returns 1 when a page id is
+ * outside the pool (those tokens are left out). */
+static int attend_row(const uint16_t *qrow, int L, const int32_t *page_row, int h, int Hkv,
+                      int D, int P, int num_pages, int k_block, int v_block, double sm_scale,
+                      const uint8_t *k_codes, const uint8_t *v_codes,
+                      const uint16_t *k_params, const uint16_t *v_params, double *o)
+{
+    double qx[1024], qr[1024], acc[1024], kh[1024];
+    int bad = 0;
+    for (int d = 0; d < D; ++d)
+        acc[d] = 0.0;
+    if (L <= 0) {
+        for (int d = 0; d < D; ++d)
+            o[d] = 0.0;
+        return 0;
+    }
+    for (int d = 0; d < D; ++d)
+        qx[d] = (double)kvrq_oracle_bf16_to_f32(qrow[d]);
+    kvrq_oracle_rotate_f64(qx, qr, D, k_block);
+
+    double *score = (double *)malloc(sizeof(double) * (size_t)L);
+    double m = -INFINITY;
+    for (int t = 0; t < L; ++t) {
+        const int32_t page = page_row[t / P];
+        if (page < 0 || page >= num_pages) {
+            bad = 1;
+            score[t] = -INFINITY;
+            continue;
+        }
+        const int64_t cell = ((int64_t)page * Hkv + h) * P + t % P;
+        const double sc = kvrq_oracle_f16_to_f32(k_params[cell * 2 + 0]);
+        const double zr = kvrq_oracle_f16_to_f32(k_params[cell * 2 + 1]);
+        const uint8_t *c = k_codes + cell * (D / 2);
+        for (int d = 0; d < D; ++d) {
+            const int code = (d & 1) ? (c[d / 2] >> 4) : (c[d / 2] & 15);
+            kh[d] = code * sc + zr;
+        }
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d)
+            dot += qr[d] * kh[d];
+        score[t] = sm_scale * dot;
+        if (score[t] > m)
+            m = score[t];
+    }
+    double l = 0.0;
+    for (int t = 0; t < L; ++t) {
+        const double p = exp(score[t] - m);
+        l += p;
+        const int32_t page = page_row[t / P];
+        if (page < 0 || page >= num_pages)
+            continue;
+        const int64_t cell = ((int64_t)page * Hkv + h) * P + t % P;
+        const double sc = kvrq_oracle_f16_to_f32(v_params[cell * 2 + 0]);
+        const double zr = kvrq_oracle_f16_to_f32(v_params[cell * 2 + 1]);
+        const uint8_t *c = v_codes + cell * (D / 2);
+        for (int d = 0; d < D; ++d) {
+            const int code = (d & 1) ? (c[d / 2] >> 4) : (c[d / 2] & 15);
+            acc[d] += p * (code * sc + zr);
+        }
+    }
+    free(score);
+    for (int d = 0; d < D; ++d)
+        acc[d] /= l;
+    kvrq_oracle_rotate_f64(acc, o, D, v_block);
+    return bad;
+}
+
 /* Attention of S sequences x Hq query heads over the de-quantised cache.
  *   q           bf16 bits [S][Hq][D]
  *   page_table  int32 [S][max_pages]
@@ -322,65 +395,55 @@ ORACLE_API int kvrq_oracle_decode(int S, int Hq, int Hkv, int D, int P, int num_
     for (int64_t sg = 0; sg < (int64_t)S * Hq; ++sg) {
         const int s = (int)(sg / Hq);
         const int g = (int)(sg % Hq);
-        const int h = g / G;
-        const int L = seq_lens[s];
-        double *o = out + sg * D;
-        double qx[1024], qr[1024], acc[1024], kh[1024];
-        for (int d = 0; d < D; ++d)
-            acc[d] = 0.0;
-        if (L <= 0) {
-            for (int d = 0; d < D; ++d)
-                o[d] = 0.0;
-            continue;
-        }
-        for (int d = 0; d < D; ++d)
-            qx[d] = (double)kvrq_oracle_bf16_to_f32(q[sg * D + d]);
-        kvrq_oracle_rotate_f64(qx, qr, D, k_block);
+        bad |= attend_row(q + sg * D, seq_lens[s], page_table + (int64_t)s * max_pages, g / G,
+                          Hkv, D, P, num_pages, k_block, v_block, sm_scale, k_codes, v_codes,
+                          k_params, v_params, out + sg * D);
+    }
+    return bad ? 2 : 0;
+}
 
-        double *score = (double *)malloc(sizeof(double) * (size_t)L);
-        double m = -INFINITY;
-        for (int t = 0; t < L; ++t) {
-            const int32_t page = page_table[(int64_t)s * max_pages + t / P];
-            if (page < 0 || page >= num_pages) {
-                bad = 1;
-                score[t] = -INFINITY;
-                continue;
-            }
-            const int64_t cell = ((int64_t)page * Hkv + h) * P + t % P;
-            const double sc = kvrq_oracle_f16_to_f32(k_params[cell * 2 + 0]);
-            const double zr = kvrq_oracle_f16_to_f32(k_params[cell * 2 + 1]);
-            const uint8_t *c = k_codes + cell * (D / 2);
-            for (int d = 0; d < D; ++d) {
-                const int code = (d & 1) ? (c[d / 2] >> 4) : (c[d / 2] & 15);
-                kh[d] = code * sc + zr;
-            }
-            double dot = 0.0;
-            for (int d = 0; d < D; ++d)
-                dot += qr[d] * kh[d];
-            score[t] = sm_scale * dot;
-            if (score[t] > m)
-                m = score[t];
-        }
-        double l = 0.0;
-        for (int t = 0; t < L; ++t) {
-            const double p = exp(score[t] - m);
-            l += p;
-            const int32_t page = page_table[(int64_t)s * max_pages + t / P];
-            if (page < 0 || page >= num_pages)
-                continue;
-            const int64_t cell = ((int64_t)page * Hkv + h) * P + t % P;
-            const double sc = kvrq_oracle_f16_to_f32(v_params[cell * 2 + 0]);
-            const double zr = kvrq_oracle_f16_to_f32(v_params[cell * 2 + 1]);
-            const uint8_t *c = v_codes + cell * (D / 2);
-            for (int d = 0; d < D; ++d) {
-                const int code = (d & 1) ? (c[d / 2] >> 4) : (c[d / 2] & 15);
-                acc[d] += p * (code * sc + zr);
-            }
-        }
-        free(score);
-        for (int d = 0; d < D; ++d)
-            acc[d] /= l;
-        kvrq_oracle_rotate_f64(acc, o, D, v_block);
+/* Extend (chunked prefill) attention over the paged cache: sequence s holds seq_lens[s]
+ * tokens, the last n_s = qo_start[s + 1] - qo_start[s] of which are the new chunk with
+ * one query row each.  Row i of the chunk sits at position p = seq_lens[s] - n_s + i and
+ * attends causally over tokens 0..p, i.e. it is the decode of a sequence of p + 1
+ * tokens.
+ *   q           bf16 bits [total_q][Hq][D], total_q = qo_start[S]
+ *   qo_start    int32 [S + 1], non-decreasing, qo_start[0] = 0
+ *   out         fp64 [total_q][Hq][D]
+ * Returns 0, 1 for bad shapes (including n_s > seq_lens[s]), 2 for a page id outside
+ * the pool. */
+ORACLE_API int kvrq_oracle_extend(int S, int Hq, int Hkv, int D, int P, int num_pages,
+                                  int k_block, int v_block, const uint16_t *q,
+                                  const int32_t *qo_start, const int32_t *page_table,
+                                  int max_pages, const int32_t *seq_lens, double sm_scale,
+                                  const uint8_t *k_codes, const uint8_t *v_codes,
+                                  const uint16_t *k_params, const uint16_t *v_params,
+                                  double *out)
+{
+    if (Hkv <= 0 || Hq % Hkv || D > 1024 || qo_start[0] != 0)
+        return 1;
+    for (int s = 0; s < S; ++s) {
+        const int n = qo_start[s + 1] - qo_start[s];
+        if (n < 0 || n > seq_lens[s])
+            return 1;
+    }
+    const int G = Hq / Hkv;
+    if (sm_scale <= 0.0)
+        sm_scale = 1.0 / sqrt((double)D);
+    const int64_t total_q = qo_start[S];
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t rg = 0; rg < total_q * Hq; ++rg) {
+        const int64_t r = rg / Hq;
+        const int g = (int)(rg % Hq);
+        int s = 0;
+        while (qo_start[s + 1] <= r)
+            ++s;
+        const int n = qo_start[s + 1] - qo_start[s];
+        const int len = seq_lens[s] - n + (int)(r - qo_start[s]) + 1;
+        bad |= attend_row(q + rg * D, len, page_table + (int64_t)s * max_pages, g / G, Hkv, D, P,
+                          num_pages, k_block, v_block, sm_scale, k_codes, v_codes, k_params,
+                          v_params, out + rg * D);
     }
     return bad ? 2 : 0;
 }
