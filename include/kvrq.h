@@ -19,6 +19,8 @@
  *                         product equals the original one), INT4 pages are
  *                         de-quantised on the fly, the V rotation is undone on
  *                         the output;
+ *   kv_int4_paged_extend  causal attention of a chunk of new query tokens
+ *                         over the same cache (chunked prefill);
  *   kvrq_pool_*           a host page allocator and page table for the fixed-
  *                         size pages the pages insist on (wispaper.ai blog,
  *                         section 1: PagedAttention needs uniform pages).
@@ -206,6 +208,43 @@ KVRQ_API kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_c
                                  const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
                                  int32_t split_tokens, float *out, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* Workspace bytes kv_int4_paged_extend needs (arguments as in that call;
+ * split_tokens 0 = automatic). */
+KVRQ_API kvrq_status kv_int4_paged_extend_workspace(const kvrq_cache_desc *d, int32_t num_seqs,
+                                                    int32_t num_q_heads, int32_t total_q,
+                                                    int32_t max_q_len, int32_t max_seq_len,
+                                                    int32_t split_tokens, size_t *bytes);
+
+/* Paged INT4 extend (chunked prefill) attention: several new query tokens per
+ * sequence, causal, over the same rotated INT4 cache -- the attention of the
+ * prefill side of a serving engine (fugumt.com abstract: fused attention
+ * execution over paged layouts).  The new tokens' K and V must already be in
+ * the cache (kv_rotquant_write first).
+ *   q               device bf16 [total_q][num_q_heads][head_dim], unrotated;
+ *                   rows qo_start[s] .. qo_start[s+1]-1 are the last
+ *                   n_s = qo_start[s+1] - qo_start[s] tokens of sequence s
+ *   qo_start        device int32 [num_seqs + 1]; qo_start[0] = 0,
+ *                   non-decreasing, qo_start[num_seqs] = total_q, every
+ *                   n_s <= max_q_len and n_s <= seq_lens[s] (preconditions on
+ *                   device data: violating rows get unspecified values, never
+ *                   an out-of-bounds access)
+ *   seq_lens        device int32 [num_seqs]: tokens in the cache, new ones
+ *                   included (clamped to max_seq_len)
+ *   max_q_len       host bound on every n_s (plans the grid); <= max_seq_len
+ *   other arguments as in kv_int4_paged_decode
+ *   out             device fp32 [total_q][num_q_heads][head_dim]
+ * Row i of sequence s sits at position p = seq_lens[s] - n_s + i and its
+ * output is the decode of the sequence's first p + 1 tokens with that row's
+ * query (tokens after p are masked).  Two launches on `stream`. */
+KVRQ_API kvrq_status kv_int4_paged_extend(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
+                                          const void *q, int32_t total_q, int32_t num_seqs,
+                                          int32_t num_q_heads, const int32_t *qo_start,
+                                          const int32_t *page_table, int32_t max_pages_per_seq,
+                                          const int32_t *seq_lens, int32_t max_seq_len,
+                                          int32_t max_q_len, float sm_scale, int32_t split_tokens,
+                                          float *out, void *workspace, size_t workspace_bytes,
+                                          void *stream);
 
 /* ------------------------------------------------------------------------
  * Measurement helpers (same conventions)

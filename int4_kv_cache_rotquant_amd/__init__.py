@@ -21,6 +21,8 @@ from ._binding import (  # noqa: F401
     Pool,
     kv_int4_paged_decode,
     kv_int4_paged_decode_workspace,
+    kv_int4_paged_extend,
+    kv_int4_paged_extend_workspace,
     kv_rotquant_write,
     kvrq_bf16_paged_write,
     kvrq_cache_sizes,

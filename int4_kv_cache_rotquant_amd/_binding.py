@@ -46,6 +46,13 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m int4_kv_cache_rotquant_amd.build` (there is no fallback)")
+    # torch carries its own HIP runtime under the soname the library links against; load
+    # torch first so that the library binds to that one copy (a second copy loaded before
+    # torch would not see the device memory torch allocates)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     st = ctypes.c_int32
@@ -65,6 +72,9 @@ def lib() -> ctypes.CDLL:
         "kv_int4_paged_decode_workspace": (st, [P, i32, i32, i32, i32, P]),
         "kv_int4_paged_decode": (st, [P, P, P, i32, i32, P, i32, P, i32, ctypes.c_float, i32, P, P,
                                       sz, P]),
+        "kv_int4_paged_extend_workspace": (st, [P, i32, i32, i32, i32, i32, i32, P]),
+        "kv_int4_paged_extend": (st, [P, P, P, i32, i32, i32, P, P, i32, P, i32, i32, ctypes.c_float,
+                                      i32, P, P, sz, P]),
         "kvrq_bf16_paged_write": (st, [P, P, P, P, P, i64, i64, i64, P, P]),
         "kvrq_device_copy": (st, [P, P, sz, P]),
     }
@@ -184,6 +194,46 @@ def kv_int4_paged_decode(cache: PagedInt4Cache, q, page_table, seq_lens, max_seq
         ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(q), S, Hq, _ptr(page_table),
         int(page_table.shape[1]), _ptr(seq_lens), int(max_seq_len), float(sm_scale), int(split_tokens),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def kv_int4_paged_extend_workspace(cache: PagedInt4Cache, num_seqs: int, num_q_heads: int,
+                                   total_q: int, max_q_len: int, max_seq_len: int,
+                                   split_tokens: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().kv_int4_paged_extend_workspace(ctypes.byref(cache.desc), num_seqs, num_q_heads,
+                                                total_q, max_q_len, max_seq_len, split_tokens,
+                                                ctypes.byref(n)))
+    return n.value
+
+
+def kv_int4_paged_extend(cache: PagedInt4Cache, q, qo_start, page_table, seq_lens,
+                         max_seq_len: int, max_q_len: int, out=None, sm_scale: float = 0.0,
+                         split_tokens: int = 0, workspace=None, stream=None):
+    """Causal extend attention of bf16 ``q`` [total_q][Hq][128] (rows qo_start[s]..
+    qo_start[s+1]-1 = the last tokens of sequence s); returns fp32 ``out`` like ``q``."""
+    import torch
+    total_q, Hq, D = q.shape
+    S = seq_lens.shape[0]
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or D != HEAD_DIM:
+        raise ValueError("q must be contiguous bf16 [total_q][Hq][128]")
+    if qo_start.dtype != torch.int32 or qo_start.shape != (S + 1,):
+        raise ValueError("qo_start must be int32 [S+1]")
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.shape[0] != S:
+        raise ValueError("page_table must be contiguous int32 [S][max_pages]")
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32 [S]")
+    if out is None:
+        out = torch.empty((total_q, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = kv_int4_paged_extend_workspace(cache, S, Hq, total_q, max_q_len, max_seq_len,
+                                           split_tokens)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().kv_int4_paged_extend(
+        ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(q), total_q, S, Hq,
+        _ptr(qo_start), _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens),
+        int(max_seq_len), int(max_q_len), float(sm_scale), int(split_tokens), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

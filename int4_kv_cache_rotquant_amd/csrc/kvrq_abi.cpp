@@ -163,6 +163,53 @@ kvrq_status check_decode_shape(const kvrq_cache_desc *d, int32_t num_seqs, int32
     return KVRQ_OK;
 }
 
+// Extend: query rows per workgroup, so that a wave's 16 MFMA columns hold whole rows.
+int32_t extend_rows_per_block(int32_t group)
+{
+    return std::max<int32_t>(1, kvrq::kMaxGroup / group);
+}
+
+kvrq_status check_extend_shape(const kvrq_cache_desc *d, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
+                               int32_t split_tokens)
+{
+    kvrq_status st = check_decode_shape(d, num_seqs, num_q_heads, max_seq_len, split_tokens);
+    if (st)
+        return st;
+    if (total_q < 0 || max_q_len < 0)
+        return fail(KVRQ_EINVAL, "total_q and max_q_len must be >= 0");
+    if (total_q > 0 && max_q_len < 1)
+        return fail(KVRQ_EINVAL, "max_q_len must be >= 1 when there are query rows");
+    if (max_q_len > max_seq_len)
+        return fail(KVRQ_EINVAL, "max_q_len %d exceeds max_seq_len %d", max_q_len, max_seq_len);
+    const int64_t r = extend_rows_per_block(num_q_heads / d->num_kv_heads);
+    if (int64_t(num_seqs) * ((max_q_len + r - 1) / r) > 0x7fffffff)
+        return fail(KVRQ_EUNSUPPORTED, "too many query row blocks");
+    return KVRQ_OK;
+}
+
+// Extend: split the key range only when the (row block, KV head) workgroups alone are too
+// few to fill the chip; at least 512 tokens per split.
+kvrq::DecodePlan plan_extend(int32_t num_seqs, int32_t num_kv_heads, int32_t group,
+                             int32_t max_q_len, int32_t max_seq_len, int32_t split_tokens)
+{
+    kvrq::DecodePlan p;
+    const int64_t step = int64_t(kvrq::kTile) * kvrq::kDecodeWaves;
+    if (split_tokens <= 0) {
+        const int64_t r = extend_rows_per_block(group);
+        const int64_t blocks = std::max<int64_t>(1, int64_t(num_seqs) * ((max_q_len + r - 1) / r) *
+                                                        num_kv_heads);
+        int64_t splits = (4096 + blocks - 1) / blocks;
+        splits = std::max<int64_t>(1, std::min<int64_t>(splits, (max_seq_len + 511) / 512));
+        int64_t st = (std::max<int64_t>(max_seq_len, 1) + splits - 1) / splits;
+        st = (st + step - 1) / step * step;
+        split_tokens = (int32_t)std::min<int64_t>(st, int64_t(1) << 30);
+    }
+    p.split_tokens = split_tokens;
+    p.max_splits = std::max<int32_t>(1, (max_seq_len + split_tokens - 1) / split_tokens);
+    return p;
+}
+
 }  // namespace
 
 // --------------------------------------------------------------------------
@@ -452,7 +499,100 @@ kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buff
     a.max_splits = plan.max_splits;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(d->head_dim));
     a.q_scale = scale * 1.4426950408889634f;
+    a.qo_start = nullptr;
+    a.num_rows = num_seqs;
+    a.rows_per_block = 1;
+    a.blocks_per_seq = 1;
     return hip_status(kvrq::launch_decode(d->k_block, d->v_block, a, stream), "kv_int4_paged_decode");
+}
+
+KVRQ_API kvrq_status kv_int4_paged_extend_workspace(const kvrq_cache_desc *d, int32_t num_seqs,
+                                                    int32_t num_q_heads, int32_t total_q,
+                                                    int32_t max_q_len, int32_t max_seq_len,
+                                                    int32_t split_tokens, size_t *bytes)
+{
+    kvrq_status st = check_extend_shape(d, num_seqs, num_q_heads, total_q, max_q_len, max_seq_len,
+                                        split_tokens);
+    if (st)
+        return st;
+    if (!bytes)
+        return fail(KVRQ_EINVAL, "bytes is NULL");
+    const kvrq::DecodePlan plan = plan_extend(num_seqs, d->num_kv_heads, num_q_heads / d->num_kv_heads,
+                                              max_q_len, max_seq_len, split_tokens);
+    *bytes = decode_workspace_bytes(total_q, num_q_heads, plan);
+    return KVRQ_OK;
+}
+
+KVRQ_API kvrq_status kv_int4_paged_extend(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
+                                          const void *q, int32_t total_q, int32_t num_seqs,
+                                          int32_t num_q_heads, const int32_t *qo_start,
+                                          const int32_t *page_table, int32_t max_pages_per_seq,
+                                          const int32_t *seq_lens, int32_t max_seq_len,
+                                          int32_t max_q_len, float sm_scale, int32_t split_tokens,
+                                          float *out, void *workspace, size_t workspace_bytes,
+                                          void *stream)
+{
+    kvrq_status st = check_extend_shape(d, num_seqs, num_q_heads, total_q, max_q_len, max_seq_len,
+                                        split_tokens);
+    if (st)
+        return st;
+    st = check_buffers(b);
+    if (st)
+        return st;
+    if (num_seqs == 0 || total_q == 0)
+        return KVRQ_OK;
+    if (!q || !qo_start || !page_table || !seq_lens || !out)
+        return fail(KVRQ_EINVAL, "q, qo_start, page_table, seq_lens and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4) ||
+        !aligned(qo_start, 4))
+        return fail(KVRQ_EINVAL, "q and out must be 16-byte aligned, the int32 arrays 4-byte");
+    if (max_pages_per_seq < 1)
+        return fail(KVRQ_EINVAL, "max_pages_per_seq must be >= 1");
+    if (int64_t(max_pages_per_seq) * d->page_size < max_seq_len)
+        return fail(KVRQ_EINVAL, "max_seq_len %d exceeds max_pages_per_seq*page_size", max_seq_len);
+    if (!std::isfinite(sm_scale))
+        return fail(KVRQ_EINVAL, "sm_scale must be finite");
+    const int32_t group = num_q_heads / d->num_kv_heads;
+    const kvrq::DecodePlan plan = plan_extend(num_seqs, d->num_kv_heads, group, max_q_len,
+                                              max_seq_len, split_tokens);
+    const size_t need = decode_workspace_bytes(total_q, num_q_heads, plan);
+    if (!workspace || workspace_bytes < need)
+        return fail(KVRQ_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : size_t(0));
+    if (!aligned(workspace, 16))
+        return fail(KVRQ_EINVAL, "workspace must be 16-byte aligned");
+    if (plan.max_splits > 65535)
+        return fail(KVRQ_EUNSUPPORTED, "too many splits");
+
+    kvrq::DecodeArgs a;
+    a.k_codes = b->k_codes;
+    a.v_codes = b->v_codes;
+    a.k_params = reinterpret_cast<const uint32_t *>(b->k_params);
+    a.v_params = reinterpret_cast<const uint32_t *>(b->v_params);
+    a.q = static_cast<const uint16_t *>(q);
+    a.page_table = page_table;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    const size_t rows = size_t(total_q) * num_q_heads * plan.max_splits;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = a.part_o + rows * kvrq::kHeadDim;
+    a.num_seqs = num_seqs;
+    a.num_pages = d->num_pages;
+    a.max_seq_len = max_seq_len;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = d->num_kv_heads;
+    a.group = group;
+    a.page_log2 = log2_exact(d->page_size);
+    a.max_pages = max_pages_per_seq;
+    a.split_tokens = plan.split_tokens;
+    a.max_splits = plan.max_splits;
+    const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(d->head_dim));
+    a.q_scale = scale * 1.4426950408889634f;
+    a.qo_start = qo_start;
+    a.num_rows = total_q;
+    a.rows_per_block = extend_rows_per_block(group);
+    a.blocks_per_seq = (max_q_len + a.rows_per_block - 1) / a.rows_per_block;
+    return hip_status(kvrq::launch_decode(d->k_block, d->v_block, a, stream), "kv_int4_paged_extend");
 }
 
 kvrq_status kvrq_bf16_paged_write(const kvrq_cache_desc *d, void *k_cache, void *v_cache, const void *k,

@@ -299,9 +299,10 @@ struct WaveState {
             recentre();
     }
 
-    template <int F>
+    template <int F, bool EXT>
     __device__ __forceinline__ void consume(const Tile &T, int t0, int t_end, int lane, float kscale,
-                                            const QOperand<F> &qop, ParLds &pl)
+                                            const QOperand<F> &qop, ParLds &pl, int col_len,
+                                            int mask_from)
     {
         constexpr int NS = 8 / F;            // scores per lane
         const int n16 = lane & 15, kq = lane >> 4;
@@ -374,6 +375,15 @@ struct WaveState {
 #pragma unroll
         for (int i = 0; i < NS; ++i)
             sc[i] = fmaf(sc[i], sk[i], fmaf(zk[i], qsum, bk[i]));
+        if constexpr (EXT) {
+            // causal: token t is visible to the lane's column only if t < col_len
+            if (t0 + kTile > mask_from) {
+                const int kq4 = 4 * (lane >> 4);
+#pragma unroll
+                for (int i = 0; i < NS; ++i)
+                    sc[i] = t0 + 16 * (i >> 2) + kq4 + (i & 3) < col_len ? sc[i] : -INFINITY;
+            }
+        }
 
         // ---- a9: online softmax (base 2), lazy maximum ------------------------------------
         // Most tiles change nothing: the maximum moves only when a score exceeds it by more
@@ -432,14 +442,20 @@ struct WaveState {
         z = fmaf(pz, uE, z);
         wsum += ws;
         wpend += ws;
-        // B operand of PV, f16 high and low parts, both rounded to nearest (an unbiased
-        // split: the removed constant part of the V operands then adds no drift):
+        // B operand of PV, f16 high and low parts: the high part is w cut to the 11
+        // significant bits of an f16 (exact to convert for the weights here, all below
+        // 2^14), the low part the exact fp32 remainder rounded to nearest (an unbiased
+        // split: the removed constant part of the V operands then adds no drift).  The high
+        // part comes from the bits of w, never from a rounding, so no rewrite of the
+        // product p * scale by the compiler can make the two parts disagree by an ulp.
         // k slot e of lane (n16, kq) is token 16 (e / 4) + 4 kq + e % 4
         uint32_t hp[NS / 2], lp[NS / 2];
 #pragma unroll
         for (int j = 0; j < NS / 2; ++j) {
-            const f16x2 h = {(_Float16)w[2 * j], (_Float16)w[2 * j + 1]};
-            const f16x2 r = {(_Float16)(w[2 * j] - (float)h[0]), (_Float16)(w[2 * j + 1] - (float)h[1])};
+            const float h0 = __uint_as_float(__float_as_uint(w[2 * j]) & 0xFFFFE000u);
+            const float h1 = __uint_as_float(__float_as_uint(w[2 * j + 1]) & 0xFFFFE000u);
+            const f16x2 h = {(_Float16)h0, (_Float16)h1};
+            const f16x2 r = {(_Float16)(w[2 * j] - h0), (_Float16)(w[2 * j + 1] - h1)};
             hp[j] = __builtin_bit_cast(uint32_t, h);
             lp[j] = __builtin_bit_cast(uint32_t, r);
         }
@@ -478,14 +494,37 @@ struct WaveState {
     }
 };
 
-template <int BK, int F>
+template <int BK, int F, bool EXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? 4 : 2)))
 void decode_split_kernel(DecodeArgs a)
 {
-    const int split = blockIdx.x;
+    static_assert(!EXT || F == 1, "extend columns use the 16-column layout");
     const int h = blockIdx.y;
-    const int s = blockIdx.z;
-    const int L = min(a.seq_lens[s], a.max_seq_len);
+    const int G = a.group;
+    // The MFMA columns: decode: the G query heads of sequence s (grid: split, KV head,
+    // sequence); extend: query rows row0 .. row0 + nrows - 1 of sequence s, G heads each
+    // (grid: row block, KV head, split), row i of the chunk attending over tokens 0..pos.
+    int s, L, ncols, split;
+    int64_t row0 = 0;      // extend: first query row of this workgroup
+    int pos0 = 0;          // extend: the position of that row in its sequence
+    if constexpr (EXT) {
+        split = blockIdx.z;
+        s = blockIdx.x / a.blocks_per_seq;
+        const int lb = blockIdx.x - s * a.blocks_per_seq;
+        const int q0 = a.qo_start[s], n = a.qo_start[s + 1] - q0;
+        if (lb * a.rows_per_block >= n)
+            return;
+        const int nrows = min(a.rows_per_block, n - lb * a.rows_per_block);
+        row0 = q0 + lb * a.rows_per_block;
+        pos0 = min(a.seq_lens[s], a.max_seq_len) - n + lb * a.rows_per_block;
+        L = pos0 + nrows;
+        ncols = nrows * G;
+    } else {
+        split = blockIdx.x;
+        s = blockIdx.z;
+        L = min(a.seq_lens[s], a.max_seq_len);
+        ncols = G;
+    }
     const int wg_begin = split * a.split_tokens;
     if (wg_begin >= L)
         return;
@@ -494,7 +533,6 @@ void decode_split_kernel(DecodeArgs a)
     // the wave index, and with it the token range, is uniform across the wave: keep it
     // scalar so the page-table lookups and the loop control stay on the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G = a.group;
     const int wave_tokens = a.split_tokens / kDecodeWaves;
     const int t_begin = wg_begin + wave * wave_tokens;
     const int t_end = min(L, t_begin + wave_tokens);
@@ -516,9 +554,10 @@ void decode_split_kernel(DecodeArgs a)
     if (wave == 0) {
         const int g = lane >> 2, ql = lane & 3;
         float x[32];
-        if (g < G) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(
-                a.q + ((int64_t)s * a.num_q_heads + h * G + g) * kHeadDim + 32 * ql);
+        if (g < ncols) {
+            const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
+                                     : (int64_t)s * a.num_q_heads + h * G + g;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + qrow * kHeadDim + 32 * ql);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const u32x4 w = src[j];
@@ -567,7 +606,7 @@ void decode_split_kernel(DecodeArgs a)
         const int n = ln & 15, q4 = ln >> 4;
         const int par = slot & 1, jj = slot >> 1;
         const int g = F == 2 ? (n & 7) : n;
-        const bool live = g < G && (F == 1 || (n >> 3) == (q4 >> 1));
+        const bool live = g < ncols && (F == 1 || (n >> 3) == (q4 >> 1));
         const int ch0 = F == 2 ? 64 * (q4 & 1) + 32 * jj + par : 32 * q4 + par;
         uint32_t dig[3][4];
 #pragma unroll
@@ -594,7 +633,11 @@ void decode_split_kernel(DecodeArgs a)
     }
     const int n16 = lane & 15;
     const int kq = lane >> 4;
-    const int gl = F == 2 ? (n16 & 7) : n16;   // this lane's query head
+    const int gl = F == 2 ? (n16 & 7) : n16;   // this lane's column (query head)
+    // extend: the lane's column sees tokens 0 .. col_len - 1; tiles that reach past the
+    // first row's position mask per column
+    const int col_len = EXT ? (gl < ncols ? pos0 + gl / G + 1 : 0) : 0;
+    const int mask_from = pos0 + 1;
     WaveState st;
     st.qsum = lds_qsum[gl];
     // K lanes scale by 2^-f (the integer query's grid), V lanes by 1
@@ -634,13 +677,13 @@ void decode_split_kernel(DecodeArgs a)
         load_tile<F>(B, a, pid, h, min(cb + kTile, t_last), ce, lane);
         int t0 = cb;
         while (true) {
-            st.template consume<F>(A, t0, ce, lane, kscale, qop, pl);
+            st.template consume<F, EXT>(A, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
             st.tick();
             if (t0 + kTile >= ce)
                 break;
             load_tile<F>(A, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
             t0 += kTile;
-            st.template consume<F>(B, t0, ce, lane, kscale, qop, pl);
+            st.template consume<F, EXT>(B, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
             st.tick();
             if (t0 + kTile >= ce)
                 break;
@@ -678,7 +721,7 @@ void decode_split_kernel(DecodeArgs a)
             for (int r = 0; r < 4; ++r)
                 o[b][r] = o[b][r] * fa + dpp_row_ror8(o[b][r]) * fb;
     }
-    if (n16 < kSlots && gl < G) {
+    if (n16 < kSlots && gl < ncols) {
 #pragma unroll
         for (int b = 0; b < 8; ++b)
 #pragma unroll
@@ -690,7 +733,7 @@ void decode_split_kernel(DecodeArgs a)
         }
     }
     __syncthreads();
-    for (int i = tid; i < G * kHeadDim; i += 64 * kDecodeWaves) {
+    for (int i = tid; i < ncols * kHeadDim; i += 64 * kDecodeWaves) {
         const int g = i >> 7, d = i & (kHeadDim - 1);
         float M = lds_m[0][g];
 #pragma unroll
@@ -703,13 +746,34 @@ void decode_split_kernel(DecodeArgs a)
             acc += f * lds_o[w][g][d];
             lsum += f * lds_l[w][g];
         }
-        const int64_t row = ((int64_t)s * a.num_q_heads + h * G + g) * a.max_splits + split;
+        const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
+                                 : (int64_t)s * a.num_q_heads + h * G + g;
+        const int64_t row = qrow * a.max_splits + split;
         a.part_o[row * kHeadDim + d] = acc;
         if (d == 0) {
             a.part_ml[2 * row] = M;
             a.part_ml[2 * row + 1] = lsum;
         }
     }
+}
+
+// Tokens attended by output row r of the combine: the sequence length (decode) or the
+// causal length of query row r (extend: the sequence holding r by binary search over
+// qo_start, then its position + 1).
+__device__ __forceinline__ int row_length(const DecodeArgs &a, int r)
+{
+    if (a.qo_start == nullptr)
+        return min(a.seq_lens[r], a.max_seq_len);
+    int lo = 0, hi = a.num_seqs;   // qo_start[lo] <= r < qo_start[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.qo_start[mid] <= r)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    const int n = a.qo_start[lo + 1] - a.qo_start[lo];
+    return min(a.seq_lens[lo], a.max_seq_len) - n + (r - a.qo_start[lo]) + 1;
 }
 
 // Inverse V rotation of one output row held as channels (2 lane, 2 lane + 1) by the
@@ -738,12 +802,12 @@ __device__ __forceinline__ void inverse_rotate_pair(float &o0, float &o1, int la
 template <int BV>
 __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a)
 {
-    // one workgroup of 16 waves per (query head, sequence), for many splits
-    const int g = blockIdx.x;
-    const int s = blockIdx.y;
+    // one workgroup of 16 waves per (output row, query head), for many splits
+    const int s = blockIdx.x;
+    const int g = blockIdx.y;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
-    const int L = min(a.seq_lens[s], a.max_seq_len);
+    const int L = row_length(a, s);
     float *out = a.out + ((int64_t)s * a.num_q_heads + g) * kHeadDim;
     if (L <= 0) {
         if (tid < kHeadDim)
@@ -821,11 +885,11 @@ template <int BV>
 __global__ __launch_bounds__(256) void decode_combine_wave_kernel(DecodeArgs a)
 {
     const int lane = threadIdx.x & 63;
-    const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int s = blockIdx.y;
+    const int s = blockIdx.x;
+    const int g = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (g >= a.num_q_heads)
         return;
-    const int L = min(a.seq_lens[s], a.max_seq_len);
+    const int L = row_length(a, s);
     float *out = a.out + ((int64_t)s * a.num_q_heads + g) * kHeadDim;
     if (L <= 0) {
         *reinterpret_cast<float2 *>(out + 2 * lane) = make_float2(0.0f, 0.0f);
@@ -879,11 +943,17 @@ __global__ __launch_bounds__(256) void decode_combine_wave_kernel(DecodeArgs a)
 template <int BK>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
 {
+    if (a.qo_start != nullptr) {
+        const dim3 grid((unsigned)(a.num_seqs * a.blocks_per_seq), (unsigned)a.num_kv_heads,
+                        (unsigned)a.max_splits);
+        hipLaunchKernelGGL((decode_split_kernel<BK, 1, true>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
     if (a.group <= 8)
-        hipLaunchKernelGGL((decode_split_kernel<BK, 2>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+        hipLaunchKernelGGL((decode_split_kernel<BK, 2, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_split_kernel<BK, 1>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+        hipLaunchKernelGGL((decode_split_kernel<BK, 1, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
     return hipGetLastError();
 }
 
@@ -891,10 +961,10 @@ template <int BV>
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t s)
 {
     if (a.max_splits <= 64) {
-        const dim3 grid((unsigned)((a.num_q_heads + 3) / 4), (unsigned)a.num_seqs);
+        const dim3 grid((unsigned)a.num_rows, (unsigned)((a.num_q_heads + 3) / 4));
         hipLaunchKernelGGL(decode_combine_wave_kernel<BV>, grid, dim3(256), 0, s, a);
     } else {
-        const dim3 grid((unsigned)a.num_q_heads, (unsigned)a.num_seqs);
+        const dim3 grid((unsigned)a.num_rows, (unsigned)a.num_q_heads);
         hipLaunchKernelGGL(decode_combine_kernel<BV>, grid, dim3(1024), 0, s, a);
     }
     return hipGetLastError();
@@ -904,7 +974,7 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t s)
 
 int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream)
 {
-    if (a.num_seqs == 0)
+    if (a.num_seqs == 0 || a.num_rows == 0)
         return 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;

@@ -74,12 +74,19 @@ struct DecodeArgs {
     int32_t split_tokens;
     int32_t max_splits;
     float q_scale;              // sm_scale * log2(e)
+    // extend (chunked prefill) only; qo_start == nullptr for the decode.  The output
+    // rows are then query rows: q, out [total_q][Hq][128], part_* [total_q][Hq][splits]
+    const int32_t *qo_start;    // [S + 1] first query row of each sequence
+    int32_t num_rows;           // rows of the combine: S (decode) or total_q (extend)
+    int32_t rows_per_block;     // query rows per workgroup (16 / group, at least 1)
+    int32_t blocks_per_seq;     // ceil(max_q_len / rows_per_block)
 };
 
 // Returns a hipError_t value (0 = success).
 int launch_rotquant_write(int k_block, int v_block, const WriteArgs &a, void *stream);
 int launch_bf16_paged_write(const CopyArgs &a, void *stream);
 int launch_device_copy(void *dst, const void *src, size_t bytes, void *stream);
+// decode, or extend when a.qo_start is set
 int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream);
 const char *hip_error_string(int err);
 

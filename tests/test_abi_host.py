@@ -131,6 +131,41 @@ def test_decode_validation(K):
     assert dec(wsp=0) == K.KVRQ_EWORKSPACE
 
 
+def test_extend_validation(K):
+    L = K.lib()
+    size = ctypes.c_size_t()
+
+    def ws(desc=None, S=4, Hq=64, total_q=40, max_q=16, maxlen=1000, split=0):
+        desc = desc or _desc(K)
+        return L.kv_int4_paged_extend_workspace(ctypes.byref(desc), S, Hq, total_q, max_q, maxlen,
+                                                split, ctypes.byref(size))
+
+    assert ws() == K.KVRQ_OK and size.value > 0
+    base = size.value
+    assert ws(total_q=80) == K.KVRQ_OK and size.value == 2 * base   # per query row and head
+    assert ws(Hq=60) == K.KVRQ_EINVAL
+    assert ws(total_q=-1) == K.KVRQ_EINVAL
+    assert ws(max_q=0) == K.KVRQ_EINVAL                 # rows but no row per sequence
+    assert ws(total_q=0, max_q=0) == K.KVRQ_OK
+    assert ws(max_q=1001) == K.KVRQ_EINVAL              # a chunk longer than the sequence
+    assert "max_q_len" in K.last_error()
+    assert ws(split=48) == K.KVRQ_EINVAL
+
+    def ext(q=0x1000, total_q=40, S=4, Hq=64, qo=0x6000, tab=0x2000, maxp=100, lens=0x3000,
+            maxlen=1000, max_q=16, scale=0.0, split=0, out=0x4000, wsp=0x5000, wsb=1 << 30):
+        return L.kv_int4_paged_extend(ctypes.byref(_desc(K)), ctypes.byref(_bufs(K)), q, total_q, S,
+                                      Hq, qo, tab, maxp, lens, maxlen, max_q, scale, split, out, wsp,
+                                      wsb, None)
+
+    assert ext(S=0) == K.KVRQ_OK and ext(total_q=0) == K.KVRQ_OK   # nothing to launch
+    assert ext(qo=0) == K.KVRQ_EINVAL
+    assert ext(qo=0x6002) == K.KVRQ_EINVAL
+    assert ext(out=0x4004) == K.KVRQ_EINVAL
+    assert ext(maxp=10) == K.KVRQ_EINVAL
+    assert ext(scale=float("inf")) == K.KVRQ_EINVAL
+    assert ext(wsb=16) == K.KVRQ_EWORKSPACE
+
+
 def test_helper_validation(K):
     L = K.lib()
     assert L.kvrq_device_copy(0x1000, 0x2000, 0, None) == K.KVRQ_OK
