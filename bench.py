@@ -46,6 +46,8 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+# attention at MFMA peak: half the flops on int8 (5.0 POP/s dense), half on f16 (2.5 PFLOP/s)
+MFMA_ATTENTION_PEAK_TFLOPS = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
 D = 128
 CODE_ROW = 64 + 4            # bytes per (token, head) row in the INT4 cache
 
@@ -334,6 +336,58 @@ class Setup:
                                out=self.out, split_tokens=self.args.split_tokens, workspace=self.ws)
         ev[2].record()
 
+    # -- chunked prefill: prefixes written untimed; a step writes every sequence's chunk and
+    #    runs the causal extend of the chunk rows over prefix + chunk
+    def setup_chunked_prefill(self):
+        K, torch, w = self.K, self.torch, self.w
+        kb = self.args.k_block if self.args.k_block is not None else w.k_block
+        self.kb, self.vb = kb, w.v_block
+        S, Hkv, Hq, P = w.num_seqs, w.num_kv_heads, w.num_q_heads, w.page_size
+        C, prefix = w.notes["chunk"], w.notes["prefix"]
+        self.cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, kb, w.v_block)
+        pre = np.concatenate([w.paging.slots(s, 0, int(L)) for s, L in enumerate(prefix)])
+        for s0 in range(0, len(pre), 1 << 16):
+            sl = pre[s0:s0 + (1 << 16)]
+            K.kv_rotquant_write(self.cache, self.rows(len(sl), Hkv, w.k_out),
+                                self.rows(len(sl), Hkv, w.v_out), self.dev_i32(sl))
+        T = S * C
+        self.sets = [(self.rows(T, Hkv, w.k_out), self.rows(T, Hkv, w.v_out),
+                      torch.randn((T, Hq, D), generator=self.gen, device=self.dev).to(torch.bfloat16))
+                     for _ in range(2)]
+        self.slots = self.dev_i32(np.concatenate([w.paging.slots(s, int(L), C)
+                                                  for s, L in enumerate(prefix)]))
+        self.qo = self.dev_i32(np.arange(S + 1) * C)
+        self.tab = self.dev_i32(w.paging.page_table())
+        self.lens = self.dev_i32(w.seq_lens)
+        self.maxlen = int(w.seq_lens.max())
+        self.out = torch.empty((T, Hq, D), dtype=torch.float32, device=self.dev)
+        n = K.kv_int4_paged_extend_workspace(self.cache, S, Hq, T, C, self.maxlen, self.args.split_tokens)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        # attended (row, key) pairs: row i of a chunk at position prefix + i sees prefix + i + 1
+        pairs = int(sum(C * int(L) + C * (C + 1) // 2 for L in prefix))
+        self.kernels = {"kv_rotquant_write": self.write_bytes(T, Hkv),
+                        "kv_int4_paged_extend": int(w.seq_lens.sum() * Hkv * 2 * CODE_ROW
+                                                    + T * Hq * (2 * D + 4 * D)
+                                                    + np.ceil(w.seq_lens / P).sum() * 4)}
+        # QK^T and PV: 2 D flops each per (row, head, key)
+        self.kernel_flops = {"kv_int4_paged_extend": pairs * Hq * 4 * D}
+        self.tokens_per_step = T
+        self.unit = "prefill tokens/s"
+        self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                       "num_seqs": S, "chunk": C, "prefix_tokens": int(prefix.sum()),
+                       "attended_pairs": pairs, "page_size": P, "k_block": kb, "v_block": w.v_block}
+
+    def step_chunked_prefill(self, i, ev):
+        K = self.K
+        k, v, q = self.sets[i % len(self.sets)]
+        C = self.w.notes["chunk"]
+        ev[0].record()
+        K.kv_rotquant_write(self.cache, k, v, self.slots)
+        ev[1].record()
+        K.kv_int4_paged_extend(self.cache, q, self.qo, self.tab, self.lens, self.maxlen, C,
+                               out=self.out, split_tokens=self.args.split_tokens, workspace=self.ws)
+        ev[2].record()
+
     # -- tiny
     def setup_tiny(self):
         K, torch, w = self.K, self.torch, self.w
@@ -376,6 +430,8 @@ def cpu_baseline(args):
     if args.workload == "prefill_chunk" and args.variant == "plain":
         kb = 0
     rng = w.rng(77)
+    if args.workload == "chunked_prefill":
+        return cpu_baseline_extend(args, w, kb, rng, cores)
     # sample: up to 8 sequences (long context: 65536 tokens) of the workload's own shapes
     if args.workload == "long_context":
         lens = np.array([65536])
@@ -405,6 +461,36 @@ def cpu_baseline(args):
     what = f"{reps} x (write {T} tokens" + (f" + decode {len(lens)} sequences)" if decode else ")")
     return {"value": tokens / t_total, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{what}, {args.workload} shapes, OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', cores)}",
+            "seconds": round(t_total, 3)}
+
+
+def cpu_baseline_extend(args, w, kb, rng, cores):
+    """Oracle write of a chunk + causal extend, on the workload's first sequence with a
+    256-token chunk (prefix as in the workload)."""
+    import oracle
+    C = 256
+    prefix = int(w.notes["prefix"][0])
+    L = prefix + C
+    paging = W.assign_pages(rng, [L], w.page_size)
+    k = W.make_rows(rng, L, w.num_kv_heads, w.k_out)
+    v = W.make_rows(rng, L, w.num_kv_heads, w.v_out)
+    slots = paging.slots(0, 0, L)
+    q = W.f32_to_bf16_bits(rng.standard_normal((C, w.num_q_heads, D)).astype(np.float32))
+    tab = paging.page_table()
+    qo = np.array([0, C], np.int32)
+    cache = oracle.Cache(paging.num_pages, w.num_kv_heads, w.page_size)
+    oracle.write(cache, k[:prefix], v[:prefix], slots[:prefix], kb, w.v_block)   # untimed prefix
+    reps, t_total = 0, 0.0
+    while t_total < args.cpu_seconds and reps < 1000:
+        t0 = time.perf_counter()
+        oracle.write(cache, k[prefix:], v[prefix:], slots[prefix:], kb, w.v_block)
+        oracle.extend(q, (cache.k_codes, cache.v_codes, cache.k_params, cache.v_params), qo, tab,
+                      np.array([L], np.int32), w.num_kv_heads, w.page_size, kb, w.v_block)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * C / t_total, "unit": "prefill tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x (write {C} tokens + extend {C} rows over {L} tokens), "
+                      f"chunked_prefill shapes, OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', cores)}",
             "seconds": round(t_total, 3)}
 
 
@@ -532,19 +618,36 @@ def main():
                             "algorithmic_bytes": s.kernels[name],
                             "algorithmic_gbps": round(s.kernels[name] / (mean_ms * 1e-3) / 1e9, 1),
                             "launches_per_step": launches}
+    flops = getattr(s, "kernel_flops", {})
+    for name, f in flops.items():
+        per_kernel[name]["algorithmic_flops"] = f
+        per_kernel[name]["algorithmic_tflops"] = round(f / (per_kernel[name]["mean_us"] * 1e-6) / 1e12, 1)
     dominant = max(names, key=lambda n: per_kernel[n]["mean_us"] * per_kernel[n]["launches_per_step"])
     dk = per_kernel[dominant]
-    achieved = dk["algorithmic_gbps"]
     symbol = {"kv_rotquant_write": "rotquant_write_kernel", "kv_int4_paged_decode": "decode_split_kernel",
+              "kv_int4_paged_extend": "decode_split_kernel",
               "kvrq_bf16_paged_write": "bf16_paged_write_kernel"}[dominant]
     traffic, traffic_note = traffic_from_counters(args.counters, symbol, copy_bytes)
+    if dominant in flops:
+        # dense attention: QK^T on int8 MFMA (5.0 POP/s), PV on f16 MFMA (2.5 PFLOP/s), half
+        # the flops each, so the time at peak is that of 3.33 PFLOP/s
+        achieved = dk["algorithmic_tflops"]
+        roofline = {"bound": "mfma", "kernel": dominant, "achieved": achieved,
+                    "peak": MFMA_ATTENTION_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_ATTENTION_PEAK_TFLOPS, 4),
+                    "traffic": None if traffic is None else round(traffic), "traffic_note": traffic_note}
+    else:
+        achieved = dk["algorithmic_gbps"]
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": None if traffic is None else round(traffic), "traffic_note": traffic_note}
 
     ms_per_step = elapsed / args.steps * 1e3
     value = s.tokens_per_step * args.steps / elapsed
     result = {
         "metric": "KV tokens/s and achieved HBM GB/s (% of peak) for rotquant write + INT4 decode",
         "value": round(value, 1),
-        "unit": "KV tokens/s",
+        "unit": getattr(s, "unit", "KV tokens/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -556,10 +659,7 @@ def main():
         "data": "synthetic (seeded N(0,1) with outlier channels; no model weights)",
         "config": s.config,
         "kernels": per_kernel,
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None if traffic is None else round(traffic),
-                     "traffic_note": traffic_note},
+        "roofline": roofline,
         "hbm_gbps_step": round(sum(per_kernel[n]["algorithmic_bytes"] * per_kernel[n]["launches_per_step"]
                                    for n in names) / (ms_per_step * 1e-3) / 1e9, 1),
         "copy_probe_gbps": None if copy_gbps is None else round(copy_gbps, 1),

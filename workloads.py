@@ -155,7 +155,7 @@ def lognormal_lengths(rng: np.random.Generator, n: int, median: float, sigma: fl
 
 
 # --------------------------------------------------------------------------
-# the five workloads
+# the workloads
 # --------------------------------------------------------------------------
 @dataclasses.dataclass
 class Workload:
@@ -255,10 +255,26 @@ def long_context() -> Workload:
                     k_out, v_out, seed, notes={"chunk": 16384})
 
 
+def chunked_prefill() -> Workload:
+    """Qwen3-4B-like heads (Hq=32, Hkv=8), 8 sequences with prefixes of U{1024..6144}
+    tokens already cached, each extended by a 1024-token chunk: the chunk is written, then
+    its rows attend causally over prefix + chunk.  Page 16 scattered; K block 64, V plain."""
+    seed = BASE_SEED + 5
+    rng = np.random.Generator(np.random.PCG64([seed, 0]))
+    chunk = 1024
+    prefix = rng.integers(1024, 6144, size=8, endpoint=True)
+    k_out = OutlierSpec.random(rng, 8)
+    lens = prefix + chunk
+    paging = assign_pages(rng, list(lens), 16)
+    return Workload("chunked_prefill", 8, 32, 16, 64, 0, lens, paging, k_out, OutlierSpec.none(8),
+                    seed, notes={"chunk": chunk, "prefix": prefix})
+
+
 WORKLOADS = {
     "tiny": tiny,
     "qwen3_4b_like": qwen3_4b_like,
     "prefill_chunk": prefill_chunk,
     "qwen3_32b_like_decode": qwen3_32b_like_decode,
     "long_context": long_context,
+    "chunked_prefill": chunked_prefill,
 }
