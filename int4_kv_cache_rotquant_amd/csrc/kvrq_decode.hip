@@ -533,9 +533,12 @@ void decode_split_kernel(DecodeArgs a)
     // the wave index, and with it the token range, is uniform across the wave: keep it
     // scalar so the page-table lookups and the loop control stay on the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wave_tokens = a.split_tokens / kDecodeWaves;
-    const int t_begin = wg_begin + wave * wave_tokens;
-    const int t_end = min(L, t_begin + wave_tokens);
+    // the waves share the split's tiles up to the row's length evenly (a split that the
+    // length cuts short still keeps all four waves busy)
+    const int wg_end = min(L, wg_begin + a.split_tokens);
+    const int n_tiles = (wg_end - wg_begin + kTile - 1) / kTile;
+    const int t_begin = wg_begin + (wave * n_tiles / kDecodeWaves) * kTile;
+    const int t_end = min(wg_end, wg_begin + ((wave + 1) * n_tiles / kDecodeWaves) * kTile);
 
     // rotated query rows in the prologue, the waves' partial states in the epilogue
     // (F = 2: the two halves of each column are merged inside the wave first, so one slot
