@@ -16,9 +16,14 @@ Workloads (sizes of the SAW-INT4 serving shapes; synthetic data):
                          --variant bdr (K block --k-block) | plain | bf16
   qwen3_32b_like_decode  Hq=64, Hkv=8, 256 log-normal sequences (~2.94M
                          tokens), page 16; a step writes 1 token per sequence
-                         and decodes all sequences over L+1
+                         and decodes all sequences over L+1; --variant fused
+                         does both in one kv_int4_paged_decode_step call
+  small_batch_decode     the same step for 4 sequences of 4096 tokens, Hq=32,
+                         Hkv=8 (latency-bound; --variant fused as above)
   long_context           1M-token sequence, Hq=64, Hkv=8, page 64, blocks
                          128/128; a step is the 64-chunk fill plus one decode
+  chunked_prefill        Hq=32, Hkv=8, 8 sequences with cached prefixes, each
+                         extended by a 1024-token chunk: write + causal extend
 
 Prints ONE JSON line.  ``value`` is KV tokens/s over the timed steps (tokens
 written plus tokens attended, each token = all KV heads of K and V), wall
@@ -58,8 +63,9 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_4b_like", choices=sorted(W.WORKLOADS))
-    ap.add_argument("--variant", default="bdr", choices=["bdr", "plain", "bf16"],
-                    help="prefill_chunk only: fused BDR write, plain INT4 write, or bf16 paged copy")
+    ap.add_argument("--variant", default="bdr", choices=["bdr", "plain", "bf16", "fused"],
+                    help="prefill_chunk: fused BDR write, plain INT4 write, or bf16 paged copy; "
+                         "qwen3_32b_like_decode: fused = write + decode in one call")
     ap.add_argument("--k-block", type=int, default=None, help="override the workload's K block")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -283,17 +289,33 @@ class Setup:
         n = K.kv_int4_paged_decode_workspace(self.cache, S, Hq, self.maxlen, self.args.split_tokens)
         self.ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
         mid = w.seq_lens + n_steps // 2
-        self.kernels = {"kv_rotquant_write": self.write_bytes(S, Hkv),
-                        "kv_int4_paged_decode": self.decode_bytes(mid, Hkv, Hq, P)}
+        if self.args.variant == "fused":
+            self.kernels = {"kv_int4_paged_decode_step": self.write_bytes(S, Hkv)
+                            + self.decode_bytes(mid, Hkv, Hq, P)}
+        else:
+            self.kernels = {"kv_rotquant_write": self.write_bytes(S, Hkv),
+                            "kv_int4_paged_decode": self.decode_bytes(mid, Hkv, Hq, P)}
         self.tokens_per_step = S + int(mid.sum())
         self.n_steps_max = n_steps
         self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                        "num_seqs": S, "tokens_written": S, "tokens_attended_mid": int(mid.sum()),
-                       "page_size": P, "k_block": kb, "v_block": w.v_block}
+                       "page_size": P, "k_block": kb, "v_block": w.v_block,
+                       "variant": "fused" if self.args.variant == "fused" else "write+decode"}
+
+    # -- small-batch decode steps: the same step as the high-concurrency one
+    setup_small_batch_decode = setup_qwen3_32b_like_decode
 
     def step_qwen3_32b_like_decode(self, i, ev):
         K = self.K
         j = i % self.n_steps_max
+        if self.args.variant == "fused":
+            ev[0].record()
+            K.kv_int4_paged_decode_step(self.cache, self.new_k[j % len(self.new_k)],
+                                        self.new_v[j % len(self.new_v)], self.step_slots[j], self.q,
+                                        self.tab, self.step_lens[j], self.maxlen, out=self.out,
+                                        split_tokens=self.args.split_tokens, workspace=self.ws)
+            ev[1].record()
+            return
         ev[0].record()
         K.kv_rotquant_write(self.cache, self.new_k[j % len(self.new_k)], self.new_v[j % len(self.new_v)],
                             self.step_slots[j])
@@ -301,6 +323,9 @@ class Setup:
         K.kv_int4_paged_decode(self.cache, self.q, self.tab, self.step_lens[j], self.maxlen,
                                out=self.out, split_tokens=self.args.split_tokens, workspace=self.ws)
         ev[2].record()
+
+    def step_small_batch_decode(self, i, ev):
+        self.step_qwen3_32b_like_decode(i, ev)
 
     # -- long context: 64 chunk writes + one decode
     def setup_long_context(self):
@@ -435,7 +460,7 @@ def cpu_baseline(args):
     # sample: up to 8 sequences (long context: 65536 tokens) of the workload's own shapes
     if args.workload == "long_context":
         lens = np.array([65536])
-    elif args.workload == "qwen3_32b_like_decode":
+    elif args.workload in ("qwen3_32b_like_decode", "small_batch_decode"):
         lens = w.seq_lens[:4]
     else:
         lens = w.seq_lens[:8]
@@ -625,6 +650,7 @@ def main():
     dominant = max(names, key=lambda n: per_kernel[n]["mean_us"] * per_kernel[n]["launches_per_step"])
     dk = per_kernel[dominant]
     symbol = {"kv_rotquant_write": "rotquant_write_kernel", "kv_int4_paged_decode": "decode_split_kernel",
+              "kv_int4_paged_decode_step": "decode_split_kernel",
               "kv_int4_paged_extend": "decode_split_kernel",
               "kvrq_bf16_paged_write": "bf16_paged_write_kernel"}[dominant]
     traffic, traffic_note = traffic_from_counters(args.counters, symbol, copy_bytes)

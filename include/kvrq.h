@@ -19,6 +19,8 @@
  *                         product equals the original one), INT4 pages are
  *                         de-quantised on the fly, the V rotation is undone on
  *                         the output;
+ *   kv_int4_paged_decode_step  the write of one new token per sequence
+ *                         fused into the decode that reads it;
  *   kv_int4_paged_extend  causal attention of a chunk of new query tokens
  *                         over the same cache (chunked prefill);
  *   kvrq_pool_*           a host page allocator and page table for the fixed-
@@ -208,6 +210,39 @@ KVRQ_API kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_c
                                  const int32_t *seq_lens, int32_t max_seq_len, float sm_scale,
                                  int32_t split_tokens, float *out, void *workspace,
                                  size_t workspace_bytes, void *stream);
+
+/* Fused decode step: write each sequence's new token and decode over it, in
+ * one pass of the decode's split kernel (plus its combine).  For the
+ * small-batch, latency-bound regime the pages serve next to the
+ * high-concurrency one (fugumt.com abstract: serving must support both, and
+ * the fused kernel matches plain INT4 across concurrency levels), where a
+ * separate write launch of a few hundred rows costs as much as its launch.
+ *   k_new, v_new    device bf16 [num_seqs][num_kv_heads][head_dim], one new
+ *                   token per sequence, token strides as in kv_rotquant_write
+ *   new_slots       device int32 [num_seqs]: the slot of position
+ *                   seq_lens[s] - 1 of sequence s (the same slot its page
+ *                   table gives); a negative slot writes nothing
+ *   the rest        as in kv_int4_paged_decode; seq_lens counts the new token
+ * The workgroup whose split holds position seq_lens[s] - 1 of sequence s and
+ * KV head h encodes that head's K and V rows exactly as kv_rotquant_write
+ * does (bit-identical cache bytes), stores them, and only then reads its
+ * tiles; no other workgroup reads that position.  A sequence with
+ * seq_lens[s] <= 0 writes nothing.  Preconditions (device data, not checked):
+ * seq_lens[s] <= max_seq_len (a longer one is clamped, and its new row is
+ * written but not attended), and new_slots[s] equal to the slot the page
+ * table gives for position seq_lens[s] - 1 (otherwise the decode reads
+ * whatever that position holds).
+ * Output and workspace are those of kv_int4_paged_decode with the same
+ * arguments (kv_int4_paged_decode_workspace gives the size). */
+KVRQ_API kvrq_status kv_int4_paged_decode_step(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
+                                               const void *k_new, const void *v_new,
+                                               int64_t k_token_stride, int64_t v_token_stride,
+                                               const int32_t *new_slots, const void *q,
+                                               int32_t num_seqs, int32_t num_q_heads,
+                                               const int32_t *page_table, int32_t max_pages_per_seq,
+                                               const int32_t *seq_lens, int32_t max_seq_len,
+                                               float sm_scale, int32_t split_tokens, float *out,
+                                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes kv_int4_paged_extend needs (arguments as in that call;
  * split_tokens 0 = automatic). */

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     Pool,
     kv_int4_paged_decode,
     kv_int4_paged_decode_workspace,
+    kv_int4_paged_decode_step,
     kv_int4_paged_extend,
     kv_int4_paged_extend_workspace,
     kv_rotquant_write,

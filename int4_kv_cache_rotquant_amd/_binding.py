@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         "kv_int4_paged_decode_workspace": (st, [P, i32, i32, i32, i32, P]),
         "kv_int4_paged_decode": (st, [P, P, P, i32, i32, P, i32, P, i32, ctypes.c_float, i32, P, P,
                                       sz, P]),
+        "kv_int4_paged_decode_step": (st, [P, P, P, P, i64, i64, P, P, i32, i32, P, i32, P, i32,
+                                           ctypes.c_float, i32, P, P, sz, P]),
         "kv_int4_paged_extend_workspace": (st, [P, i32, i32, i32, i32, i32, i32, P]),
         "kv_int4_paged_extend": (st, [P, P, P, i32, i32, i32, P, P, i32, P, i32, i32, ctypes.c_float,
                                       i32, P, P, sz, P]),
@@ -194,6 +196,39 @@ def kv_int4_paged_decode(cache: PagedInt4Cache, q, page_table, seq_lens, max_seq
         ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(q), S, Hq, _ptr(page_table),
         int(page_table.shape[1]), _ptr(seq_lens), int(max_seq_len), float(sm_scale), int(split_tokens),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def kv_int4_paged_decode_step(cache: PagedInt4Cache, k_new, v_new, new_slots, q, page_table, seq_lens,
+                              max_seq_len: int, out=None, sm_scale: float = 0.0, split_tokens: int = 0,
+                              workspace=None, stream=None):
+    """Write one new token per sequence (bf16 ``k_new``/``v_new`` [S][Hkv][128] into
+    ``new_slots`` [S]) and decode ``q`` over it, in one pass; returns fp32 ``out``."""
+    import torch
+    S, Hq, D = q.shape
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or D != HEAD_DIM:
+        raise ValueError("q must be contiguous bf16 [S][Hq][128]")
+    for t in (k_new, v_new):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.shape[0] != S or t.stride(2) != 1 or \
+                t.stride(1) != HEAD_DIM:
+            raise ValueError("k_new and v_new must be bf16 [S][Hkv][128] with contiguous heads")
+    if new_slots.dtype != torch.int32 or new_slots.shape != (S,):
+        raise ValueError("new_slots must be int32 [S]")
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.shape[0] != S:
+        raise ValueError("page_table must be contiguous int32 [S][max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (S,):
+        raise ValueError("seq_lens must be int32 [S]")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = kv_int4_paged_decode_workspace(cache, S, Hq, max_seq_len, split_tokens)
+        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().kv_int4_paged_decode_step(
+        ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(k_new), _ptr(v_new),
+        k_new.stride(0), v_new.stride(0), _ptr(new_slots), _ptr(q), S, Hq, _ptr(page_table),
+        int(page_table.shape[1]), _ptr(seq_lens), int(max_seq_len), float(sm_scale),
+        int(split_tokens), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
     return out
 
 

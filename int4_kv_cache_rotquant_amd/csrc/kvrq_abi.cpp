@@ -441,11 +441,21 @@ kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, int32_t num
     return KVRQ_OK;
 }
 
-kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, const void *q,
-                                 int32_t num_seqs, int32_t num_q_heads, const int32_t *page_table,
-                                 int32_t max_pages_per_seq, const int32_t *seq_lens,
-                                 int32_t max_seq_len, float sm_scale, int32_t split_tokens, float *out,
-                                 void *workspace, size_t workspace_bytes, void *stream)
+namespace {
+
+// The new token rows of a fused decode step.
+struct StepRows {
+    const void *k, *v;
+    int64_t k_stride, v_stride;
+    const int32_t *slots;
+};
+
+kvrq_status decode_impl(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, const void *q,
+                        int32_t num_seqs, int32_t num_q_heads, const int32_t *page_table,
+                        int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
+                        float sm_scale, int32_t split_tokens, float *out, void *workspace,
+                        size_t workspace_bytes, void *stream, const StepRows *step,
+                        const char *what)
 {
     kvrq_status st = check_decode_shape(d, num_seqs, num_q_heads, max_seq_len, split_tokens);
     if (st)
@@ -453,6 +463,11 @@ kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buff
     st = check_buffers(b);
     if (st)
         return st;
+    if (step) {
+        st = check_rows(d, step->k, step->v, num_seqs, step->k_stride, step->v_stride, step->slots);
+        if (st)
+            return st;
+    }
     if (num_seqs == 0)
         return KVRQ_OK;
     if (!q || !page_table || !seq_lens || !out)
@@ -503,7 +518,49 @@ kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buff
     a.num_rows = num_seqs;
     a.rows_per_block = 1;
     a.blocks_per_seq = 1;
-    return hip_status(kvrq::launch_decode(d->k_block, d->v_block, a, stream), "kv_int4_paged_decode");
+    if (step) {
+        a.new_slots = step->slots;
+        a.k_new = static_cast<const uint16_t *>(step->k);
+        a.v_new = static_cast<const uint16_t *>(step->v);
+        a.k_new_stride = step->k_stride;
+        a.v_new_stride = step->v_stride;
+        a.k_codes_w = b->k_codes;
+        a.v_codes_w = b->v_codes;
+        a.k_params_w = reinterpret_cast<uint32_t *>(b->k_params);
+        a.v_params_w = reinterpret_cast<uint32_t *>(b->v_params);
+        a.num_slots = int64_t(d->num_pages) * d->page_size;
+        a.v_block = d->v_block;
+    }
+    return hip_status(kvrq::launch_decode(d->k_block, d->v_block, a, stream), what);
+}
+
+}  // namespace
+
+kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, const void *q,
+                                 int32_t num_seqs, int32_t num_q_heads, const int32_t *page_table,
+                                 int32_t max_pages_per_seq, const int32_t *seq_lens,
+                                 int32_t max_seq_len, float sm_scale, int32_t split_tokens, float *out,
+                                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    return decode_impl(d, b, q, num_seqs, num_q_heads, page_table, max_pages_per_seq, seq_lens,
+                       max_seq_len, sm_scale, split_tokens, out, workspace, workspace_bytes, stream,
+                       nullptr, "kv_int4_paged_decode");
+}
+
+KVRQ_API kvrq_status kv_int4_paged_decode_step(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
+                                               const void *k_new, const void *v_new,
+                                               int64_t k_token_stride, int64_t v_token_stride,
+                                               const int32_t *new_slots, const void *q,
+                                               int32_t num_seqs, int32_t num_q_heads,
+                                               const int32_t *page_table, int32_t max_pages_per_seq,
+                                               const int32_t *seq_lens, int32_t max_seq_len,
+                                               float sm_scale, int32_t split_tokens, float *out,
+                                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    const StepRows step{k_new, v_new, k_token_stride, v_token_stride, new_slots};
+    return decode_impl(d, b, q, num_seqs, num_q_heads, page_table, max_pages_per_seq, seq_lens,
+                       max_seq_len, sm_scale, split_tokens, out, workspace, workspace_bytes, stream,
+                       &step, "kv_int4_paged_decode_step");
 }
 
 KVRQ_API kvrq_status kv_int4_paged_extend_workspace(const kvrq_cache_desc *d, int32_t num_seqs,

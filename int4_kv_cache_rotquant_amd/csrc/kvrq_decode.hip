@@ -30,6 +30,7 @@
 // decode_combine_kernel (a 16-wave workgroup per (query head, sequence)) beyond.
 #include <hip/hip_runtime.h>
 
+#include "kvrq_encode.h"
 #include "kvrq_internal.h"
 
 namespace kvrq {
@@ -494,6 +495,35 @@ struct WaveState {
     }
 };
 
+// Fused decode step: lanes 0-3 encode the new K row of (sequence s, KV head h) and lanes
+// 4-7 its V row, exactly as the write kernel does, into the slot given for it.
+template <int BK>
+__device__ __forceinline__ void write_new_rows(const DecodeArgs &a, int s, int h,
+                                               int lane)
+{
+    const int ql = lane & 3;
+    const bool is_v = lane >= 4;
+    const int32_t slot = a.new_slots[s];
+    const uint16_t *src = (is_v ? a.v_new + s * a.v_new_stride : a.k_new + s * a.k_new_stride)
+                          + h * kHeadDim + 32 * ql;
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        bf16x8_to_f32(reinterpret_cast<const u32x4 *>(src)[j], x + 8 * j);
+    if (!is_v) {
+        encode_row<BK>(x, slot, a.k_codes_w, a.k_params_w, a.num_slots, a.num_kv_heads,
+                       a.page_log2, h, ql);
+        return;
+    }
+    switch (a.v_block) {
+    case 16: encode_row<16>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
+    case 32: encode_row<32>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
+    case 64: encode_row<64>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
+    case 128: encode_row<128>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
+    default: encode_row<0>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
+    }
+}
+
 template <int BK, int F, bool EXT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? 4 : 2)))
 void decode_split_kernel(DecodeArgs a)
@@ -533,6 +563,13 @@ void decode_split_kernel(DecodeArgs a)
     // the wave index, and with it the token range, is uniform across the wave: keep it
     // scalar so the page-table lookups and the loop control stay on the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // fused decode step: the workgroup holding position L - 1 writes that token's rows
+    // first; the barrier after the query prologue orders those stores before the tile
+    // loads of all four waves, and no other workgroup reads that position
+    if constexpr (!EXT) {
+        if (a.new_slots != nullptr && wave == 1 && split == (L - 1) / a.split_tokens && lane < 8)
+            write_new_rows<BK>(a, s, h, lane);
+    }
     // the waves share the split's tiles up to the row's length evenly (a split that the
     // length cuts short still keeps all four waves busy)
     const int wg_end = min(L, wg_begin + a.split_tokens);

@@ -1,0 +1,152 @@
+// Row encoder of the rotated INT4 cache, shared by the write kernel and the fused decode
+// step: block Walsh-Hadamard rotation + token-wise INT4 quantisation of one 128-channel
+// (token, head) row held by a quad of lanes (32 channels each), stored into its page
+// (SAW-INT4: K~ = quant(K H_blk), V~ = quant(V H_blk); wispaper.ai blog, section 3 core
+// formula, and section 2 for the block-diagonal matrix).
+//
+// Bit-exactness: every step runs in IEEE binary32 in a fixed order -- butterfly widths
+// 1, 2, 4, ... with (u+w, u-w), then * fp32(1/sqrt b); exact min/max; correctly rounded
+// (mx-mn)/15 and 1/scale; round-to-nearest-even binary16 parameters; codes from the
+// stored parameters.  No multiply-add is fused here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kvrq_internal.h"
+
+namespace kvrq {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 value of 1/sqrt(b), the rotation's normalisation.
+template <int B> struct InvSqrt;
+template <> struct InvSqrt<16> { static constexpr float value = 0x1p-2f; };
+template <> struct InvSqrt<32> { static constexpr float value = 0x1.6a09e6p-3f; };
+template <> struct InvSqrt<64> { static constexpr float value = 0x1p-3f; };
+template <> struct InvSqrt<128> { static constexpr float value = 0x1.6a09e6p-4f; };
+
+// DPP quad permutes: value of lane ql^1 / ql^2 within the quad.
+__device__ __forceinline__ float quad_swap1(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float quad_swap2(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4 &w, float *x)
+{
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        x[2 * m] = __uint_as_float(d[m] << 16);
+        x[2 * m + 1] = __uint_as_float(d[m] & 0xFFFF0000u);
+    }
+}
+
+// Block Walsh-Hadamard transform of a row, this lane's 32 channels.
+template <int B>
+__device__ __forceinline__ void rotate_row(float (&x)[32], int ql)
+{
+#pragma clang fp contract(off)
+    if constexpr (B > 1) {
+        constexpr int in_lane = B < 32 ? B : 32;
+#pragma unroll
+        for (int h = 1; h < in_lane; h <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                if (i & h)
+                    continue;
+                const float u = x[i];
+                const float w = x[i + h];
+                x[i] = u + w;
+                x[i + h] = u - w;
+            }
+        }
+        if constexpr (B >= 64) {
+            // width 32: the lower lane keeps u + w, the upper lane u - w (= partner - self)
+            const float sgn = (ql & 1) ? -1.0f : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                x[i] = __builtin_fmaf(x[i], sgn, quad_swap1(x[i]));
+        }
+        if constexpr (B >= 128) {
+            const float sgn = (ql & 2) ? -1.0f : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                x[i] = __builtin_fmaf(x[i], sgn, quad_swap2(x[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            x[i] = x[i] * InvSqrt<B>::value;
+    }
+}
+
+// Rotate, quantise and store one row held in x; called by all four lanes of the quad.
+template <int B>
+__device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t *__restrict__ codes,
+                                           uint32_t *__restrict__ params, int64_t num_slots,
+                                           int num_kv_heads, int page_log2, int h, int ql)
+{
+#pragma clang fp contract(off)
+    rotate_row<B>(x, ql);
+
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+        mn = fminf(mn, x[i]);
+        mx = fmaxf(mx, x[i]);
+    }
+    mn = fminf(mn, quad_swap1(mn));
+    mx = fmaxf(mx, quad_swap1(mx));
+    mn = fminf(mn, quad_swap2(mn));
+    mx = fmaxf(mx, quad_swap2(mx));
+    mn = mn + 0.0f;  // a zero minimum is stored as +0
+    mx = mx + 0.0f;
+
+    const float scale32 = (mx - mn) / 15.0f;
+    const _Float16 s16 = (_Float16)scale32;
+    const _Float16 z16 = (_Float16)mn;
+    const uint32_t s_bits = __builtin_bit_cast(uint16_t, s16);
+    const uint32_t z_bits = __builtin_bit_cast(uint16_t, z16);
+
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    if (s_bits != 0u) {
+        const float zf = (float)z16;
+        const float inv = 1.0f / (float)s16;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t pair[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                uint32_t bits[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float v = (x[8 * k + 2 * m + e] - zf) * inv;
+                    // clamp to [0, 15], then round half to even: adding 1.5 * 2^23 leaves
+                    // the nearest integer in the low mantissa bits
+                    const float c = __builtin_amdgcn_fmed3f(v, 0.0f, 15.0f) + 12582912.0f;
+                    bits[e] = __float_as_uint(c);
+                }
+                pair[m] = (bits[1] << 4) | bits[0];  // low byte = code(2m) | code(2m+1) << 4
+            }
+            const uint32_t lo = __builtin_amdgcn_perm(pair[1], pair[0], 0x0C0C0400u);
+            const uint32_t hi = __builtin_amdgcn_perm(pair[3], pair[2], 0x0C0C0400u);
+            out[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        }
+    }
+    if (slot >= 0 && slot < num_slots) {
+        const int64_t page = slot >> page_log2;
+        const int64_t off = slot & ((1 << page_log2) - 1);
+        const int64_t cell = ((page * num_kv_heads + h) << page_log2) + off;
+        u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + ql;
+        *dst = u32x4{out[0], out[1], out[2], out[3]};
+        if (ql == 0)
+            params[cell] = s_bits | (z_bits << 16);
+    }
+}
+
+}  // namespace
+}  // namespace kvrq

@@ -76,10 +76,23 @@ struct DecodeArgs {
     float q_scale;              // sm_scale * log2(e)
     // extend (chunked prefill) only; qo_start == nullptr for the decode.  The output
     // rows are then query rows: q, out [total_q][Hq][128], part_* [total_q][Hq][splits]
-    const int32_t *qo_start;    // [S + 1] first query row of each sequence
+    const int32_t *qo_start = nullptr;  // [S + 1] first query row of each sequence
     int32_t num_rows;           // rows of the combine: S (decode) or total_q (extend)
     int32_t rows_per_block;     // query rows per workgroup (16 / group, at least 1)
     int32_t blocks_per_seq;     // ceil(max_q_len / rows_per_block)
+    // fused decode step only (new_slots == nullptr otherwise): each sequence's new token,
+    // written by the workgroup whose split holds position seq_len - 1, before it reads
+    const int32_t *new_slots = nullptr;  // [S] slot of the new token (negative: not written)
+    const uint16_t *k_new = nullptr;     // bf16 rows [S][Hkv][128], token strides below
+    const uint16_t *v_new = nullptr;
+    int64_t k_new_stride = 0;            // elements
+    int64_t v_new_stride = 0;
+    uint8_t *k_codes_w = nullptr;        // the same cache as k_codes ..., writable
+    uint8_t *v_codes_w = nullptr;
+    uint32_t *k_params_w = nullptr;
+    uint32_t *v_params_w = nullptr;
+    int64_t num_slots = 0;               // num_pages * page_size
+    int32_t v_block = 0;
 };
 
 // Returns a hipError_t value (0 = success).

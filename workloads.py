@@ -243,6 +243,18 @@ def qwen3_32b_like_decode(num_steps: int = 100) -> Workload:
                     OutlierSpec.none(8), seed, notes={"steps": num_steps})
 
 
+def small_batch_decode(num_steps: int = 100) -> Workload:
+    """Latency-bound decode steps: Hq=32, Hkv=8, 4 sequences of 4096 tokens, page 16
+    scattered, pool sized for ``num_steps`` more tokens each; K block 128, V plain."""
+    seed = BASE_SEED + 6
+    rng = np.random.Generator(np.random.PCG64([seed, 0]))
+    lens = np.full(4, 4096, np.int64)
+    k_out = OutlierSpec.random(rng, 8)
+    paging = assign_pages(rng, [int(L) + num_steps for L in lens], 16)
+    return Workload("small_batch_decode", 8, 32, 16, 128, 0, lens, paging, k_out,
+                    OutlierSpec.none(8), seed, notes={"steps": num_steps})
+
+
 def long_context() -> Workload:
     """One sequence of 1,048,576 tokens, Hkv=8, Hq=64, page 64 scattered, blocks 128/128,
     filled by 64 writes of 16384 tokens."""
@@ -277,4 +289,5 @@ WORKLOADS = {
     "qwen3_32b_like_decode": qwen3_32b_like_decode,
     "long_context": long_context,
     "chunked_prefill": chunked_prefill,
+    "small_batch_decode": small_batch_decode,
 }
