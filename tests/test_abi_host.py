@@ -131,6 +131,26 @@ def test_decode_validation(K):
     assert dec(wsp=0) == K.KVRQ_EWORKSPACE
 
 
+def test_decode_step_validation(K):
+    L = K.lib()
+
+    def step(k=0x10000, v=0x20000, ks=1024, vs=1024, slots=0x30000, S=2, q=0x1000, wsb=1 << 30,
+             lens=0x3000, out=0x4000):
+        return L.kv_int4_paged_decode_step(ctypes.byref(_desc(K)), ctypes.byref(_bufs(K)), k, v, ks, vs,
+                                           slots, q, S, 64, 0x2000, 100, lens, 1000, 0.0, 0, out,
+                                           0x5000, wsb, None)
+
+    assert step(S=0) == K.KVRQ_OK
+    assert step(k=0) == K.KVRQ_EINVAL and "non-NULL" in K.last_error()
+    assert step(slots=0) == K.KVRQ_EINVAL
+    assert step(ks=1000) == K.KVRQ_EINVAL and "strides" in K.last_error()
+    assert step(vs=1028) == K.KVRQ_EINVAL
+    assert step(v=0x20008) == K.KVRQ_EINVAL and "aligned" in K.last_error()
+    assert step(slots=0x30002) == K.KVRQ_EINVAL
+    assert step(q=0) == K.KVRQ_EINVAL
+    assert step(wsb=16) == K.KVRQ_EWORKSPACE
+
+
 def test_extend_validation(K):
     L = K.lib()
     size = ctypes.c_size_t()
