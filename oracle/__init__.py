@@ -65,16 +65,16 @@ def lib() -> ctypes.CDLL:
         L.kvrq_oracle_fwht_f32.restype = None
         L.kvrq_oracle_rotate_f64.argtypes = [P, P, i32, i32]
         L.kvrq_oracle_rotate_f64.restype = None
-        L.kvrq_oracle_quant_row.argtypes = [P, i32, i32, P, P, P, P]
+        L.kvrq_oracle_quant_row.argtypes = [P, i32, i32, i32, P, P, P, P]
         L.kvrq_oracle_quant_row.restype = i32
-        L.kvrq_oracle_write.argtypes = [i32, i32, i32, i32, i32, i32, i32, P, P, i64, i64, P,
-                                        P, P, P, P, P, P]
+        L.kvrq_oracle_write.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P, i64,
+                                        i64, P, P, P, P, P, P, P]
         L.kvrq_oracle_write.restype = i32
-        L.kvrq_oracle_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, i32, P,
-                                         f64, P, P, P, P, P]
+        L.kvrq_oracle_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P,
+                                         i32, P, f64, P, P, P, P, P]
         L.kvrq_oracle_decode.restype = i32
-        L.kvrq_oracle_extend.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, P, P, P, i32, P,
-                                         ctypes.c_double, P, P, P, P, P]
+        L.kvrq_oracle_extend.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P,
+                                         P, i32, P, ctypes.c_double, P, P, P, P, P]
         L.kvrq_oracle_extend.restype = i32
         _lib = L
     return _lib
@@ -125,30 +125,32 @@ def rotate_f64(x: np.ndarray, b: int) -> np.ndarray:
 
 
 # ------------------------------------------------------------------ write
-def quant_row(x_bf16: np.ndarray, b: int):
-    """One row -> (codes uint8[D/2], (s16, z16) uint16[2], vpre f32[D], y f32[D])."""
+def quant_row(x_bf16: np.ndarray, b: int, bits: int = 4):
+    """One row -> (codes uint8[D*bits/8], (s16, z16) uint16[2], vpre f32[D], y f32[D])."""
     x = np.ascontiguousarray(x_bf16, np.uint16)
     D = x.shape[0]
-    codes = np.zeros(D // 2, np.uint8)
+    codes = np.zeros(D * bits // 8, np.uint8)
     params = np.zeros(2, np.uint16)
     vpre = np.zeros(D, np.float32)
     y = np.zeros(D, np.float32)
-    rc = lib().kvrq_oracle_quant_row(_p(x), D, b, _p(codes), _p(params), _p(vpre), _p(y))
+    rc = lib().kvrq_oracle_quant_row(_p(x), D, b, bits, _p(codes), _p(params), _p(vpre), _p(y))
     if rc:
         raise ValueError("bad row shape")
     return codes, params, vpre, y
 
 
 class Cache:
-    """Host copy of one layer's paged INT4 cache (oracle side)."""
+    """Host copy of one layer's paged INT4 (or 2-bit) cache (oracle side)."""
 
     def __init__(self, num_pages: int, num_kv_heads: int, page_size: int, head_dim: int = 128,
-                 fill: int = 0xAA):
+                 fill: int = 0xAA, k_bits: int = 4, v_bits: int = 4):
         self.num_pages, self.Hkv, self.P, self.D = num_pages, num_kv_heads, page_size, head_dim
-        shape_c = (num_pages, num_kv_heads, page_size, head_dim // 2)
+        self.k_bits, self.v_bits = k_bits, v_bits
         shape_p = (num_pages, num_kv_heads, page_size, 2)
-        self.k_codes = np.full(shape_c, fill, np.uint8)
-        self.v_codes = np.full(shape_c, fill, np.uint8)
+        self.k_codes = np.full((num_pages, num_kv_heads, page_size, head_dim * k_bits // 8), fill,
+                               np.uint8)
+        self.v_codes = np.full((num_pages, num_kv_heads, page_size, head_dim * v_bits // 8), fill,
+                               np.uint8)
         self.k_params = np.full(shape_p, fill * 0x101, np.uint16)
         self.v_params = np.full(shape_p, fill * 0x101, np.uint16)
 
@@ -165,7 +167,8 @@ def write(cache: Cache, k: np.ndarray, v: np.ndarray, slots: np.ndarray, k_block
     if want_vpre:
         kv = np.zeros((T, Hkv, D), np.float32)
         vv = np.zeros((T, Hkv, D), np.float32)
-    rc = lib().kvrq_oracle_write(T, Hkv, D, cache.P, cache.num_pages, k_block, v_block, _p(k),
+    rc = lib().kvrq_oracle_write(T, Hkv, D, cache.P, cache.num_pages, k_block, v_block,
+                                 cache.k_bits, cache.v_bits, _p(k),
                                  _p(v), Hkv * D, Hkv * D, _p(slots), _p(cache.k_codes),
                                  _p(cache.v_codes), _p(cache.k_params), _p(cache.v_params),
                                  _p(kv), _p(vv))
@@ -175,19 +178,29 @@ def write(cache: Cache, k: np.ndarray, v: np.ndarray, slots: np.ndarray, k_block
 
 
 # ------------------------------------------------------------------ decode
+def code_bits(codes: np.ndarray, head_dim: int) -> int:
+    """Code width of a pool from its row bytes: D/2 -> 4 bits, D/4 -> 2 bits."""
+    bits = codes.shape[-1] * 8 // head_dim
+    if bits not in (2, 4) or codes.shape[-1] * 8 != bits * head_dim:
+        raise ValueError(f"code rows of {codes.shape[-1]} bytes fit no supported width")
+    return bits
+
+
 def decode(q: np.ndarray, cache_arrays, page_table: np.ndarray, seq_lens: np.ndarray,
            num_kv_heads: int, page_size: int, k_block: int, v_block: int,
            sm_scale: float = 0.0) -> np.ndarray:
-    """fp64 attention; ``cache_arrays`` = (k_codes, v_codes, k_params, v_params)."""
+    """fp64 attention; ``cache_arrays`` = (k_codes, v_codes, k_params, v_params); the
+    code widths follow from the code arrays' row bytes (D/2: 4 bits, D/4: 2 bits)."""
     q = np.ascontiguousarray(q, np.uint16)
     S, Hq, D = q.shape
     kc, vc, kp, vp = [np.ascontiguousarray(a) for a in cache_arrays]
+    kbits, vbits = code_bits(kc, D), code_bits(vc, D)
     num_pages = kc.shape[0]
     page_table = np.ascontiguousarray(page_table, np.int32)
     seq_lens = np.ascontiguousarray(seq_lens, np.int32)
     out = np.zeros((S, Hq, D), np.float64)
     rc = lib().kvrq_oracle_decode(S, Hq, num_kv_heads, D, page_size, num_pages, k_block, v_block,
-                                  _p(q), _p(page_table), page_table.shape[1], _p(seq_lens),
+                                  kbits, vbits, _p(q), _p(page_table), page_table.shape[1], _p(seq_lens),
                                   float(sm_scale), _p(kc), _p(vc), _p(kp), _p(vp), _p(out))
     if rc == 1:
         raise ValueError("bad decode shapes")
@@ -204,6 +217,7 @@ def extend(q: np.ndarray, cache_arrays, qo_start: np.ndarray, page_table: np.nda
     q = np.ascontiguousarray(q, np.uint16)
     total_q, Hq, D = q.shape
     kc, vc, kp, vp = [np.ascontiguousarray(a) for a in cache_arrays]
+    kbits, vbits = code_bits(kc, D), code_bits(vc, D)
     num_pages = kc.shape[0]
     qo_start = np.ascontiguousarray(qo_start, np.int32)
     page_table = np.ascontiguousarray(page_table, np.int32)
@@ -213,7 +227,7 @@ def extend(q: np.ndarray, cache_arrays, qo_start: np.ndarray, page_table: np.nda
         raise ValueError("qo_start must have S+1 entries ending at total_q")
     out = np.zeros((total_q, Hq, D), np.float64)
     rc = lib().kvrq_oracle_extend(S, Hq, num_kv_heads, D, page_size, num_pages, k_block,
-                                  v_block, _p(q), _p(qo_start), _p(page_table),
+                                  v_block, kbits, vbits, _p(q), _p(qo_start), _p(page_table),
                                   page_table.shape[1], _p(seq_lens), float(sm_scale), _p(kc),
                                   _p(vc), _p(kp), _p(vp), _p(out))
     if rc == 1:

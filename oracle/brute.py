@@ -52,12 +52,14 @@ def fwht_f32_vec(x: np.ndarray, b: int) -> np.ndarray:
     return (blocks * r).reshape(y.shape)
 
 
-def quantize_rows(x_bf16: np.ndarray, b: int):
-    """Rows [..., D] -> (codes uint8 [..., D/2], s16 bits, z16 bits, vpre f32)."""
+def quantize_rows(x_bf16: np.ndarray, b: int, bits: int = 4):
+    """Rows [..., D] -> (codes uint8 [..., D*bits/8], s16 bits, z16 bits, vpre f32); 2^bits - 1
+    levels, channel d at bit (d*bits) % 8 of byte d*bits/8."""
+    levels = (1 << bits) - 1
     y = fwht_f32_vec(bf16_to_f32(x_bf16), b)
     mn = y.min(axis=-1) + np.float32(0.0)
     mx = y.max(axis=-1) + np.float32(0.0)
-    scale32 = (mx - mn) / np.float32(15.0)
+    scale32 = (mx - mn) / np.float32(levels)
     s16 = scale32.astype(np.float16)
     z16 = mn.astype(np.float16)
     sf = s16.astype(np.float32)[..., None]
@@ -67,17 +69,27 @@ def quantize_rows(x_bf16: np.ndarray, b: int):
         v = (y - zf) * inv
     zero = (s16.view(np.uint16) & 0x7FFF) == 0
     v = np.where(zero[..., None], np.float32(0.0), v).astype(np.float32)
-    q = np.clip(np.rint(v), 0, 15).astype(np.uint8)
-    codes = (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8)
+    q = np.clip(np.rint(v), 0, levels).astype(np.uint8)
+    per = 8 // bits
+    codes = np.zeros(q.shape[:-1] + (q.shape[-1] // per,), np.uint8)
+    for j in range(per):
+        codes |= (q[..., j::per] << (bits * j)).astype(np.uint8)
     return codes, s16.view(np.uint16), z16.view(np.uint16), v
 
 
-def dequant_rows(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
-    """Codes [..., D/2] with fp16 bits (s, z) -> fp64 values q*s + z."""
+def unpack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Codes [..., D*bits/8] -> integer codes [..., D]."""
     c = np.asarray(codes, np.uint8)
-    q = np.empty(c.shape[:-1] + (2 * c.shape[-1],), np.float64)
-    q[..., 0::2] = c & 15
-    q[..., 1::2] = c >> 4
+    per = 8 // bits
+    q = np.empty(c.shape[:-1] + (per * c.shape[-1],), np.int64)
+    for j in range(per):
+        q[..., j::per] = (c >> (bits * j)) & ((1 << bits) - 1)
+    return q
+
+
+def dequant_rows(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray, bits: int = 4) -> np.ndarray:
+    """Codes [..., D*bits/8] with fp16 bits (s, z) -> fp64 values q*s + z."""
+    q = unpack_codes(codes, bits).astype(np.float64)
     s = np.asarray(s16, np.uint16).view(np.float16).astype(np.float64)[..., None]
     z = np.asarray(z16, np.uint16).view(np.float16).astype(np.float64)[..., None]
     return q * s + z
@@ -89,8 +101,11 @@ def gather_seq(cache_arrays, page_table_row: np.ndarray, L: int, page_size: int,
     t = np.arange(L)
     pages = np.asarray(page_table_row)[t // page_size]
     off = t % page_size
-    K = dequant_rows(kc[pages, h, off], kp[pages, h, off, 0], kp[pages, h, off, 1])
-    V = dequant_rows(vc[pages, h, off], vp[pages, h, off, 0], vp[pages, h, off, 1])
+    D = 128
+    K = dequant_rows(kc[pages, h, off], kp[pages, h, off, 0], kp[pages, h, off, 1],
+                     kc.shape[-1] * 8 // D)
+    V = dequant_rows(vc[pages, h, off], vp[pages, h, off, 0], vp[pages, h, off, 1],
+                     vc.shape[-1] * 8 // D)
     return K, V
 
 

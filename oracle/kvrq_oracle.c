@@ -40,6 +40,11 @@
  *   7. byte i = q[2i] | q[2i+1] << 4
  *   8. codes at [page][Hkv][P][D/2], (s16, z16) at [page][Hkv][P][2]
  *
+ * The 2-bit variant (an open question on the pages: wispaper.ai blog, section
+ * 5, limitations) takes the same steps with 3 levels for 15 (scale32 =
+ * (mx - mn) / 3.0f, q clamped to [0, 3]), four codes per byte (channel d at
+ * bit 2 (d % 4) of byte d / 4) and D/4-byte rows.
+ *
  * The decode has a plain definition and is computed in fp64 from it.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
@@ -186,18 +191,22 @@ ORACLE_API void kvrq_oracle_rotate_f64(const double *x, double *y, int n, int b)
 /* write                                                                   */
 /* ---------------------------------------------------------------------- */
 
-/* Quantise one row of D bf16 values with rotation block b.
- *   codes   D/2 bytes (even channel in the low nibble)
+/* Quantise one row of D bf16 values with rotation block b to `bits` bits (4, or 2 for
+ * the 2-bit variant the pages leave open: wispaper.ai blog, section 5, limitations).
+ *   codes   D*bits/8 bytes; channel d sits at bit (d*bits) % 8 of byte d*bits/8
+ *           (4 bits: the even channel in the low nibble)
  *   params  [0] = s16 bits, [1] = z16 bits
  *   vpre    optional, D fp32 pre-round values v (0 when s16 == 0)
  *   y_out   optional, D fp32 rotated values y
- * Returns 0. */
-ORACLE_API int kvrq_oracle_quant_row(const uint16_t *x, int D, int b, uint8_t *codes,
+ * The steps are those of 4 bits with 2^bits - 1 levels in place of 15.
+ * Returns 0, or 1 for a bad shape. */
+ORACLE_API int kvrq_oracle_quant_row(const uint16_t *x, int D, int b, int bits, uint8_t *codes,
                                      uint16_t *params, float *vpre, float *y_out)
 {
     float y[1024];
-    if (D > 1024 || D % 2 || (b > 1 && D % b))
+    if (D > 1024 || D % 8 || (b > 1 && D % b) || (bits != 4 && bits != 2))
         return 1;
+    const float levels = (float)((1 << bits) - 1);
     for (int d = 0; d < D; ++d)
         y[d] = kvrq_oracle_bf16_to_f32(x[d]);
     kvrq_oracle_fwht_f32(y, D, b);
@@ -211,7 +220,7 @@ ORACLE_API int kvrq_oracle_quant_row(const uint16_t *x, int D, int b, uint8_t *c
     }
     mn = mn + 0.0f;
     mx = mx + 0.0f;
-    const float scale32 = (mx - mn) / 15.0f;
+    const float scale32 = (mx - mn) / levels;
     const uint16_t s16 = kvrq_oracle_f32_to_f16(scale32);
     const uint16_t z16 = kvrq_oracle_f32_to_f16(mn);
     params[0] = s16;
@@ -234,15 +243,17 @@ ORACLE_API int kvrq_oracle_quant_row(const uint16_t *x, int D, int b, uint8_t *c
             float r = rintf(v);
             if (r < 0.0f)
                 r = 0.0f;
-            if (r > 15.0f)
-                r = 15.0f;
+            if (r > levels)
+                r = levels;
             q[d] = (uint8_t)r;
             if (vpre)
                 vpre[d] = v;
         }
     }
-    for (int i = 0; i < D / 2; ++i)
-        codes[i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));
+    for (int i = 0; i < D * bits / 8; ++i)
+        codes[i] = 0;
+    for (int d = 0; d < D; ++d)
+        codes[d * bits / 8] |= (uint8_t)(q[d] << ((d * bits) % 8));
     if (y_out)
         for (int d = 0; d < D; ++d)
             y_out[d] = y[d];
@@ -252,17 +263,20 @@ ORACLE_API int kvrq_oracle_quant_row(const uint16_t *x, int D, int b, uint8_t *c
 /* Write T tokens of K and V into the paged cache.
  *   k, v          bf16 bits, token t head h at  k[t*k_stride + h*D]
  *   slots         [T], slot = page*P + off, < 0 = skip
- *   *_codes       uint8 [num_pages][Hkv][P][D/2]
+ *   *_codes       uint8 [num_pages][Hkv][P][D*bits/8], bits = k_bits or v_bits (4 or 2)
  *   *_params      uint16 [num_pages][Hkv][P][2]
  *   k_vpre/v_vpre optional fp32 [T][Hkv][D] pre-round values
- * Returns 0, or 2 for a slot outside the pool. */
+ * Returns 0, 1 for bad bit widths, or 2 for a slot outside the pool. */
 ORACLE_API int kvrq_oracle_write(int T, int Hkv, int D, int P, int num_pages, int k_block,
-                                 int v_block, const uint16_t *k, const uint16_t *v,
+                                 int v_block, int k_bits, int v_bits, const uint16_t *k,
+                                 const uint16_t *v,
                                  int64_t k_stride, int64_t v_stride, const int32_t *slots,
                                  uint8_t *k_codes, uint8_t *v_codes, uint16_t *k_params,
                                  uint16_t *v_params, float *k_vpre, float *v_vpre)
 {
     int bad = 0;
+    if ((k_bits != 4 && k_bits != 2) || (v_bits != 4 && v_bits != 2))
+        return 1;
     const int64_t rows = (int64_t)T * Hkv;
 #pragma omp parallel for schedule(static) reduction(| : bad)
     for (int64_t r = 0; r < rows; ++r) {
@@ -281,12 +295,14 @@ ORACLE_API int kvrq_oracle_write(int T, int Hkv, int D, int P, int num_pages, in
         for (int tensor = 0; tensor < 2; ++tensor) {
             const uint16_t *src = tensor == 0 ? k + (int64_t)t * k_stride + (int64_t)h * D
                                               : v + (int64_t)t * v_stride + (int64_t)h * D;
-            uint8_t *dst_c = (tensor == 0 ? k_codes : v_codes) + cell * (D / 2);
+            const int bits = tensor == 0 ? k_bits : v_bits;
+            uint8_t *dst_c = (tensor == 0 ? k_codes : v_codes) + cell * (D * bits / 8);
             uint16_t *dst_p = (tensor == 0 ? k_params : v_params) + cell * 2;
             float *vp = tensor == 0 ? k_vpre : v_vpre;
             if (vp)
                 vp += ((int64_t)t * Hkv + h) * D;
-            kvrq_oracle_quant_row(src, D, tensor == 0 ? k_block : v_block, dst_c, dst_p, vp, NULL);
+            kvrq_oracle_quant_row(src, D, tensor == 0 ? k_block : v_block, bits, dst_c, dst_p, vp,
+                                  NULL);
         }
     }
     return bad ? 2 : 0;
@@ -295,6 +311,12 @@ ORACLE_API int kvrq_oracle_write(int T, int Hkv, int D, int P, int num_pages, in
 /* ---------------------------------------------------------------------- */
 /* decode (fp64, plain definition)                                          */
 /* ---------------------------------------------------------------------- */
+
+/* Code of channel d in a row of `bits`-bit codes (the write's packing). */
+static int code_at(const uint8_t *row, int d, int bits)
+{
+    return (row[d * bits / 8] >> ((d * bits) % 8)) & ((1 << bits) - 1);
+}
 
 /* Softmax attention of one query row over tokens 0..L-1 of KV head h of one
  * sequence, written from its definition (wispaper.ai blog, section 3: the query is
@@ -305,7 +327,8 @@ ORACLE_API int kvrq_oracle_write(int T, int Hkv, int D, int P, int num_pages, in
  * qrow: bf16 bits [D]; o: fp64 [D]; L <= 0 gives zeros.  Returns 1 when a page id is
  * outside the pool (those tokens are left out). */
 static int attend_row(const uint16_t *qrow, int L, const int32_t *page_row, int h, int Hkv,
-                      int D, int P, int num_pages, int k_block, int v_block, double sm_scale,
+                      int D, int P, int num_pages, int k_block, int v_block, int k_bits,
+                      int v_bits, double sm_scale,
                       const uint8_t *k_codes, const uint8_t *v_codes,
                       const uint16_t *k_params, const uint16_t *v_params, double *o)
 {
@@ -334,9 +357,9 @@ static int attend_row(const uint16_t *qrow, int L, const int32_t *page_row, int 
         const int64_t cell = ((int64_t)page * Hkv + h) * P + t % P;
         const double sc = kvrq_oracle_f16_to_f32(k_params[cell * 2 + 0]);
         const double zr = kvrq_oracle_f16_to_f32(k_params[cell * 2 + 1]);
-        const uint8_t *c = k_codes + cell * (D / 2);
+        const uint8_t *c = k_codes + cell * (D * k_bits / 8);
         for (int d = 0; d < D; ++d) {
-            const int code = (d & 1) ? (c[d / 2] >> 4) : (c[d / 2] & 15);
+            const int code = code_at(c, d, k_bits);
             kh[d] = code * sc + zr;
         }
         double dot = 0.0;
@@ -356,9 +379,9 @@ static int attend_row(const uint16_t *qrow, int L, const int32_t *page_row, int 
         const int64_t cell = ((int64_t)page * Hkv + h) * P + t % P;
         const double sc = kvrq_oracle_f16_to_f32(v_params[cell * 2 + 0]);
         const double zr = kvrq_oracle_f16_to_f32(v_params[cell * 2 + 1]);
-        const uint8_t *c = v_codes + cell * (D / 2);
+        const uint8_t *c = v_codes + cell * (D * v_bits / 8);
         for (int d = 0; d < D; ++d) {
-            const int code = (d & 1) ? (c[d / 2] >> 4) : (c[d / 2] & 15);
+            const int code = code_at(c, d, v_bits);
             acc[d] += p * (code * sc + zr);
         }
     }
@@ -374,18 +397,21 @@ static int attend_row(const uint16_t *qrow, int L, const int32_t *page_row, int 
  *   page_table  int32 [S][max_pages]
  *   seq_lens    int32 [S]; tokens 0..L-1 are attended
  *   sm_scale    softmax scale (<= 0: 1/sqrt(D))
+ *   k_bits, v_bits  code widths of the two pools (4, or 2)
  *   out         fp64 [S][Hq][D]; an empty sequence yields zeros
  * Query head g reads KV head g / (Hq/Hkv).  Returns 0, 1 for bad shapes,
  * 2 for a page id outside the pool. */
 ORACLE_API int kvrq_oracle_decode(int S, int Hq, int Hkv, int D, int P, int num_pages,
-                                  int k_block, int v_block, const uint16_t *q,
+                                  int k_block, int v_block, int k_bits, int v_bits,
+                                  const uint16_t *q,
                                   const int32_t *page_table, int max_pages,
                                   const int32_t *seq_lens, double sm_scale,
                                   const uint8_t *k_codes, const uint8_t *v_codes,
                                   const uint16_t *k_params, const uint16_t *v_params,
                                   double *out)
 {
-    if (Hkv <= 0 || Hq % Hkv || D > 1024)
+    if (Hkv <= 0 || Hq % Hkv || D > 1024 || (k_bits != 4 && k_bits != 2) ||
+        (v_bits != 4 && v_bits != 2))
         return 1;
     const int G = Hq / Hkv;
     if (sm_scale <= 0.0)
@@ -396,8 +422,8 @@ ORACLE_API int kvrq_oracle_decode(int S, int Hq, int Hkv, int D, int P, int num_
         const int s = (int)(sg / Hq);
         const int g = (int)(sg % Hq);
         bad |= attend_row(q + sg * D, seq_lens[s], page_table + (int64_t)s * max_pages, g / G,
-                          Hkv, D, P, num_pages, k_block, v_block, sm_scale, k_codes, v_codes,
-                          k_params, v_params, out + sg * D);
+                          Hkv, D, P, num_pages, k_block, v_block, k_bits, v_bits, sm_scale,
+                          k_codes, v_codes, k_params, v_params, out + sg * D);
     }
     return bad ? 2 : 0;
 }
@@ -413,14 +439,16 @@ ORACLE_API int kvrq_oracle_decode(int S, int Hq, int Hkv, int D, int P, int num_
  * Returns 0, 1 for bad shapes (including n_s > seq_lens[s]), 2 for a page id outside
  * the pool. */
 ORACLE_API int kvrq_oracle_extend(int S, int Hq, int Hkv, int D, int P, int num_pages,
-                                  int k_block, int v_block, const uint16_t *q,
+                                  int k_block, int v_block, int k_bits, int v_bits,
+                                  const uint16_t *q,
                                   const int32_t *qo_start, const int32_t *page_table,
                                   int max_pages, const int32_t *seq_lens, double sm_scale,
                                   const uint8_t *k_codes, const uint8_t *v_codes,
                                   const uint16_t *k_params, const uint16_t *v_params,
                                   double *out)
 {
-    if (Hkv <= 0 || Hq % Hkv || D > 1024 || qo_start[0] != 0)
+    if (Hkv <= 0 || Hq % Hkv || D > 1024 || qo_start[0] != 0 || (k_bits != 4 && k_bits != 2) ||
+        (v_bits != 4 && v_bits != 2))
         return 1;
     for (int s = 0; s < S; ++s) {
         const int n = qo_start[s + 1] - qo_start[s];
@@ -442,8 +470,8 @@ ORACLE_API int kvrq_oracle_extend(int S, int Hq, int Hkv, int D, int P, int num_
         const int n = qo_start[s + 1] - qo_start[s];
         const int len = seq_lens[s] - n + (int)(r - qo_start[s]) + 1;
         bad |= attend_row(q + rg * D, len, page_table + (int64_t)s * max_pages, g / G, Hkv, D, P,
-                          num_pages, k_block, v_block, sm_scale, k_codes, v_codes, k_params,
-                          v_params, out + rg * D);
+                          num_pages, k_block, v_block, k_bits, v_bits, sm_scale, k_codes,
+                          v_codes, k_params, v_params, out + rg * D);
     }
     return bad ? 2 : 0;
 }
