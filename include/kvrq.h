@@ -45,7 +45,8 @@
  * Cache layout (per layer, separate K and V pools):
  *   codes   uint8   [num_pages][num_kv_heads][page_size][head_dim/2]
  *           byte i of a row holds channel 2i in its low nibble and channel
- *           2i+1 in its high nibble;
+ *           2i+1 in its high nibble (a 2-bit pool: [..][head_dim/4], byte i
+ *           holds channels 4i..4i+3 at bits 0, 2, 4, 6);
  *   params  uint16  [num_pages][num_kv_heads][page_size][2]
  *           binary16 bit patterns (scale, zero); a row de-quantises as
  *           code * scale + zero in the rotated basis.
@@ -87,7 +88,13 @@ KVRQ_API const char *kvrq_last_error(void);
 
 /* Geometry of one layer's cache.  k_block / v_block: rotation block of the
  * K and V rows (0 = no rotation), the block sizes 16..128 of the pages
- * (wispaper.ai blog, section 2, block-diagonal bullet). */
+ * (wispaper.ai blog, section 2, block-diagonal bullet).  k_bits / v_bits:
+ * code width of each pool, 4 (0 means 4) or 2.  The 2-bit variant is the
+ * open question of the pages (wispaper.ai blog, section 5, limitations:
+ * whether the rotation keeps 2-bit accurate, perhaps with mixed precision);
+ * it quantises with 3 levels instead of 15 and stores four codes per byte,
+ * channel d at bit 2 (d % 4) of byte d / 4, in 32-byte rows.  K and V may
+ * differ (mixed precision). */
 typedef struct {
     int32_t head_dim;      /* D, must be 128 */
     int32_t num_kv_heads;  /* Hkv >= 1 */
@@ -95,6 +102,8 @@ typedef struct {
     int32_t num_pages;     /* pages in each pool, >= 1 */
     int32_t k_block;       /* 0, 16, 32, 64 or 128 */
     int32_t v_block;       /* 0, 16, 32, 64 or 128 */
+    int32_t k_bits;        /* 0 or 4: INT4; 2: 2-bit */
+    int32_t v_bits;        /* 0 or 4: INT4; 2: 2-bit */
 } kvrq_cache_desc;
 
 /* Device buffers of one layer's cache (caller-allocated, layout above).
@@ -106,9 +115,11 @@ typedef struct {
     uint16_t *v_params;
 } kvrq_cache_buffers;
 
-/* Bytes of ONE codes pool and ONE params pool for `d` (K and V each need
- * one of both).  Validates `d`. */
-KVRQ_API kvrq_status kvrq_cache_sizes(const kvrq_cache_desc *d, size_t *codes_bytes, size_t *params_bytes);
+/* Bytes of the K codes pool, the V codes pool and ONE params pool for `d`
+ * (K and V each need a params pool).  Validates `d`.  Any output may be
+ * NULL. */
+KVRQ_API kvrq_status kvrq_cache_sizes(const kvrq_cache_desc *d, size_t *k_codes_bytes,
+                                      size_t *v_codes_bytes, size_t *params_bytes);
 
 /* ------------------------------------------------------------------------
  * Host page pool and page table (host memory only; one pool per cache;

@@ -27,7 +27,8 @@ class KvrqError(RuntimeError):
 class CacheDesc(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-                ("k_block", ctypes.c_int32), ("v_block", ctypes.c_int32)]
+                ("k_block", ctypes.c_int32), ("v_block", ctypes.c_int32),
+                ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32)]
 
 
 class CacheBuffers(ctypes.Structure):
@@ -59,7 +60,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "kvrq_status_str": (ctypes.c_char_p, [st]),
         "kvrq_last_error": (ctypes.c_char_p, []),
-        "kvrq_cache_sizes": (st, [P, P, P]),
+        "kvrq_cache_sizes": (st, [P, P, P, P]),
         "kvrq_pool_create": (st, [i32, i32, i32, i32, ctypes.c_uint64, P]),
         "kvrq_pool_destroy": (None, [P]),
         "kvrq_seq_extend": (st, [P, i32, i32]),
@@ -114,30 +115,37 @@ def last_error() -> str:
 
 
 # --------------------------------------------------------------------- cache
-def kvrq_cache_sizes(desc: CacheDesc) -> Tuple[int, int]:
-    cb, pb = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(lib().kvrq_cache_sizes(ctypes.byref(desc), ctypes.byref(cb), ctypes.byref(pb)))
-    return cb.value, pb.value
+def kvrq_cache_sizes(desc: CacheDesc) -> Tuple[int, int, int]:
+    """(K codes bytes, V codes bytes, params bytes of one pool)."""
+    kb, vb, pb = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().kvrq_cache_sizes(ctypes.byref(desc), ctypes.byref(kb), ctypes.byref(vb),
+                                  ctypes.byref(pb)))
+    return kb.value, vb.value, pb.value
 
 
 class PagedInt4Cache:
-    """One layer's INT4 cache: descriptor + four torch device tensors."""
+    """One layer's INT4 (or 2-bit: ``k_bits``/``v_bits`` = 2) cache: descriptor + four torch
+    device tensors."""
 
     def __init__(self, num_pages: int, num_kv_heads: int, page_size: int, k_block: int,
-                 v_block: int, device="cuda", fill: Optional[int] = None):
+                 v_block: int, device="cuda", fill: Optional[int] = None, k_bits: int = 4,
+                 v_bits: int = 4):
         import torch
-        self.desc = CacheDesc(HEAD_DIM, num_kv_heads, page_size, num_pages, k_block, v_block)
-        codes_bytes, params_bytes = kvrq_cache_sizes(self.desc)
-        shape_c = (num_pages, num_kv_heads, page_size, HEAD_DIM // 2)
+        self.desc = CacheDesc(HEAD_DIM, num_kv_heads, page_size, num_pages, k_block, v_block,
+                              k_bits, v_bits)
+        k_bytes, v_bytes, params_bytes = kvrq_cache_sizes(self.desc)
         shape_p = (num_pages, num_kv_heads, page_size, 2)
-        self.k_codes = torch.empty(shape_c, dtype=torch.uint8, device=device)
-        self.v_codes = torch.empty(shape_c, dtype=torch.uint8, device=device)
+        self.k_codes = torch.empty((num_pages, num_kv_heads, page_size, HEAD_DIM * k_bits // 8),
+                                   dtype=torch.uint8, device=device)
+        self.v_codes = torch.empty((num_pages, num_kv_heads, page_size, HEAD_DIM * v_bits // 8),
+                                   dtype=torch.uint8, device=device)
         self.k_params = torch.empty(shape_p, dtype=torch.int16, device=device)
         self.v_params = torch.empty(shape_p, dtype=torch.int16, device=device)
         if fill is not None:
             for t in (self.k_codes, self.v_codes, self.k_params, self.v_params):
                 t.view(torch.uint8).fill_(fill)
-        assert self.k_codes.numel() == codes_bytes and self.k_params.numel() * 2 == params_bytes
+        assert self.k_codes.numel() == k_bytes and self.v_codes.numel() == v_bytes
+        assert self.k_params.numel() * 2 == params_bytes
         self.buffers = CacheBuffers(self.k_codes.data_ptr(), self.v_codes.data_ptr(),
                                     self.k_params.data_ptr(), self.v_params.data_ptr())
 

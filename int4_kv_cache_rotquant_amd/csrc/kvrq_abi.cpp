@@ -42,6 +42,10 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool valid_block(int b) { return b == 0 || b == 16 || b == 32 || b == 64 || b == 128; }
 
+// Code width of a pool: 0 (the default) and 4 mean INT4, 2 the 2-bit variant.
+int code_bits(int32_t b) { return b == 2 ? 2 : 4; }
+bool valid_bits(int32_t b) { return b == 0 || b == 2 || b == 4; }
+
 kvrq_status check_desc(const kvrq_cache_desc *d)
 {
     if (!d)
@@ -57,6 +61,9 @@ kvrq_status check_desc(const kvrq_cache_desc *d)
     if (!valid_block(d->k_block) || !valid_block(d->v_block))
         return fail(KVRQ_EUNSUPPORTED, "rotation blocks (%d, %d) unsupported (0, 16, 32, 64, 128)",
                     d->k_block, d->v_block);
+    if (!valid_bits(d->k_bits) || !valid_bits(d->v_bits))
+        return fail(KVRQ_EUNSUPPORTED, "code widths (%d, %d) unsupported (0 or 4 = INT4, 2)",
+                    d->k_bits, d->v_bits);
     const int64_t cells = int64_t(d->num_pages) * d->num_kv_heads * d->page_size;
     if (cells > (int64_t(1) << 40))
         return fail(KVRQ_EINVAL, "cache too large");
@@ -254,14 +261,17 @@ const char *kvrq_status_str(kvrq_status s)
 
 const char *kvrq_last_error(void) { return g_last_error.c_str(); }
 
-kvrq_status kvrq_cache_sizes(const kvrq_cache_desc *d, size_t *codes_bytes, size_t *params_bytes)
+kvrq_status kvrq_cache_sizes(const kvrq_cache_desc *d, size_t *k_codes_bytes, size_t *v_codes_bytes,
+                             size_t *params_bytes)
 {
     kvrq_status st = check_desc(d);
     if (st)
         return st;
     const size_t cells = size_t(d->num_pages) * d->num_kv_heads * d->page_size;
-    if (codes_bytes)
-        *codes_bytes = cells * (d->head_dim / 2);
+    if (k_codes_bytes)
+        *k_codes_bytes = cells * (d->head_dim * code_bits(d->k_bits) / 8);
+    if (v_codes_bytes)
+        *v_codes_bytes = cells * (d->head_dim * code_bits(d->v_bits) / 8);
     if (params_bytes)
         *params_bytes = cells * 2 * sizeof(uint16_t);
     return KVRQ_OK;
@@ -424,6 +434,8 @@ kvrq_status kv_rotquant_write(const kvrq_cache_desc *d, const kvrq_cache_buffers
     a.num_slots = int64_t(d->num_pages) * d->page_size;
     a.num_kv_heads = d->num_kv_heads;
     a.page_log2 = log2_exact(d->page_size);
+    a.k_bits = code_bits(d->k_bits);
+    a.v_bits = code_bits(d->v_bits);
     return hip_status(kvrq::launch_rotquant_write(d->k_block, d->v_block, a, stream), "kv_rotquant_write");
 }
 
@@ -510,6 +522,8 @@ kvrq_status decode_impl(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, c
     a.group = num_q_heads / d->num_kv_heads;
     a.page_log2 = log2_exact(d->page_size);
     a.max_pages = max_pages_per_seq;
+    a.k_bits = code_bits(d->k_bits);
+    a.v_bits = code_bits(d->v_bits);
     a.split_tokens = plan.split_tokens;
     a.max_splits = plan.max_splits;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(d->head_dim));
@@ -641,6 +655,8 @@ KVRQ_API kvrq_status kv_int4_paged_extend(const kvrq_cache_desc *d, const kvrq_c
     a.group = group;
     a.page_log2 = log2_exact(d->page_size);
     a.max_pages = max_pages_per_seq;
+    a.k_bits = code_bits(d->k_bits);
+    a.v_bits = code_bits(d->v_bits);
     a.split_tokens = plan.split_tokens;
     a.max_splits = plan.max_splits;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(d->head_dim));

@@ -184,11 +184,32 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const f16x8 &a, const f16x8 &b, co
 //   vc[j]   code dword n16 (channels 8 n16 .. 8 n16 + 7) of token 16 (j / 4) + 4 kq + j % 4
 //   par     lanes 0..31: (scale, zero) of K of token lane; lanes 32..63: V of token
 //           lane - 32; converted and shared through LDS when the tile is consumed
+// 2-bit pools (CB bit 0: K, bit 1: V; the 16-column layout only) load half the bytes:
+//   kc[j].xy  8 code bytes of token 16 j + n16, bytes [8 kq, 8 kq + 8) (channels
+//             32 kq .. 32 kq + 31 as for 4 bits)
+//   vc[j]     the 16-bit code word n16 (channels 8 n16 .. 8 n16 + 7)
+// and widen them to the 4-bit layout when the tile is consumed (spread2), so the rest of
+// the pipeline is the same: a 2-bit code is a 4-bit code below 4 with the same meaning.
 struct Tile {
     u32x4 kc[2];
     uint32_t vc[8];
     uint32_t par;
 };
+
+template <int CB> struct CodeWidths {
+    static constexpr bool k2 = (CB & 1) != 0;
+    static constexpr bool v2 = (CB & 2) != 0;
+    static constexpr int k_row = k2 ? kRowCodeBytes / 2 : kRowCodeBytes;
+    static constexpr int v_row = v2 ? kRowCodeBytes / 2 : kRowCodeBytes;
+};
+
+// Eight 2-bit codes (bits 2i of a 16-bit value) -> eight 4-bit codes (bits 4i).
+__device__ __forceinline__ uint32_t spread2(uint32_t x)
+{
+    x = (x | (x << 8)) & 0x00FF00FFu;
+    x = (x | (x << 4)) & 0x0F0F0F0Fu;
+    return (x | (x << 2)) & 0x33333333u;
+}
 
 // Issues the loads of the tile starting at t0 (< t_end).  A half tile that starts past
 // the end re-reads the first half's rows: every load is in bounds and unconditional, and
@@ -213,10 +234,11 @@ struct PageIds {
     }
 };
 
-template <int F>
+template <int F, int CB>
 __device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const PageIds &pid, int h,
                                           int t0, int t_end, int lane)
 {
+    using CW = CodeWidths<CB>;
     const int P = 1 << a.page_log2;
     const int n16 = lane & 15, kq = lane >> 4;
     // (page, head) row bases of the two 16-token halves; uniform, so on the scalar unit
@@ -227,12 +249,19 @@ __device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const Pa
         const int tb = hf && t0 + 16 >= t_end ? t0 : t0 + 16 * hf;
         const int page = pid.page(tb >> a.page_log2);
         const int64_t cell0 = ((int64_t)page * a.num_kv_heads + h) * P + (tb & (P - 1));
-        kb[hf] = a.k_codes + cell0 * kRowCodeBytes;
-        vb[hf] = a.v_codes + cell0 * kRowCodeBytes;
+        kb[hf] = a.k_codes + cell0 * CW::k_row;
+        vb[hf] = a.v_codes + cell0 * CW::v_row;
         kp[hf] = a.k_params + cell0;
         vp[hf] = a.v_params + cell0;
     }
-    if constexpr (F == 1) {
+    if constexpr (CW::k2) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const u32x2 w = *reinterpret_cast<const u32x2 *>(kb[hf] + n16 * CW::k_row + 8 * kq);
+            T.kc[hf].x = w.x;
+            T.kc[hf].y = w.y;
+        }
+    } else if constexpr (F == 1) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
             T.kc[hf] = *reinterpret_cast<const u32x4 *>(kb[hf] + n16 * kRowCodeBytes + 16 * kq);
@@ -244,9 +273,14 @@ __device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const Pa
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            T.vc[4 * hf + r] = *reinterpret_cast<const uint32_t *>(
-                vb[hf] + (uint32_t)((4 * kq + r) * kRowCodeBytes + 4 * n16));
+        for (int r = 0; r < 4; ++r) {
+            if constexpr (CW::v2)
+                T.vc[4 * hf + r] = *reinterpret_cast<const uint16_t *>(
+                    vb[hf] + (uint32_t)((4 * kq + r) * CW::v_row + 2 * n16));
+            else
+                T.vc[4 * hf + r] = *reinterpret_cast<const uint32_t *>(
+                    vb[hf] + (uint32_t)((4 * kq + r) * kRowCodeBytes + 4 * n16));
+        }
     }
     const int ph = (lane >> 4) & 1;
     T.par = *((lane < 32 ? (ph ? kp[1] : kp[0]) : (ph ? vp[1] : vp[0])) + (lane & 15));
@@ -300,7 +334,7 @@ struct WaveState {
             recentre();
     }
 
-    template <int F, bool EXT>
+    template <int F, bool EXT, int CB>
     __device__ __forceinline__ void consume(const Tile &T, int t0, int t_end, int lane, float kscale,
                                             const QOperand<F> &qop, ParLds &pl, int col_len,
                                             int mask_from)
@@ -343,7 +377,10 @@ struct WaveState {
         if constexpr (F == 1) {
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const u32x4 w = T.kc[hf];
+                u32x4 w = T.kc[hf];
+                if constexpr (CodeWidths<CB>::k2)
+                    w = u32x4{spread2(T.kc[hf].x & 0xFFFFu), spread2(T.kc[hf].x >> 16),
+                              spread2(T.kc[hf].y & 0xFFFFu), spread2(T.kc[hf].y >> 16)};
                 const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
                 const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
                 i32x4 dg[3];
@@ -472,12 +509,16 @@ struct WaveState {
         const f16x8 bl = __builtin_bit_cast(f16x8, blu);
 
         // ---- PV: A = V codes (rows: channel 8 n16 + b, k: the 8 tokens), B = weights -------
+        uint32_t vcode[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            vcode[j] = CodeWidths<CB>::v2 ? spread2(T.vc[j]) : T.vc[j];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             uint32_t src[4];   // byte k of tokens (2p, 2p + 1) in bits 0..7 and 16..23
 #pragma unroll
             for (int p = 0; p < 4; ++p)
-                src[p] = __builtin_amdgcn_perm(T.vc[2 * p + 1], T.vc[2 * p],
+                src[p] = __builtin_amdgcn_perm(vcode[2 * p + 1], vcode[2 * p],
                                                0x0C000C00u | ((4u + k) << 16) | (uint32_t)k);
             u32x4 lo, hi;
 #pragma unroll
@@ -511,24 +552,27 @@ __device__ __forceinline__ void write_new_rows(const DecodeArgs &a, int s, int h
     for (int j = 0; j < 4; ++j)
         bf16x8_to_f32(reinterpret_cast<const u32x4 *>(src)[j], x + 8 * j);
     if (!is_v) {
-        encode_row<BK>(x, slot, a.k_codes_w, a.k_params_w, a.num_slots, a.num_kv_heads,
-                       a.page_log2, h, ql);
+        encode_row<BK, true>(x, slot, a.k_codes_w, a.k_params_w, a.num_slots, a.num_kv_heads,
+                             a.page_log2, h, ql, a.k_bits);
         return;
     }
+    uint8_t *vc = a.v_codes_w;
+    uint32_t *vp = a.v_params_w;
     switch (a.v_block) {
-    case 16: encode_row<16>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
-    case 32: encode_row<32>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
-    case 64: encode_row<64>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
-    case 128: encode_row<128>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
-    default: encode_row<0>(x, slot, a.v_codes_w, a.v_params_w, a.num_slots, a.num_kv_heads, a.page_log2, h, ql); break;
+    case 16: encode_row<16, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
+    case 32: encode_row<32, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
+    case 64: encode_row<64, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
+    case 128: encode_row<128, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
+    default: encode_row<0, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
     }
 }
 
-template <int BK, int F, bool EXT>
+template <int BK, int F, bool EXT, int CB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? 4 : 2)))
 void decode_split_kernel(DecodeArgs a)
 {
     static_assert(!EXT || F == 1, "extend columns use the 16-column layout");
+    static_assert(CB == 0 || F == 1, "2-bit pools use the 16-column layout");
     const int h = blockIdx.y;
     const int G = a.group;
     // The MFMA columns: decode: the G query heads of sequence s (grid: split, KV head,
@@ -713,21 +757,21 @@ void decode_split_kernel(DecodeArgs a)
         // covers only that tile's loads.
         const int t_last = cb + (ce - 1 - cb) / kTile * kTile;
         Tile A, B;
-        load_tile<F>(A, a, pid, h, cb, ce, lane);
-        load_tile<F>(B, a, pid, h, min(cb + kTile, t_last), ce, lane);
+        load_tile<F, CB>(A, a, pid, h, cb, ce, lane);
+        load_tile<F, CB>(B, a, pid, h, min(cb + kTile, t_last), ce, lane);
         int t0 = cb;
         while (true) {
-            st.template consume<F, EXT>(A, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
+            st.template consume<F, EXT, CB>(A, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
             st.tick();
             if (t0 + kTile >= ce)
                 break;
-            load_tile<F>(A, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
+            load_tile<F, CB>(A, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
             t0 += kTile;
-            st.template consume<F, EXT>(B, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
+            st.template consume<F, EXT, CB>(B, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
             st.tick();
             if (t0 + kTile >= ce)
                 break;
-            load_tile<F>(B, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
+            load_tile<F, CB>(B, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
             t0 += kTile;
         }
     }
@@ -980,20 +1024,38 @@ __global__ __launch_bounds__(256) void decode_combine_wave_kernel(DecodeArgs a)
     *reinterpret_cast<float2 *>(out + 2 * lane) = make_float2(o0, o1);
 }
 
+template <int BK, bool EXT, int CB>
+void launch_f1(const DecodeArgs &a, const dim3 &grid, hipStream_t s)
+{
+    hipLaunchKernelGGL((decode_split_kernel<BK, 1, EXT, CB>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+}
+
+template <int BK, bool EXT>
+void launch_f1_widths(const DecodeArgs &a, const dim3 &grid, hipStream_t s)
+{
+    const int cb = (a.k_bits == 2 ? 1 : 0) | (a.v_bits == 2 ? 2 : 0);
+    switch (cb) {
+    case 1: launch_f1<BK, EXT, 1>(a, grid, s); break;
+    case 2: launch_f1<BK, EXT, 2>(a, grid, s); break;
+    case 3: launch_f1<BK, EXT, 3>(a, grid, s); break;
+    default: launch_f1<BK, EXT, 0>(a, grid, s); break;
+    }
+}
+
 template <int BK>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
 {
     if (a.qo_start != nullptr) {
         const dim3 grid((unsigned)(a.num_seqs * a.blocks_per_seq), (unsigned)a.num_kv_heads,
                         (unsigned)a.max_splits);
-        hipLaunchKernelGGL((decode_split_kernel<BK, 1, true>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+        launch_f1_widths<BK, true>(a, grid, s);
         return hipGetLastError();
     }
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    if (a.group <= 8)
-        hipLaunchKernelGGL((decode_split_kernel<BK, 2, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+    if (a.group <= 8 && a.k_bits != 2 && a.v_bits != 2)
+        hipLaunchKernelGGL((decode_split_kernel<BK, 2, false, 0>), grid, dim3(64 * kDecodeWaves), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_split_kernel<BK, 1, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+        launch_f1_widths<BK, false>(a, grid, s);
     return hipGetLastError();
 }
 

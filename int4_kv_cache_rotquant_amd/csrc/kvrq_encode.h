@@ -18,6 +18,7 @@ namespace kvrq {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // fp32 value of 1/sqrt(b), the rotation's normalisation.
 template <int B> struct InvSqrt;
@@ -85,12 +86,17 @@ __device__ __forceinline__ void rotate_row(float (&x)[32], int ql)
 }
 
 // Rotate, quantise and store one row held in x; called by all four lanes of the quad.
-template <int B>
+// bits = 4: 15 levels, two codes per byte, 64-byte rows; bits = 2: 3 levels, four codes
+// per byte (channel d at bit 2 (d % 4) of byte d / 4), 32-byte rows.  With NARROW false
+// only 4 bits are compiled (bits is ignored), so the INT4 kernels carry no 2-bit code.
+template <int B, bool NARROW = false>
 __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t *__restrict__ codes,
                                            uint32_t *__restrict__ params, int64_t num_slots,
-                                           int num_kv_heads, int page_log2, int h, int ql)
+                                           int num_kv_heads, int page_log2, int h, int ql,
+                                           int bits = 4)
 {
 #pragma clang fp contract(off)
+    const bool two = NARROW && bits == 2;
     rotate_row<B>(x, ql);
 
     float mn = x[0], mx = x[0];
@@ -106,12 +112,51 @@ __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t
     mn = mn + 0.0f;  // a zero minimum is stored as +0
     mx = mx + 0.0f;
 
-    const float scale32 = (mx - mn) / 15.0f;
+    const float levels = two ? 3.0f : 15.0f;
+    const float scale32 = (mx - mn) / levels;
     const _Float16 s16 = (_Float16)scale32;
     const _Float16 z16 = (_Float16)mn;
     const uint32_t s_bits = __builtin_bit_cast(uint16_t, s16);
     const uint32_t z_bits = __builtin_bit_cast(uint16_t, z16);
 
+    const bool store = slot >= 0 && slot < num_slots;
+    const int64_t page = slot >> page_log2;
+    const int64_t off = slot & ((1 << page_log2) - 1);
+    const int64_t cell = ((page * num_kv_heads + h) << page_log2) + off;
+    if (two) {
+        uint32_t out[2] = {0u, 0u};
+        if (s_bits != 0u) {
+            const float zf = (float)z16;
+            const float inv = 1.0f / (float)s16;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                uint32_t byte[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    uint32_t acc = 0u;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = (x[16 * k + 4 * m + e] - zf) * inv;
+                        // clamp to [0, 3], then round half to even as for 4 bits; the
+                        // integer sits in bits 0..1, bits 2..21 are zero
+                        const float c = __builtin_amdgcn_fmed3f(v, 0.0f, 3.0f) + 12582912.0f;
+                        acc |= __float_as_uint(c) << (2 * e);
+                    }
+                    byte[m] = acc;
+                }
+                const uint32_t lo = __builtin_amdgcn_perm(byte[1], byte[0], 0x0C0C0400u);
+                const uint32_t hi = __builtin_amdgcn_perm(byte[3], byte[2], 0x0C0C0400u);
+                out[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            }
+        }
+        if (store) {
+            u32x2 *dst = reinterpret_cast<u32x2 *>(codes + cell * (kRowCodeBytes / 2)) + ql;
+            *dst = u32x2{out[0], out[1]};
+            if (ql == 0)
+                params[cell] = s_bits | (z_bits << 16);
+        }
+        return;
+    }
     uint32_t out[4] = {0u, 0u, 0u, 0u};
     if (s_bits != 0u) {
         const float zf = (float)z16;
@@ -121,26 +166,23 @@ __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t
             uint32_t pair[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                uint32_t bits[2];
+                uint32_t bits2[2];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const float v = (x[8 * k + 2 * m + e] - zf) * inv;
                     // clamp to [0, 15], then round half to even: adding 1.5 * 2^23 leaves
                     // the nearest integer in the low mantissa bits
                     const float c = __builtin_amdgcn_fmed3f(v, 0.0f, 15.0f) + 12582912.0f;
-                    bits[e] = __float_as_uint(c);
+                    bits2[e] = __float_as_uint(c);
                 }
-                pair[m] = (bits[1] << 4) | bits[0];  // low byte = code(2m) | code(2m+1) << 4
+                pair[m] = (bits2[1] << 4) | bits2[0];  // low byte = code(2m) | code(2m+1) << 4
             }
             const uint32_t lo = __builtin_amdgcn_perm(pair[1], pair[0], 0x0C0C0400u);
             const uint32_t hi = __builtin_amdgcn_perm(pair[3], pair[2], 0x0C0C0400u);
             out[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
         }
     }
-    if (slot >= 0 && slot < num_slots) {
-        const int64_t page = slot >> page_log2;
-        const int64_t off = slot & ((1 << page_log2) - 1);
-        const int64_t cell = ((page * num_kv_heads + h) << page_log2) + off;
+    if (store) {
         u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + ql;
         *dst = u32x4{out[0], out[1], out[2], out[3]};
         if (ql == 0)

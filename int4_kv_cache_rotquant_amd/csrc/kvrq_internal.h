@@ -9,7 +9,7 @@
 namespace kvrq {
 
 constexpr int kHeadDim = 128;       // channels per head
-constexpr int kRowCodeBytes = 64;   // packed INT4 bytes per (token, head) row
+constexpr int kRowCodeBytes = 64;   // packed INT4 bytes per (token, head) row (2-bit: 32)
 constexpr int kTile = 32;           // decode tokens per inner step
 constexpr int kWriteTile = 16;      // write tokens per wave step (four lanes per row)
 constexpr int kWriteWavesPerSimd = 5;  // occupancy target (the kernel fits six)
@@ -31,6 +31,8 @@ struct WriteArgs {
     int64_t num_slots;          // num_pages * page_size; slots at or above are skipped
     int32_t num_kv_heads;
     int32_t page_log2;
+    int32_t k_bits = 4;         // code widths of the pools: 4, or 2 (32-byte rows)
+    int32_t v_bits = 4;
 };
 
 struct CopyArgs {
@@ -93,6 +95,10 @@ struct DecodeArgs {
     uint32_t *v_params_w = nullptr;
     int64_t num_slots = 0;               // num_pages * page_size
     int32_t v_block = 0;
+    // code widths of the two pools: 4, or 2 (32-byte rows; the kernels that read them
+    // use the 16-column layout)
+    int32_t k_bits = 4;
+    int32_t v_bits = 4;
 };
 
 // Returns a hipError_t value (0 = success).

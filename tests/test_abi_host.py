@@ -203,10 +203,16 @@ def test_status_strings(K):
 
 
 def test_cache_sizes(K):
-    cb, pb = K.kvrq_cache_sizes(_desc(K))
-    assert cb == 64 * 8 * 16 * 64 and pb == 64 * 8 * 16 * 4
+    kb, vb, pb = K.kvrq_cache_sizes(_desc(K))
+    assert kb == vb == 64 * 8 * 16 * 64 and pb == 64 * 8 * 16 * 4
     # the footprint the pages call "a quarter of the space": 68 B vs 256 B per token-head
-    assert (cb + pb) / (64 * 8 * 16) == 68
+    assert (kb + pb) / (64 * 8 * 16) == 68
+    # 2-bit pools: 32-byte rows (mixed widths allowed)
+    kb, vb, pb = K.kvrq_cache_sizes(_desc(K, k_bits=4, v_bits=2))
+    assert kb == 64 * 8 * 16 * 64 and vb == 64 * 8 * 16 * 32
+    with pytest.raises(K.KvrqError) as e:
+        K.kvrq_cache_sizes(_desc(K, k_bits=3))
+    assert e.value.status == K.KVRQ_EUNSUPPORTED
 
 
 def test_pool_identity_order_and_slots(K):
