@@ -54,7 +54,6 @@ HBM_PEAK_GBPS = 8000.0
 # attention at MFMA peak: half the flops on int8 (5.0 POP/s dense), half on f16 (2.5 PFLOP/s)
 MFMA_ATTENTION_PEAK_TFLOPS = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
 D = 128
-CODE_ROW = 64 + 4            # bytes per (token, head) row in the INT4 cache
 
 
 def parse_args(argv=None):
@@ -67,6 +66,8 @@ def parse_args(argv=None):
                     help="prefill_chunk: fused BDR write, plain INT4 write, or bf16 paged copy; "
                          "qwen3_32b_like_decode: fused = write + decode in one call")
     ap.add_argument("--k-block", type=int, default=None, help="override the workload's K block")
+    ap.add_argument("--k-bits", type=int, default=4, choices=[4, 2], help="K code width")
+    ap.add_argument("--v-bits", type=int, default=4, choices=[4, 2], help="V code width")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
@@ -179,12 +180,20 @@ class Setup:
     def dev_i32(self, a):
         return self.torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(self.dev)
 
+    def kv_row_bytes(self):
+        """Cache bytes of one (token, head) K row plus V row: codes and (scale, zero)."""
+        return D * (self.args.k_bits + self.args.v_bits) // 8 + 2 * 4
+
+    def new_cache(self, num_pages, Hkv, P, kb, vb):
+        return self.K.PagedInt4Cache(num_pages, Hkv, P, kb, vb, k_bits=self.args.k_bits,
+                                     v_bits=self.args.v_bits)
+
     def write_bytes(self, T, Hkv):
-        return T * (Hkv * 2 * (2 * D + CODE_ROW) + 4)
+        return T * (Hkv * (2 * 2 * D + self.kv_row_bytes()) + 4)
 
     def decode_bytes(self, lens, Hkv, Hq, P):
         lens = np.asarray(lens, np.int64)
-        return int(lens.sum() * Hkv * 2 * CODE_ROW + len(lens) * Hq * (2 * D + 4 * D)
+        return int(lens.sum() * Hkv * self.kv_row_bytes() + len(lens) * Hq * (2 * D + 4 * D)
                    + np.ceil(lens / P).sum() * 4 + len(lens) * 4)
 
     # -- qwen3_4b_like: write everything, decode every sequence; 3 rotating buffer sets
@@ -195,7 +204,7 @@ class Setup:
         T, Hkv, Hq = w.total_tokens, w.num_kv_heads, w.num_q_heads
         self.sets = []
         for i in range(3):
-            cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, w.page_size, kb, w.v_block)
+            cache = self.new_cache(w.paging.num_pages, Hkv, w.page_size, kb, w.v_block)
             k, v = self.rows(T, Hkv, w.k_out), self.rows(T, Hkv, w.v_out)
             q = torch.randn((w.num_seqs, Hq, D), generator=self.gen, device=self.dev).to(torch.bfloat16)
             self.sets.append((cache, k, v, q))
@@ -242,7 +251,7 @@ class Setup:
                 cache = (torch.empty(shape, dtype=torch.bfloat16, device=self.dev),
                          torch.empty(shape, dtype=torch.bfloat16, device=self.dev))
             else:
-                cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, w.page_size, kb, 0)
+                cache = self.new_cache(w.paging.num_pages, Hkv, w.page_size, kb, 0)
             self.sets.append((cache, k, v))
         self.slots = self.dev_i32(w.all_slots())
         self.desc = K.CacheDesc(D, Hkv, w.page_size, w.paging.num_pages, 0, 0)
@@ -269,7 +278,7 @@ class Setup:
         kb = self.args.k_block if self.args.k_block is not None else w.k_block
         self.kb, self.vb = kb, w.v_block
         S, Hkv, Hq, P = w.num_seqs, w.num_kv_heads, w.num_q_heads, w.page_size
-        self.cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, kb, w.v_block)
+        self.cache = self.new_cache(w.paging.num_pages, Hkv, P, kb, w.v_block)
         chunk = 1 << 16
         all_slots = w.all_slots()
         for s0 in range(0, len(all_slots), chunk):
@@ -333,7 +342,7 @@ class Setup:
         Hkv, Hq, P, C = w.num_kv_heads, w.num_q_heads, w.page_size, w.notes["chunk"]
         self.kb, self.vb = w.k_block, w.v_block
         L = w.total_tokens
-        self.cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, w.k_block, w.v_block)
+        self.cache = self.new_cache(w.paging.num_pages, Hkv, P, w.k_block, w.v_block)
         self.chunks_k = [self.rows(C, Hkv, w.k_out) for _ in range(4)]
         self.chunks_v = [self.rows(C, Hkv, w.v_out) for _ in range(4)]
         self.chunk_slots = [self.dev_i32(w.paging.slots(0, c * C, C)) for c in range(L // C)]
@@ -369,7 +378,7 @@ class Setup:
         self.kb, self.vb = kb, w.v_block
         S, Hkv, Hq, P = w.num_seqs, w.num_kv_heads, w.num_q_heads, w.page_size
         C, prefix = w.notes["chunk"], w.notes["prefix"]
-        self.cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, kb, w.v_block)
+        self.cache = self.new_cache(w.paging.num_pages, Hkv, P, kb, w.v_block)
         pre = np.concatenate([w.paging.slots(s, 0, int(L)) for s, L in enumerate(prefix)])
         for s0 in range(0, len(pre), 1 << 16):
             sl = pre[s0:s0 + (1 << 16)]
@@ -391,7 +400,7 @@ class Setup:
         # attended (row, key) pairs: row i of a chunk at position prefix + i sees prefix + i + 1
         pairs = int(sum(C * int(L) + C * (C + 1) // 2 for L in prefix))
         self.kernels = {"kv_rotquant_write": self.write_bytes(T, Hkv),
-                        "kv_int4_paged_extend": int(w.seq_lens.sum() * Hkv * 2 * CODE_ROW
+                        "kv_int4_paged_extend": int(w.seq_lens.sum() * Hkv * self.kv_row_bytes()
                                                     + T * Hq * (2 * D + 4 * D)
                                                     + np.ceil(w.seq_lens / P).sum() * 4)}
         # QK^T and PV: 2 D flops each per (row, head, key)
@@ -474,7 +483,8 @@ def cpu_baseline(args):
     decode = args.workload != "prefill_chunk"
     reps, t_total, tokens = 0, 0.0, 0
     while t_total < args.cpu_seconds and reps < 1000:
-        cache = oracle.Cache(paging.num_pages, w.num_kv_heads, w.page_size)
+        cache = oracle.Cache(paging.num_pages, w.num_kv_heads, w.page_size, k_bits=args.k_bits,
+                             v_bits=args.v_bits)
         t0 = time.perf_counter()
         oracle.write(cache, k, v, slots, kb, w.v_block)
         if decode:
@@ -503,7 +513,8 @@ def cpu_baseline_extend(args, w, kb, rng, cores):
     q = W.f32_to_bf16_bits(rng.standard_normal((C, w.num_q_heads, D)).astype(np.float32))
     tab = paging.page_table()
     qo = np.array([0, C], np.int32)
-    cache = oracle.Cache(paging.num_pages, w.num_kv_heads, w.page_size)
+    cache = oracle.Cache(paging.num_pages, w.num_kv_heads, w.page_size, k_bits=args.k_bits,
+                         v_bits=args.v_bits)
     oracle.write(cache, k[:prefix], v[:prefix], slots[:prefix], kb, w.v_block)   # untimed prefix
     reps, t_total = 0, 0.0
     while t_total < args.cpu_seconds and reps < 1000:
@@ -683,7 +694,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 in, fp32 compute, int4+fp16 cache",
         "data": "synthetic (seeded N(0,1) with outlier channels; no model weights)",
-        "config": s.config,
+        "config": dict(s.config, **({"k_bits": args.k_bits, "v_bits": args.v_bits}
+                                    if (args.k_bits, args.v_bits) != (4, 4) else {})),
         "kernels": per_kernel,
         "roofline": roofline,
         "hbm_gbps_step": round(sum(per_kernel[n]["algorithmic_bytes"] * per_kernel[n]["launches_per_step"]

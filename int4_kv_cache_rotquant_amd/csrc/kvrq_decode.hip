@@ -184,9 +184,11 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const f16x8 &a, const f16x8 &b, co
 //   vc[j]   code dword n16 (channels 8 n16 .. 8 n16 + 7) of token 16 (j / 4) + 4 kq + j % 4
 //   par     lanes 0..31: (scale, zero) of K of token lane; lanes 32..63: V of token
 //           lane - 32; converted and shared through LDS when the tile is consumed
-// 2-bit pools (CB bit 0: K, bit 1: V; the 16-column layout only) load half the bytes:
-//   kc[j].xy  8 code bytes of token 16 j + n16, bytes [8 kq, 8 kq + 8) (channels
+// 2-bit pools (CB bit 0: K, bit 1: V) load half the bytes:
+//   kc[j].xy  F = 1: 8 code bytes of token 16 j + n16, bytes [8 kq, 8 kq + 8) (channels
 //             32 kq .. 32 kq + 31 as for 4 bits)
+//   kc[0]     F = 2: 16 code bytes of token n16 + 16 (kq / 2), bytes 16 (kq % 2) + [0, 16)
+//             (channels 64 (kq % 2) .. + 63 as for 4 bits)
 //   vc[j]     the 16-bit code word n16 (channels 8 n16 .. 8 n16 + 7)
 // and widen them to the 4-bit layout when the tile is consumed (spread2), so the rest of
 // the pipeline is the same: a 2-bit code is a 4-bit code below 4 with the same meaning.
@@ -254,13 +256,17 @@ __device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const Pa
         kp[hf] = a.k_params + cell0;
         vp[hf] = a.v_params + cell0;
     }
-    if constexpr (CW::k2) {
+    if constexpr (CW::k2 && F == 1) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const u32x2 w = *reinterpret_cast<const u32x2 *>(kb[hf] + n16 * CW::k_row + 8 * kq);
             T.kc[hf].x = w.x;
             T.kc[hf].y = w.y;
         }
+    } else if constexpr (CW::k2) {
+        // the 64 channels of the F = 2 layout: 16 bytes, widened to kc[0], kc[1] on consume
+        T.kc[0] = *reinterpret_cast<const u32x4 *>((kq >> 1 ? kb[1] : kb[0]) + n16 * CW::k_row +
+                                                   16 * (kq & 1));
     } else if constexpr (F == 1) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -397,7 +403,12 @@ struct WaveState {
             i32x4 dg[3] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const u32x4 w = T.kc[j];
+                u32x4 w = T.kc[j];
+                if constexpr (CodeWidths<CB>::k2) {
+                    const uint32_t d0 = j ? T.kc[0].z : T.kc[0].x, d1 = j ? T.kc[0].w : T.kc[0].y;
+                    w = u32x4{spread2(d0 & 0xFFFFu), spread2(d0 >> 16), spread2(d1 & 0xFFFFu),
+                              spread2(d1 >> 16)};
+                }
                 const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
                 const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
 #pragma unroll
@@ -572,7 +583,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? 4 
 void decode_split_kernel(DecodeArgs a)
 {
     static_assert(!EXT || F == 1, "extend columns use the 16-column layout");
-    static_assert(CB == 0 || F == 1, "2-bit pools use the 16-column layout");
     const int h = blockIdx.y;
     const int G = a.group;
     // The MFMA columns: decode: the G query heads of sequence s (grid: split, KV head,
@@ -1052,10 +1062,18 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
         return hipGetLastError();
     }
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
-    if (a.group <= 8 && a.k_bits != 2 && a.v_bits != 2)
-        hipLaunchKernelGGL((decode_split_kernel<BK, 2, false, 0>), grid, dim3(64 * kDecodeWaves), 0, s, a);
-    else
+    const int cb = (a.k_bits == 2 ? 1 : 0) | (a.v_bits == 2 ? 2 : 0);
+    const dim3 block(64 * kDecodeWaves);
+    if (a.group > 8)
         launch_f1_widths<BK, false>(a, grid, s);
+    else if (cb == 1)
+        hipLaunchKernelGGL((decode_split_kernel<BK, 2, false, 1>), grid, block, 0, s, a);
+    else if (cb == 2)
+        hipLaunchKernelGGL((decode_split_kernel<BK, 2, false, 2>), grid, block, 0, s, a);
+    else if (cb == 3)
+        hipLaunchKernelGGL((decode_split_kernel<BK, 2, false, 3>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<BK, 2, false, 0>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 

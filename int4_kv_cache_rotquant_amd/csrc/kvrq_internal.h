@@ -95,8 +95,8 @@ struct DecodeArgs {
     uint32_t *v_params_w = nullptr;
     int64_t num_slots = 0;               // num_pages * page_size
     int32_t v_block = 0;
-    // code widths of the two pools: 4, or 2 (32-byte rows; the kernels that read them
-    // use the 16-column layout)
+    // code widths of the two pools: 4, or 2 (32-byte rows, widened to the 4-bit layout
+    // in registers)
     int32_t k_bits = 4;
     int32_t v_bits = 4;
 };

@@ -4,7 +4,9 @@
 SAW-INT4 reports that naive token-wise INT4 breaks down on keys with outlier channels,
 that block-diagonal Hadamard rotation (BDR) recovers the accuracy, that rotating K alone
 is the better trade-off, and that a 128 block balances accuracy and speed (wispaper.ai
-blog, sections 2 and 4: the core intuition and the ablation bullets).  This harness
+blog, sections 2 and 4: the core intuition and the ablation bullets).  It leaves open
+whether the rotation keeps 2-bit codes accurate, perhaps with mixed widths (section 5,
+limitations); the 2-bit rows measure that too.  This harness
 measures the same directions without models: for each (K block, V block, outlier
 strength) it writes one seeded synthetic K/V set through ``kv_rotquant_write``, decodes
 one query per sequence and query head with ``kv_int4_paged_decode``, and compares the
@@ -33,14 +35,21 @@ import workloads as W  # noqa: E402
 
 D = 128
 
-# (label, K block, V block)
+# (label, K block, V block, K bits, V bits)
 ROTATIONS = [
-    ("plain INT4", 0, 0),
-    ("BDR-16 K", 16, 0),
-    ("BDR-32 K", 32, 0),
-    ("BDR-64 K", 64, 0),
-    ("BDR-128 K", 128, 0),
-    ("BDR-128 K+V", 128, 128),
+    ("plain INT4", 0, 0, 4, 4),
+    ("BDR-16 K", 16, 0, 4, 4),
+    ("BDR-32 K", 32, 0, 4, 4),
+    ("BDR-64 K", 64, 0, 4, 4),
+    ("BDR-128 K", 128, 0, 4, 4),
+    ("BDR-128 K+V", 128, 128, 4, 4),
+    # the pages' open question (wispaper.ai blog, section 5, limitations): does the
+    # rotation keep 2 bits accurate, and does mixing widths help?
+    ("plain 2-bit", 0, 0, 2, 2),
+    ("BDR-128 K+V 2-bit", 128, 128, 2, 2),
+    ("BDR-128 K 4-bit, V 2-bit", 128, 0, 4, 2),
+    ("BDR-128 K+V, K 4-bit, V 2-bit", 128, 128, 4, 2),
+    ("BDR-128 K 2-bit, V 4-bit", 128, 0, 2, 4),
 ]
 
 # (label, outlier fraction, low factor, high factor); fraction 0 = none
@@ -98,14 +107,15 @@ def run(args):
                                   sm_scale)
         k_dev = torch.from_numpy(k_bits.view(np.int16)).cuda().view(torch.bfloat16)
         v_dev = torch.from_numpy(v_bits.view(np.int16)).cuda().view(torch.bfloat16)
-        for r_label, kb, vb in ROTATIONS:
-            cache = K.PagedInt4Cache(paging.num_pages, Hkv, P, kb, vb)
+        for r_label, kb, vb, kbits, vbits in ROTATIONS:
+            cache = K.PagedInt4Cache(paging.num_pages, Hkv, P, kb, vb, k_bits=kbits, v_bits=vbits)
             K.kv_rotquant_write(cache, k_dev, v_dev, slots)
             out = K.kv_int4_paged_decode(cache, q_dev, tab, lens_dev, L).double().cpu().numpy()
             num = np.linalg.norm(out - ref, axis=-1)
             den = np.linalg.norm(ref, axis=-1)
             rel = num / den
             row = {"outliers": o_label, "rotation": r_label, "k_block": kb, "v_block": vb,
+                   "k_bits": kbits, "v_bits": vbits,
                    "mean_rel_err": float(rel.mean()), "max_rel_err": float(rel.max()),
                    "max_abs_err": float(np.abs(out - ref).max())}
             rows.append(row)

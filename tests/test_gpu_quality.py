@@ -26,3 +26,7 @@ def test_quality_ablation_direction():
         assert err[(outl, "BDR-128 K")] < err[(outl, "plain INT4")], err
     # without outliers INT4 is already accurate; rotation must not make it much worse
     assert err[("none", "BDR-128 K")] < 2 * err[("none", "plain INT4")] + 1e-3, err
+    # 2 bits: coarser than 4 bits everywhere, and the rotation still helps on outlier keys
+    for outl in ("none", "2% x U(10,30)"):
+        assert err[(outl, "BDR-128 K+V 2-bit")] > err[(outl, "BDR-128 K+V")], err
+    assert err[("2% x U(10,30)", "BDR-128 K+V 2-bit")] < err[("2% x U(10,30)", "plain 2-bit")], err
