@@ -128,13 +128,6 @@ __device__ __forceinline__ float col_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
-    return r;
-}
-
 // V codes become f16 MFMA operands without arithmetic: a nibble moved into mantissa bits
 // 6..9 under the exponent of 1.0 is the exact f16 value 1 + code / 16 (a high nibble left
 // in bits 4..7: 1 + code / 64).  The accumulators are re-centred every kRecentre tiles by
@@ -144,7 +137,6 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c)
 // + sum_t p_t z_t + 8 sum_t p_t s_t.
 constexpr int kRecentre = 8;
 constexpr uint32_t kOne2 = 0x3C003C00u;     // f16x2 {1, 1}
-constexpr uint32_t kMant69 = 0x03C003C0u;   // mantissa bits 6..9 of both halves
 constexpr uint32_t kMant47 = 0x00F000F0u;   // mantissa bits 4..7 of both halves
 
 // K codes become int8 MFMA operands: the even and the odd nibbles of a dword, masked in
@@ -520,6 +512,12 @@ struct WaveState {
         const f16x8 bl = __builtin_bit_cast(f16x8, blu);
 
         // ---- PV: A = V codes (rows: channel 8 n16 + b, k: the 8 tokens), B = weights -------
+        // the high-nibble mask in a scalar register, opaque to constant folding, so that
+        // (x & mask) | one is a single v_and_or_b32 (both constants as literals would not
+        // fit one instruction and would cost an and and an or)
+        uint32_t mant47, one2;
+        asm("" : "=s"(mant47) : "0"(kMant47));
+        asm("" : "=v"(one2) : "0"(kOne2));
         uint32_t vcode[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -534,8 +532,11 @@ struct WaveState {
             u32x4 lo, hi;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                lo[p] = and_or(src[p] << 6, kMant69, kOne2);
-                hi[p] = and_or(src[p], kMant47, kOne2);
+                // the low nibble lands in mantissa bits 6..9; the high nibble lands in
+                // bits 10..13, which the exponent of 1.0 sets anyway, and bits 14..15
+                // receive the zero byte above it
+                lo[p] = (src[p] << 6) | one2;
+                hi[p] = (src[p] & mant47) | one2;
             }
             const f16x8 al = __builtin_bit_cast(f16x8, lo);
             const f16x8 ah = __builtin_bit_cast(f16x8, hi);
