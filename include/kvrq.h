@@ -189,7 +189,9 @@ KVRQ_API kvrq_status kv_rotquant_write(const kvrq_cache_desc *d, const kvrq_cach
 
 /* Workspace bytes kv_int4_paged_decode needs for num_seqs sequences of at
  * most max_seq_len tokens with num_q_heads query heads and the given
- * split_tokens (0 = automatic, as in the decode call). */
+ * split_tokens (0 = automatic, as in the decode call).  0 when a single split
+ * covers max_seq_len: the split kernel then writes the output itself and the
+ * workspace may be NULL. */
 KVRQ_API kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, int32_t num_seqs,
                                            int32_t num_q_heads, int32_t max_seq_len,
                                            int32_t split_tokens, size_t *bytes);
@@ -210,11 +212,13 @@ KVRQ_API kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, in
  *                   waves); 0 = automatic, otherwise a multiple of 128
  *   out             device fp32 [num_seqs][num_q_heads][head_dim]
  *   workspace       device scratch of workspace_bytes >= the size reported by
- *                   kv_int4_paged_decode_workspace (16-byte aligned)
+ *                   kv_int4_paged_decode_workspace (16-byte aligned; unused,
+ *                   and may be NULL, when that size is 0)
  * Computes, per sequence s and query head g (KV head h):
  *   q' = H_bK q,  score_t = sm_scale * q'.(code_t * scale_t + zero_t),
  *   o' = sum_t softmax(score)_t (V code_t * scale_t + zero_t),  out = H_bV o'.
- * Two launches on `stream` (split-K partials, then the combine). */
+ * Two launches on `stream` (split-K partials, then the combine), or one when a
+ * single split covers max_seq_len. */
 KVRQ_API kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
                                  const void *q, int32_t num_seqs, int32_t num_q_heads,
                                  const int32_t *page_table, int32_t max_pages_per_seq,
@@ -256,7 +260,8 @@ KVRQ_API kvrq_status kv_int4_paged_decode_step(const kvrq_cache_desc *d, const k
                                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes kv_int4_paged_extend needs (arguments as in that call;
- * split_tokens 0 = automatic). */
+ * split_tokens 0 = automatic); 0, and the workspace may be NULL, when the
+ * key range is not split (the usual case for chunks of many rows). */
 KVRQ_API kvrq_status kv_int4_paged_extend_workspace(const kvrq_cache_desc *d, int32_t num_seqs,
                                                     int32_t num_q_heads, int32_t total_q,
                                                     int32_t max_q_len, int32_t max_seq_len,

@@ -139,8 +139,11 @@ kvrq::DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max
     return p;
 }
 
+// Split partials; none when a single split writes the output itself.
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const kvrq::DecodePlan &p)
 {
+    if (p.max_splits == 1)
+        return 0;
     const size_t rows = size_t(num_seqs) * num_q_heads * p.max_splits;
     return rows * (kvrq::kHeadDim + 2) * sizeof(float);
 }
@@ -494,10 +497,10 @@ kvrq_status decode_impl(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, c
         return fail(KVRQ_EINVAL, "sm_scale must be finite");
     const kvrq::DecodePlan plan = plan_decode(num_seqs, d->num_kv_heads, max_seq_len, split_tokens);
     const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, plan);
-    if (!workspace || workspace_bytes < need)
+    if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(KVRQ_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : size_t(0));
-    if (!aligned(workspace, 16))
+    if (need > 0 && !aligned(workspace, 16))
         return fail(KVRQ_EINVAL, "workspace must be 16-byte aligned");
     if (plan.max_splits > 65535 * 64)
         return fail(KVRQ_EUNSUPPORTED, "too many splits");
@@ -524,6 +527,7 @@ kvrq_status decode_impl(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, c
     a.max_pages = max_pages_per_seq;
     a.k_bits = code_bits(d->k_bits);
     a.v_bits = code_bits(d->v_bits);
+    a.v_block = d->v_block;
     a.split_tokens = plan.split_tokens;
     a.max_splits = plan.max_splits;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(d->head_dim));
@@ -627,10 +631,10 @@ KVRQ_API kvrq_status kv_int4_paged_extend(const kvrq_cache_desc *d, const kvrq_c
     const kvrq::DecodePlan plan = plan_extend(num_seqs, d->num_kv_heads, group, max_q_len,
                                               max_seq_len, split_tokens);
     const size_t need = decode_workspace_bytes(total_q, num_q_heads, plan);
-    if (!workspace || workspace_bytes < need)
+    if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(KVRQ_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : size_t(0));
-    if (!aligned(workspace, 16))
+    if (need > 0 && !aligned(workspace, 16))
         return fail(KVRQ_EINVAL, "workspace must be 16-byte aligned");
     if (plan.max_splits > 65535)
         return fail(KVRQ_EUNSUPPORTED, "too many splits");
@@ -657,6 +661,7 @@ KVRQ_API kvrq_status kv_int4_paged_extend(const kvrq_cache_desc *d, const kvrq_c
     a.max_pages = max_pages_per_seq;
     a.k_bits = code_bits(d->k_bits);
     a.v_bits = code_bits(d->v_bits);
+    a.v_block = d->v_block;
     a.split_tokens = plan.split_tokens;
     a.max_splits = plan.max_splits;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(d->head_dim));

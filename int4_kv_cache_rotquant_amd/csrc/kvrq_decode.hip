@@ -548,6 +548,40 @@ struct WaveState {
     }
 };
 
+// Inverse V rotation of one output row held as channels (2 lane, 2 lane + 1) by the
+// 64 lanes of a wave: width 1 in-lane, widths 2.. across lanes.
+template <int BV>
+__device__ __forceinline__ void inverse_rotate_pair(float &o0, float &o1, int lane)
+{
+    if constexpr (BV > 1) {
+        const float u = o0 + o1, w = o0 - o1;
+        o0 = u;
+        o1 = w;
+#pragma unroll
+        for (int hw = 2; hw < BV; hw <<= 1) {
+            const int m = hw >> 1;
+            const float p0 = wave_xor(o0, m), p1 = wave_xor(o1, m);
+            const bool upper = lane & m;
+            o0 = upper ? p0 - o0 : o0 + p0;
+            o1 = upper ? p1 - o1 : o1 + p1;
+        }
+        o0 *= InvSqrtF<BV>::value;
+        o1 *= InvSqrtF<BV>::value;
+    }
+}
+
+// The inverse V rotation for a block size known only at run time (uniform branch).
+__device__ __forceinline__ void inverse_rotate_pair_rt(float &o0, float &o1, int lane, int bv)
+{
+    switch (bv) {
+    case 16: inverse_rotate_pair<16>(o0, o1, lane); break;
+    case 32: inverse_rotate_pair<32>(o0, o1, lane); break;
+    case 64: inverse_rotate_pair<64>(o0, o1, lane); break;
+    case 128: inverse_rotate_pair<128>(o0, o1, lane); break;
+    default: break;
+    }
+}
+
 // Fused decode step: lanes 0-3 encode the new K row of (sequence s, KV head h) and lanes
 // 4-7 its V row, exactly as the write kernel does, into the slot given for it.
 template <int BK>
@@ -611,8 +645,16 @@ void decode_split_kernel(DecodeArgs a)
         ncols = G;
     }
     const int wg_begin = split * a.split_tokens;
-    if (wg_begin >= L)
+    if (wg_begin >= L) {
+        // a single split writes the output itself: an empty sequence gets zero rows
+        if (a.max_splits == 1 && !EXT) {
+            float4 *o = reinterpret_cast<float4 *>(
+                a.out + ((int64_t)s * a.num_q_heads + (int64_t)h * G) * kHeadDim);
+            for (int i = threadIdx.x; i < G * kHeadDim / 4; i += blockDim.x)
+                o[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
         return;
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // the wave index, and with it the token range, is uniform across the wave: keep it
@@ -828,6 +870,33 @@ void decode_split_kernel(DecodeArgs a)
         }
     }
     __syncthreads();
+    if (a.max_splits == 1) {
+        // the only split: merge the waves, normalise, undo the V rotation and write the
+        // output rows here (no combine launch); wave w takes columns w, w + 4, ...,
+        // lane l channels 2 l and 2 l + 1
+        for (int g = wave; g < ncols; g += kDecodeWaves) {
+            float M = lds_m[0][g];
+#pragma unroll
+            for (int w = 1; w < kDecodeWaves; ++w)
+                M = fmaxf(M, lds_m[w][g]);
+            float o0 = 0.0f, o1 = 0.0f, lsum = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kDecodeWaves; ++w) {
+                const float f = __builtin_amdgcn_exp2f(lds_m[w][g] - M);
+                o0 += f * lds_o[w][g][2 * lane];
+                o1 += f * lds_o[w][g][2 * lane + 1];
+                lsum += f * lds_l[w][g];
+            }
+            const float inv_l = 1.0f / lsum;
+            o0 *= inv_l;
+            o1 *= inv_l;
+            inverse_rotate_pair_rt(o0, o1, lane, a.v_block);
+            const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
+                                     : (int64_t)s * a.num_q_heads + h * G + g;
+            *reinterpret_cast<float2 *>(a.out + qrow * kHeadDim + 2 * lane) = make_float2(o0, o1);
+        }
+        return;
+    }
     for (int i = tid; i < ncols * kHeadDim; i += 64 * kDecodeWaves) {
         const int g = i >> 7, d = i & (kHeadDim - 1);
         float M = lds_m[0][g];
@@ -869,28 +938,6 @@ __device__ __forceinline__ int row_length(const DecodeArgs &a, int r)
     }
     const int n = a.qo_start[lo + 1] - a.qo_start[lo];
     return min(a.seq_lens[lo], a.max_seq_len) - n + (r - a.qo_start[lo]) + 1;
-}
-
-// Inverse V rotation of one output row held as channels (2 lane, 2 lane + 1) by the
-// 64 lanes of a wave: width 1 in-lane, widths 2.. across lanes.
-template <int BV>
-__device__ __forceinline__ void inverse_rotate_pair(float &o0, float &o1, int lane)
-{
-    if constexpr (BV > 1) {
-        const float u = o0 + o1, w = o0 - o1;
-        o0 = u;
-        o1 = w;
-#pragma unroll
-        for (int hw = 2; hw < BV; hw <<= 1) {
-            const int m = hw >> 1;
-            const float p0 = wave_xor(o0, m), p1 = wave_xor(o1, m);
-            const bool upper = lane & m;
-            o0 = upper ? p0 - o0 : o0 + p0;
-            o1 = upper ? p1 - o1 : o1 + p1;
-        }
-        o0 *= InvSqrtF<BV>::value;
-        o1 *= InvSqrtF<BV>::value;
-    }
 }
 
 // ---- a10: combine the splits of one (sequence, query head), undo the V rotation ---------
@@ -1107,7 +1154,7 @@ int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream)
     case 128: e = launch_split<128>(a, s); break;
     default: return hipErrorInvalidValue;
     }
-    if (e != hipSuccess)
+    if (e != hipSuccess || a.max_splits == 1)   // one split writes the output itself
         return e;
     switch (v_block) {
     case 0: return launch_combine<0>(a, s);

@@ -240,3 +240,21 @@ def test_long_context_one_kv_head(K):
     ref = _ref(orc, q[:, :8].copy(), tab, lens, 1, P, 128, 128)
     decode_compare(out[:, :8], ref, "long_context_h0")
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("G,vb", [(4, 128), (16, 0), (8, 32)])
+def test_single_split_writes_the_output(K, G, vb):
+    """One split covering every sequence: the split kernel merges, normalises, rotates V
+    back and writes the rows itself (no combine, no workspace); an empty sequence gets
+    zero rows.  The output buffer starts as NaN so a row left unwritten fails."""
+    import torch
+    lens = [0, 5, 100, 128]
+    Hkv = 2
+    cache, orc, q, tab, L = _build(K, lens, Hkv, Hkv * G, 16, 128, vb, seed=900 + G)
+    assert K.kv_int4_paged_decode_workspace(cache, len(lens), Hkv * G, 128, 128) == 0
+    out = torch.full((len(lens), Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
+    K.kv_int4_paged_decode(cache, bf16_dev(q), to_dev(tab), to_dev(L), 128, out=out, split_tokens=128)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[0] == 0.0)
+    decode_compare(got, _ref(orc, q, tab, L, Hkv, 16, 128, vb), f"single split G{G} vb{vb}")
