@@ -173,10 +173,11 @@ kvrq_status check_decode_shape(const kvrq_cache_desc *d, int32_t num_seqs, int32
     return KVRQ_OK;
 }
 
-// Extend: query rows per workgroup, so that a wave's 16 MFMA columns hold whole rows.
+// Extend: query rows per workgroup, so that a wave's blocks of 16 MFMA columns hold whole
+// rows.
 int32_t extend_rows_per_block(int32_t group)
 {
-    return std::max<int32_t>(1, kvrq::kMaxGroup / group);
+    return std::max<int32_t>(1, kvrq::kMaxGroup * kvrq::kExtendBlocks / group);
 }
 
 kvrq_status check_extend_shape(const kvrq_cache_desc *d, int32_t num_seqs, int32_t num_q_heads,

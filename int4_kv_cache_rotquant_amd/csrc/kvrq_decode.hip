@@ -332,101 +332,15 @@ struct WaveState {
             recentre();
     }
 
-    template <int F, bool EXT, int CB>
-    __device__ __forceinline__ void consume(const Tile &T, int t0, int t_end, int lane, float kscale,
-                                            const QOperand<F> &qop, ParLds &pl, int col_len,
-                                            int mask_from)
+    // ---- a9: online softmax (base 2) of one tile's scores, the PV weights as f16 high and
+    // low B operands
+    template <int F>
+    __device__ __forceinline__ void softmax(float (&sc)[8 / F], const float (&sv)[8 / F],
+                                            const float (&zv)[8 / F], int lane, f16x8 &bh,
+                                            f16x8 &bl)
     {
         constexpr int NS = 8 / F;            // scores per lane
-        const int n16 = lane & 15, kq = lane >> 4;
-        const int sub = F == 2 ? (n16 >> 3) : 0;
-
-        // parameters: each lane converts one (scale, zero) pair (zero past the end of the
-        // range, where the bias also removes the token from the softmax)
-        {
-            const bool valid = t0 + (lane & 31) < t_end;
-            const f16x2 pr = __builtin_bit_cast(f16x2, valid ? T.par : 0u);
-            pl.v[0][lane] = (float)pr.x * kscale;
-            pl.v[1][lane] = (float)pr.y;
-            pl.v[2][lane] = valid ? 0.0f : -INFINITY;
-        }
-        __builtin_amdgcn_wave_barrier();
-        float sk[NS], zk[NS], bk[NS], sv[NS], zv[NS];
-#pragma unroll
-        for (int j = 0; j < NS / 4; ++j) {
-            const int base = 4 * kq + 16 * (F == 2 ? sub : j);
-            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&pl.v[0][base]);
-            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&pl.v[1][base]);
-            const f32x4 a2 = *reinterpret_cast<const f32x4 *>(&pl.v[2][base]);
-            const f32x4 a3 = *reinterpret_cast<const f32x4 *>(&pl.v[0][32 + base]);
-            const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&pl.v[1][32 + base]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sk[4 * j + r] = a0[r];
-                zk[4 * j + r] = a1[r];
-                bk[4 * j + r] = a2[r];
-                sv[4 * j + r] = a3[r];
-                zv[4 * j + r] = a4[r];
-            }
-        }
-
-        // ---- a8: integer scores -----------------------------------------------------------
-        float sc[NS];
-        if constexpr (F == 1) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                u32x4 w = T.kc[hf];
-                if constexpr (CodeWidths<CB>::k2)
-                    w = u32x4{spread2(T.kc[hf].x & 0xFFFFu), spread2(T.kc[hf].x >> 16),
-                              spread2(T.kc[hf].y & 0xFFFFu), spread2(T.kc[hf].y >> 16)};
-                const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
-                const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
-                i32x4 dg[3];
-#pragma unroll
-                for (int d = 0; d < 3; ++d) {
-                    dg[d] = mfma_i8(ev, qop.v[0][d][lane], i32x4{0, 0, 0, 0});
-                    dg[d] = mfma_i8(od, qop.v[1][d][lane], dg[d]);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sc[4 * hf + r] = (float)((((dg[0][r] << 8) + dg[1][r]) << 8) + dg[2][r]);
-            }
-        } else {
-            i32x4 dg[3] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                u32x4 w = T.kc[j];
-                if constexpr (CodeWidths<CB>::k2) {
-                    const uint32_t d0 = j ? T.kc[0].z : T.kc[0].x, d1 = j ? T.kc[0].w : T.kc[0].y;
-                    w = u32x4{spread2(d0 & 0xFFFFu), spread2(d0 >> 16), spread2(d1 & 0xFFFFu),
-                              spread2(d1 >> 16)};
-                }
-                const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
-                const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
-#pragma unroll
-                for (int d = 0; d < 3; ++d) {
-                    dg[d] = mfma_i8(ev, qop.v[2 * j][d][lane], dg[d]);
-                    dg[d] = mfma_i8(od, qop.v[2 * j + 1][d][lane], dg[d]);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sc[r] = (float)((((dg[0][r] << 8) + dg[1][r]) << 8) + dg[2][r]);
-        }
-#pragma unroll
-        for (int i = 0; i < NS; ++i)
-            sc[i] = fmaf(sc[i], sk[i], fmaf(zk[i], qsum, bk[i]));
-        if constexpr (EXT) {
-            // causal: token t is visible to the lane's column only if t < col_len
-            if (t0 + kTile > mask_from) {
-                const int kq4 = 4 * (lane >> 4);
-#pragma unroll
-                for (int i = 0; i < NS; ++i)
-                    sc[i] = t0 + 16 * (i >> 2) + kq4 + (i & 3) < col_len ? sc[i] : -INFINITY;
-            }
-        }
-
-        // ---- a9: online softmax (base 2), lazy maximum ------------------------------------
+        const int sub = F == 2 ? ((lane & 15) >> 3) : 0;
         // Most tiles change nothing: the maximum moves only when a score exceeds it by more
         // than kLazyMax, the weight exponent only when a V scale reaches slim = 2^(6 - E).
         // Lanes test their own scores; the column reductions run only when some lane asks.
@@ -508,45 +422,156 @@ struct WaveState {
             bhu = sub ? u32x4{0u, 0u, hp[0], hp[1]} : u32x4{hp[0], hp[1], 0u, 0u};
             blu = sub ? u32x4{0u, 0u, lp[0], lp[1]} : u32x4{lp[0], lp[1], 0u, 0u};
         }
-        const f16x8 bh = __builtin_bit_cast(f16x8, bhu);
-        const f16x8 bl = __builtin_bit_cast(f16x8, blu);
+        bh = __builtin_bit_cast(f16x8, bhu);
+        bl = __builtin_bit_cast(f16x8, blu);
+    }
 
-        // ---- PV: A = V codes (rows: channel 8 n16 + b, k: the 8 tokens), B = weights -------
-        // the high-nibble mask in a scalar register, opaque to constant folding, so that
-        // (x & mask) | one is a single v_and_or_b32 (both constants as literals would not
-        // fit one instruction and would cost an and and an or)
-        uint32_t mant47, one2;
-        asm("" : "=s"(mant47) : "0"(kMant47));
-        asm("" : "=v"(one2) : "0"(kOne2));
-        uint32_t vcode[8];
+};
+
+// One tile for NB blocks of 16 MFMA columns (NB > 1: extend, several query rows per wave):
+// the parameters, the K operands and the V operands are built once and serve every block.
+template <int F, bool EXT, int CB, int NB>
+__device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile &T, int t0, int t_end,
+                                             int lane, float kscale, const QOperand<F> *qop,
+                                             ParLds &pl, const int (&col_len)[NB], int mask_from)
+{
+    static_assert(NB == 1 || F == 1, "several column blocks use the 16-column layout");
+    constexpr int NS = 8 / F;            // scores per lane
+    const int n16 = lane & 15, kq = lane >> 4;
+    const int sub = F == 2 ? (n16 >> 3) : 0;
+
+    // parameters: each lane converts one (scale, zero) pair (zero past the end of the
+    // range, where the bias also removes the token from the softmax)
+    {
+        const bool valid = t0 + (lane & 31) < t_end;
+        const f16x2 pr = __builtin_bit_cast(f16x2, valid ? T.par : 0u);
+        pl.v[0][lane] = (float)pr.x * kscale;
+        pl.v[1][lane] = (float)pr.y;
+        pl.v[2][lane] = valid ? 0.0f : -INFINITY;
+    }
+    __builtin_amdgcn_wave_barrier();
+    float sk[NS], zk[NS], bk[NS], sv[NS], zv[NS];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            vcode[j] = CodeWidths<CB>::v2 ? spread2(T.vc[j]) : T.vc[j];
+    for (int j = 0; j < NS / 4; ++j) {
+        const int base = 4 * kq + 16 * (F == 2 ? sub : j);
+        const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&pl.v[0][base]);
+        const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&pl.v[1][base]);
+        const f32x4 a2 = *reinterpret_cast<const f32x4 *>(&pl.v[2][base]);
+        const f32x4 a3 = *reinterpret_cast<const f32x4 *>(&pl.v[0][32 + base]);
+        const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&pl.v[1][32 + base]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            uint32_t src[4];   // byte k of tokens (2p, 2p + 1) in bits 0..7 and 16..23
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                src[p] = __builtin_amdgcn_perm(vcode[2 * p + 1], vcode[2 * p],
-                                               0x0C000C00u | ((4u + k) << 16) | (uint32_t)k);
-            u32x4 lo, hi;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                // the low nibble lands in mantissa bits 6..9; the high nibble lands in
-                // bits 10..13, which the exponent of 1.0 sets anyway, and bits 14..15
-                // receive the zero byte above it
-                lo[p] = (src[p] << 6) | one2;
-                hi[p] = (src[p] & mant47) | one2;
-            }
-            const f16x8 al = __builtin_bit_cast(f16x8, lo);
-            const f16x8 ah = __builtin_bit_cast(f16x8, hi);
-            acc[2 * k] = mfma16x16x32(al, bh, acc[2 * k]);
-            acc[2 * k] = mfma16x16x32(al, bl, acc[2 * k]);
-            acc[2 * k + 1] = mfma16x16x32(ah, bh, acc[2 * k + 1]);
-            acc[2 * k + 1] = mfma16x16x32(ah, bl, acc[2 * k + 1]);
+        for (int r = 0; r < 4; ++r) {
+            sk[4 * j + r] = a0[r];
+            zk[4 * j + r] = a1[r];
+            bk[4 * j + r] = a2[r];
+            sv[4 * j + r] = a3[r];
+            zv[4 * j + r] = a4[r];
         }
     }
-};
+
+    // ---- a8: integer scores -----------------------------------------------------------
+    float sc[NB][NS];
+    if constexpr (F == 1) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            u32x4 w = T.kc[hf];
+            if constexpr (CodeWidths<CB>::k2)
+                w = u32x4{spread2(T.kc[hf].x & 0xFFFFu), spread2(T.kc[hf].x >> 16),
+                          spread2(T.kc[hf].y & 0xFFFFu), spread2(T.kc[hf].y >> 16)};
+            const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
+            const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                i32x4 dg[3];
+#pragma unroll
+                for (int d = 0; d < 3; ++d) {
+                    dg[d] = mfma_i8(ev, qop[b].v[0][d][lane], i32x4{0, 0, 0, 0});
+                    dg[d] = mfma_i8(od, qop[b].v[1][d][lane], dg[d]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sc[b][4 * hf + r] = (float)((((dg[0][r] << 8) + dg[1][r]) << 8) + dg[2][r]);
+            }
+        }
+    } else {
+        i32x4 dg[3] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            u32x4 w = T.kc[j];
+            if constexpr (CodeWidths<CB>::k2) {
+                const uint32_t d0 = j ? T.kc[0].z : T.kc[0].x, d1 = j ? T.kc[0].w : T.kc[0].y;
+                w = u32x4{spread2(d0 & 0xFFFFu), spread2(d0 >> 16), spread2(d1 & 0xFFFFu),
+                          spread2(d1 >> 16)};
+            }
+            const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
+            const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+                dg[d] = mfma_i8(ev, qop[0].v[2 * j][d][lane], dg[d]);
+                dg[d] = mfma_i8(od, qop[0].v[2 * j + 1][d][lane], dg[d]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sc[0][r] = (float)((((dg[0][r] << 8) + dg[1][r]) << 8) + dg[2][r]);
+    }
+
+    f16x8 bh[NB], bl[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            sc[b][i] = fmaf(sc[b][i], sk[i], fmaf(zk[i], st[b].qsum, bk[i]));
+        if constexpr (EXT) {
+            // causal: token t is visible to the lane's column only if t < col_len
+            if (t0 + kTile > mask_from) {
+                const int kq4 = 4 * (lane >> 4);
+#pragma unroll
+                for (int i = 0; i < NS; ++i)
+                    sc[b][i] = t0 + 16 * (i >> 2) + kq4 + (i & 3) < col_len[b] ? sc[b][i] : -INFINITY;
+            }
+        }
+        st[b].template softmax<F>(sc[b], sv, zv, lane, bh[b], bl[b]);
+    }
+
+    // ---- PV: A = V codes (rows: channel 8 n16 + b, k: the 8 tokens), B = weights -------
+    // the high-nibble mask in a scalar register, opaque to constant folding, so that
+    // (x & mask) | one is a single v_and_or_b32 (both constants as literals would not
+    // fit one instruction and would cost an and and an or)
+    uint32_t mant47, one2;
+    asm("" : "=s"(mant47) : "0"(kMant47));
+    asm("" : "=v"(one2) : "0"(kOne2));
+    uint32_t vcode[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        vcode[j] = CodeWidths<CB>::v2 ? spread2(T.vc[j]) : T.vc[j];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t src[4];   // byte k of tokens (2p, 2p + 1) in bits 0..7 and 16..23
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+            src[p] = __builtin_amdgcn_perm(vcode[2 * p + 1], vcode[2 * p],
+                                           0x0C000C00u | ((4u + k) << 16) | (uint32_t)k);
+        u32x4 lo, hi;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            // the low nibble lands in mantissa bits 6..9; the high nibble lands in
+            // bits 10..13, which the exponent of 1.0 sets anyway, and bits 14..15
+            // receive the zero byte above it
+            lo[p] = (src[p] << 6) | one2;
+            hi[p] = (src[p] & mant47) | one2;
+        }
+        const f16x8 al = __builtin_bit_cast(f16x8, lo);
+        const f16x8 ah = __builtin_bit_cast(f16x8, hi);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            st[b].acc[2 * k] = mfma16x16x32(al, bh[b], st[b].acc[2 * k]);
+            st[b].acc[2 * k] = mfma16x16x32(al, bl[b], st[b].acc[2 * k]);
+            st[b].acc[2 * k + 1] = mfma16x16x32(ah, bh[b], st[b].acc[2 * k + 1]);
+            st[b].acc[2 * k + 1] = mfma16x16x32(ah, bl[b], st[b].acc[2 * k + 1]);
+        }
+    }
+}
 
 // Inverse V rotation of one output row held as channels (2 lane, 2 lane + 1) by the
 // 64 lanes of a wave: width 1 in-lane, widths 2.. across lanes.
@@ -618,6 +643,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? 4 
 void decode_split_kernel(DecodeArgs a)
 {
     static_assert(!EXT || F == 1, "extend columns use the 16-column layout");
+    // column blocks of 16 per wave: extend takes kExtendBlocks (more query rows share each
+    // tile's operands), the decode one
+    constexpr int NB = EXT ? kExtendBlocks : 1;
     const int h = blockIdx.y;
     const int G = a.group;
     // The MFMA columns: decode: the G query heads of sequence s (grid: split, KV head,
@@ -679,18 +707,21 @@ void decode_split_kernel(DecodeArgs a)
     // per query head and wave)
     constexpr int kSlots = F == 2 ? 8 : 16;
     __shared__ float lds_o[kDecodeWaves][kSlots][kHeadDim + 4];
-    __shared__ QOperand<F> qop;
+    __shared__ QOperand<F> qop[NB];
     __shared__ ParLds lds_par[kDecodeWaves];
     __shared__ float lds_m[kDecodeWaves][kSlots];
     __shared__ float lds_l[kDecodeWaves][kSlots];
-    __shared__ float lds_qsum[kMaxGroup];
+    __shared__ float lds_qsum[kMaxGroup * NB];
+    __shared__ float lds_amax[NB];
     __shared__ float lds_kscale;
     float(*q_lds)[kHeadDim + 4] = reinterpret_cast<float(*)[kHeadDim + 4]>(&lds_o[0][0][0]);
 
-    // ---- a6: wave 0 rotates the G queries of this KV head, folds sm_scale * log2(e) ---------
-    if (wave == 0) {
-        const int g = lane >> 2, ql = lane & 3;
-        float x[32];
+    // ---- a6: waves 0 .. NB-1 rotate the queries of this KV head (16 columns each), fold
+    // sm_scale * log2(e), and round them to one integer grid
+    const int g = wave * 16 + (lane >> 2), ql = lane & 3;
+    float x[32];
+    float amax = 0.0f, sum = 0.0f;
+    if (wave < NB) {
         if (g < ncols) {
             const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
                                      : (int64_t)s * a.num_q_heads + h * G + g;
@@ -711,7 +742,6 @@ void decode_split_kernel(DecodeArgs a)
                 x[i] = 0.0f;
         }
         rotate_query<BK>(x, ql);
-        float amax = 0.0f, sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
             x[i] *= a.q_scale;
@@ -723,26 +753,39 @@ void decode_split_kernel(DecodeArgs a)
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1)
             amax = fmaxf(amax, wave_xor(amax, o));
-        // one power-of-two factor 2^f for the whole group: max |q' 2^f| in [2^19, 2^20)
+        if (lane == 0)
+            lds_amax[wave] = amax;
+    }
+    if constexpr (NB > 1)
+        __syncthreads();
+    if (wave < NB) {
+        if constexpr (NB > 1) {
+            amax = lds_amax[0];
+#pragma unroll
+            for (int b = 1; b < NB; ++b)
+                amax = fmaxf(amax, lds_amax[b]);
+        }
+        // one power-of-two factor 2^f for all columns: max |q' 2^f| in [2^19, 2^20)
         int e = 0;
         if (amax > 0.0f)
             frexpf(amax, &e);
 #pragma unroll
         for (int i = 0; i < 32; ++i)
             q_lds[g][32 * ql + i] = ldexpf(x[i], 20 - e);
-        if (ql == 0 && g < kMaxGroup)
+        if (ql == 0 && g < kMaxGroup * NB)
             lds_qsum[g] = sum;
-        if (lane == 0)
+        if (wave == 0 && lane == 0)
             lds_kscale = ldexpf(1.0f, e - 20);
     }
     __syncthreads();
 
     // B operands of QK^T: int8 digits of the integer query in lane order
-    for (int i = tid; i < 2 * F * 64; i += 64 * kDecodeWaves) {
-        const int slot = i >> 6, ln = i & 63;     // slot = 2 j + par (F = 2) or par (F = 1)
+    for (int i = tid; i < 2 * F * 64 * NB; i += 64 * kDecodeWaves) {
+        const int blk = i / (2 * F * 64), ib = i - blk * (2 * F * 64);
+        const int slot = ib >> 6, ln = ib & 63;   // slot = 2 j + par (F = 2) or par (F = 1)
         const int n = ln & 15, q4 = ln >> 4;
         const int par = slot & 1, jj = slot >> 1;
-        const int g = F == 2 ? (n & 7) : n;
+        const int g = blk * 16 + (F == 2 ? (n & 7) : n);
         const bool live = g < ncols && (F == 1 || (n >> 3) == (q4 >> 1));
         const int ch0 = F == 2 ? 64 * (q4 & 1) + 32 * jj + par : 32 * q4 + par;
         uint32_t dig[3][4];
@@ -765,33 +808,38 @@ void decode_split_kernel(DecodeArgs a)
         }
 #pragma unroll
         for (int d = 0; d < 3; ++d)
-            qop.v[slot][d][ln] = i32x4{int32_t(dig[d][0]), int32_t(dig[d][1]), int32_t(dig[d][2]),
-                                       int32_t(dig[d][3])};
+            qop[blk].v[slot][d][ln] = i32x4{int32_t(dig[d][0]), int32_t(dig[d][1]),
+                                            int32_t(dig[d][2]), int32_t(dig[d][3])};
     }
     const int n16 = lane & 15;
     const int kq = lane >> 4;
     const int gl = F == 2 ? (n16 & 7) : n16;   // this lane's column (query head)
     // extend: the lane's column sees tokens 0 .. col_len - 1; tiles that reach past the
     // first row's position mask per column
-    const int col_len = EXT ? (gl < ncols ? pos0 + gl / G + 1 : 0) : 0;
+    int col_len[NB];
     const int mask_from = pos0 + 1;
-    WaveState st;
-    st.qsum = lds_qsum[gl];
+    WaveState st[NB];
     // K lanes scale by 2^-f (the integer query's grid), V lanes by 1
     const float kscale = lane < 32 ? lds_kscale : 1.0f;
-    // a finite start: with F = 2 half a tile may hold no valid token while nothing has been
-    // seen yet, and exp2(-inf - (-inf)) would poison the sums
-    st.m = kNoScore;
-    st.l = 0.0f;
-    st.z = 0.0f;
-    st.wsum = 0.0f;
-    st.E = 64;
-    st.slim = 0x1p-58f;   // 2^(6 - E)
-    st.wpend = 0.0f;
-    st.nt = 0;
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
-        st.acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = 0; b < NB; ++b) {
+        const int gb = b * 16 + gl;
+        col_len[b] = EXT ? (gb < ncols ? pos0 + gb / G + 1 : 0) : 0;
+        st[b].qsum = lds_qsum[gb];
+        // a finite start: with F = 2 half a tile may hold no valid token while nothing has
+        // been seen yet, and exp2(-inf - (-inf)) would poison the sums
+        st[b].m = kNoScore;
+        st[b].l = 0.0f;
+        st[b].z = 0.0f;
+        st[b].wsum = 0.0f;
+        st[b].E = 64;
+        st[b].slim = 0x1p-58f;   // 2^(6 - E)
+        st[b].wpend = 0.0f;
+        st[b].nt = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            st[b].acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     __syncthreads();   // q_lds is reused below, qop is complete
 
     // ---- a7: page walk, one tile ahead of the math --------------------------------------
@@ -814,14 +862,18 @@ void decode_split_kernel(DecodeArgs a)
         load_tile<F, CB>(B, a, pid, h, min(cb + kTile, t_last), ce, lane);
         int t0 = cb;
         while (true) {
-            st.template consume<F, EXT, CB>(A, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
-            st.tick();
+            consume_tile<F, EXT, CB, NB>(st, A, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                st[b].tick();
             if (t0 + kTile >= ce)
                 break;
             load_tile<F, CB>(A, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
             t0 += kTile;
-            st.template consume<F, EXT, CB>(B, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
-            st.tick();
+            consume_tile<F, EXT, CB, NB>(st, B, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                st[b].tick();
             if (t0 + kTile >= ce)
                 break;
             load_tile<F, CB>(B, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
@@ -829,94 +881,108 @@ void decode_split_kernel(DecodeArgs a)
         }
     }
 
-    // ---- the waves' (and, for F = 2, the two halves') partial states of this split -------
-    st.recentre();
-    st.l = col_sum(st.l);
-    st.z = col_sum(st.z);
-    st.wsum = col_sum(st.wsum);
-    float o[8][4];
-    {
-        const float u_even = ldexpf(16.0f, -st.E), u_odd = ldexpf(64.0f, -st.E);
-        const float zero = fmaf(8.0f, ldexpf(st.wsum, -st.E), st.z);
+    // ---- the waves' (and, for F = 2, the two halves') partial states of this split, one
+    // block of 16 columns at a time through the same LDS
 #pragma unroll
-        for (int b = 0; b < 8; ++b)
+    for (int blk = 0; blk < NB; ++blk) {
+        const int cb0 = blk * 16;                 // first column of the block
+        const int nc = min(ncols - cb0, 16);      // its columns (uniform)
+        if (nc <= 0)
+            break;
+        if (blk > 0)
+            __syncthreads();   // the previous block's reads of lds_o are done
+        WaveState &sb = st[blk];
+        sb.recentre();
+        sb.l = col_sum(sb.l);
+        sb.z = col_sum(sb.z);
+        sb.wsum = col_sum(sb.wsum);
+        float o[8][4];
+        {
+            const float u_even = ldexpf(16.0f, -sb.E), u_odd = ldexpf(64.0f, -sb.E);
+            const float zero = fmaf(8.0f, ldexpf(sb.wsum, -sb.E), sb.z);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                o[b][r] = fmaf(st.acc[b][r], (b & 1) ? u_odd : u_even, zero);
-    }
-    float m_w = st.m, l_w = st.l;
-    if constexpr (F == 2) {
-        // lanes n16 and n16 ^ 8 (one 16-lane row) hold the two halves of head n16 % 8
-        const float m_o = dpp_row_ror8(st.m);
-        const float M = fmaxf(st.m, m_o);
-        const float fa = __builtin_amdgcn_exp2f(st.m - M), fb = __builtin_amdgcn_exp2f(m_o - M);
-        l_w = st.l * fa + dpp_row_ror8(st.l) * fb;
-        m_w = M;
+            for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                o[b][r] = o[b][r] * fa + dpp_row_ror8(o[b][r]) * fb;
-    }
-    if (n16 < kSlots && gl < ncols) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                lds_o[wave][n16][32 * kq + 8 * r + b] = o[b][r];
-        if (kq == 0) {
-            lds_m[wave][n16] = m_w;
-            lds_l[wave][n16] = l_w;
+                for (int r = 0; r < 4; ++r)
+                    o[c][r] = fmaf(sb.acc[c][r], (c & 1) ? u_odd : u_even, zero);
         }
-    }
-    __syncthreads();
-    if (a.max_splits == 1) {
-        // the only split: merge the waves, normalise, undo the V rotation and write the
-        // output rows here (no combine launch); wave w takes columns w, w + 4, ...,
-        // lane l channels 2 l and 2 l + 1
-        for (int g = wave; g < ncols; g += kDecodeWaves) {
-            float M = lds_m[0][g];
+        float m_w = sb.m, l_w = sb.l;
+        if constexpr (F == 2) {
+            // lanes n16 and n16 ^ 8 (one 16-lane row) hold the two halves of head n16 % 8
+            const float m_o = dpp_row_ror8(sb.m);
+            const float M = fmaxf(sb.m, m_o);
+            const float fa = __builtin_amdgcn_exp2f(sb.m - M), fb = __builtin_amdgcn_exp2f(m_o - M);
+            l_w = sb.l * fa + dpp_row_ror8(sb.l) * fb;
+            m_w = M;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[c][r] = o[c][r] * fa + dpp_row_ror8(o[c][r]) * fb;
+        }
+        if (n16 < kSlots && gl < nc) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    lds_o[wave][n16][32 * kq + 8 * r + c] = o[c][r];
+            if (kq == 0) {
+                lds_m[wave][n16] = m_w;
+                lds_l[wave][n16] = l_w;
+            }
+        }
+        __syncthreads();
+        if (a.max_splits == 1) {
+            // the only split: merge the waves, normalise, undo the V rotation and write
+            // the output rows here (no combine launch); wave w takes columns w, w + 4, ...,
+            // lane l channels 2 l and 2 l + 1
+            for (int gc = wave; gc < nc; gc += kDecodeWaves) {
+                float M = lds_m[0][gc];
+#pragma unroll
+                for (int w = 1; w < kDecodeWaves; ++w)
+                    M = fmaxf(M, lds_m[w][gc]);
+                float o0 = 0.0f, o1 = 0.0f, lsum = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kDecodeWaves; ++w) {
+                    const float f = __builtin_amdgcn_exp2f(lds_m[w][gc] - M);
+                    o0 += f * lds_o[w][gc][2 * lane];
+                    o1 += f * lds_o[w][gc][2 * lane + 1];
+                    lsum += f * lds_l[w][gc];
+                }
+                const float inv_l = 1.0f / lsum;
+                o0 *= inv_l;
+                o1 *= inv_l;
+                inverse_rotate_pair_rt(o0, o1, lane, a.v_block);
+                const int g = cb0 + gc;
+                const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
+                                         : (int64_t)s * a.num_q_heads + h * G + g;
+                *reinterpret_cast<float2 *>(a.out + qrow * kHeadDim + 2 * lane) =
+                    make_float2(o0, o1);
+            }
+            continue;
+        }
+        for (int i = tid; i < nc * kHeadDim; i += 64 * kDecodeWaves) {
+            const int gc = i >> 7, d = i & (kHeadDim - 1);
+            float M = lds_m[0][gc];
 #pragma unroll
             for (int w = 1; w < kDecodeWaves; ++w)
-                M = fmaxf(M, lds_m[w][g]);
-            float o0 = 0.0f, o1 = 0.0f, lsum = 0.0f;
+                M = fmaxf(M, lds_m[w][gc]);
+            float acc = 0.0f, lsum = 0.0f;
 #pragma unroll
             for (int w = 0; w < kDecodeWaves; ++w) {
-                const float f = __builtin_amdgcn_exp2f(lds_m[w][g] - M);
-                o0 += f * lds_o[w][g][2 * lane];
-                o1 += f * lds_o[w][g][2 * lane + 1];
-                lsum += f * lds_l[w][g];
+                const float f = __builtin_amdgcn_exp2f(lds_m[w][gc] - M);
+                acc += f * lds_o[w][gc][d];
+                lsum += f * lds_l[w][gc];
             }
-            const float inv_l = 1.0f / lsum;
-            o0 *= inv_l;
-            o1 *= inv_l;
-            inverse_rotate_pair_rt(o0, o1, lane, a.v_block);
+            const int g = cb0 + gc;
             const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
                                      : (int64_t)s * a.num_q_heads + h * G + g;
-            *reinterpret_cast<float2 *>(a.out + qrow * kHeadDim + 2 * lane) = make_float2(o0, o1);
-        }
-        return;
-    }
-    for (int i = tid; i < ncols * kHeadDim; i += 64 * kDecodeWaves) {
-        const int g = i >> 7, d = i & (kHeadDim - 1);
-        float M = lds_m[0][g];
-#pragma unroll
-        for (int w = 1; w < kDecodeWaves; ++w)
-            M = fmaxf(M, lds_m[w][g]);
-        float acc = 0.0f, lsum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) {
-            const float f = __builtin_amdgcn_exp2f(lds_m[w][g] - M);
-            acc += f * lds_o[w][g][d];
-            lsum += f * lds_l[w][g];
-        }
-        const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
-                                 : (int64_t)s * a.num_q_heads + h * G + g;
-        const int64_t row = qrow * a.max_splits + split;
-        a.part_o[row * kHeadDim + d] = acc;
-        if (d == 0) {
-            a.part_ml[2 * row] = M;
-            a.part_ml[2 * row + 1] = lsum;
+            const int64_t row = qrow * a.max_splits + split;
+            a.part_o[row * kHeadDim + d] = acc;
+            if (d == 0) {
+                a.part_ml[2 * row] = M;
+                a.part_ml[2 * row + 1] = lsum;
+            }
         }
     }
 }

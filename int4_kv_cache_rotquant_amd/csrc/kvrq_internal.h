@@ -16,6 +16,7 @@ constexpr int kWriteWavesPerSimd = 5;  // occupancy target (the kernel fits six)
 constexpr int kWriteWgsPerCu = 6;      // 256-lane workgroups per CU: one wave per SIMD each
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave
 constexpr int kDecodeWaves = 4;     // waves per decode workgroup, each on its own token range
+constexpr int kExtendBlocks = 2;    // extend: 16-column blocks per wave (query rows x heads)
 
 struct WriteArgs {
     const uint16_t *k;          // bf16 bits
