@@ -81,7 +81,7 @@ struct DecodeArgs {
     // rows are then query rows: q, out [total_q][Hq][128], part_* [total_q][Hq][splits]
     const int32_t *qo_start = nullptr;  // [S + 1] first query row of each sequence
     int32_t num_rows;           // rows of the combine: S (decode) or total_q (extend)
-    int32_t rows_per_block;     // query rows per workgroup (16 / group, at least 1)
+    int32_t rows_per_block;     // query rows per workgroup (32 / group, at least 1)
     int32_t blocks_per_seq;     // ceil(max_q_len / rows_per_block)
     // fused decode step only (new_slots == nullptr otherwise): each sequence's new token,
     // written by the workgroup whose split holds position seq_len - 1, before it reads
