@@ -102,7 +102,9 @@ def test_decode_validation(K):
     def ws(desc, S=4, Hq=64, maxlen=1000, split=0):
         return L.kv_int4_paged_decode_workspace(ctypes.byref(desc), S, Hq, maxlen, split, ctypes.byref(size))
 
-    assert ws(_desc(K)) == K.KVRQ_OK and size.value > 0
+    assert ws(_desc(K), maxlen=5000) == K.KVRQ_OK and size.value > 0
+    # one split covers 1000 tokens: no partials, no workspace
+    assert ws(_desc(K)) == K.KVRQ_OK and size.value == 0
     assert ws(_desc(K), Hq=60) == K.KVRQ_EINVAL
     assert ws(_desc(K), Hq=8 * 17) == K.KVRQ_EUNSUPPORTED
     assert ws(_desc(K, page_size=8)) == K.KVRQ_EUNSUPPORTED
@@ -115,7 +117,7 @@ def test_decode_validation(K):
     ws(_desc(K), split=128)
     assert size.value > small
 
-    def dec(desc=None, q=0x1000, S=2, Hq=64, tab=0x2000, maxp=100, lens=0x3000, maxlen=1000,
+    def dec(desc=None, q=0x1000, S=2, Hq=64, tab=0x2000, maxp=400, lens=0x3000, maxlen=5000,
             scale=0.0, split=0, out=0x4000, wsp=0x5000, wsb=1 << 30):
         desc = desc or _desc(K)
         return L.kv_int4_paged_decode(ctypes.byref(desc), ctypes.byref(_bufs(K)), q, S, Hq, tab, maxp,
@@ -124,7 +126,7 @@ def test_decode_validation(K):
     assert dec(S=0) == K.KVRQ_OK
     assert dec(q=0) == K.KVRQ_EINVAL
     assert dec(q=0x1004) == K.KVRQ_EINVAL
-    assert dec(maxp=10) == K.KVRQ_EINVAL            # 10 pages of 16 < 1000 tokens
+    assert dec(maxp=10) == K.KVRQ_EINVAL            # 10 pages of 16 < 5000 tokens
     assert dec(scale=float("nan")) == K.KVRQ_EINVAL
     assert dec(wsb=16) == K.KVRQ_EWORKSPACE
     assert "workspace" in K.last_error()
@@ -137,7 +139,7 @@ def test_decode_step_validation(K):
     def step(k=0x10000, v=0x20000, ks=1024, vs=1024, slots=0x30000, S=2, q=0x1000, wsb=1 << 30,
              lens=0x3000, out=0x4000):
         return L.kv_int4_paged_decode_step(ctypes.byref(_desc(K)), ctypes.byref(_bufs(K)), k, v, ks, vs,
-                                           slots, q, S, 64, 0x2000, 100, lens, 1000, 0.0, 0, out,
+                                           slots, q, S, 64, 0x2000, 400, lens, 5000, 0.0, 0, out,
                                            0x5000, wsb, None)
 
     assert step(S=0) == K.KVRQ_OK
