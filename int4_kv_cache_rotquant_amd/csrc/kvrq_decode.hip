@@ -10,24 +10,27 @@
 // orthonormal, hence its own inverse).
 //
 // Launch 1 -- decode_split_kernel, one workgroup of four 64-lane waves per
-// (split, KV head, sequence); each wave walks a quarter of the split's tokens
-// in 32-token tiles, the next tile's loads in flight while one is consumed:
-//   QK^T  S[t][g] = sum_d code_K[t][d] q[d][g] on int8 MFMA 16x16x64: A = the
-//         INT4 codes as bytes, B = the G (<= 16) rotated queries rounded to a
-//         21-bit integer grid and cut into three int8 digits, so the products
-//         are exact integers; score = scale_t * 2^-f * S + zero_t * sum(q')
-//         (de-quantisation factored out of the dot product);
+// (split, KV head, sequence) -- for the extend, per (row block, KV head, split); the
+// waves share the split's 32-token tiles evenly, the next tiles' loads in flight while
+// one is consumed:
+//   QK^T  S[t][c] = sum_d code_K[t][d] q[d][c] on int8 MFMA 16x16x64: A = the
+//         INT4 codes as bytes, B = the rotated queries of the MFMA columns rounded to
+//         a 21-bit integer grid and cut into three int8 digits, so the products are
+//         exact integers; score = scale_t * 2^-f * S + zero_t * sum(q') (the
+//         de-quantisation factored out of the dot product);
 //   softmax online, in base 2 (log2 e is folded into q'), with a lazy maximum;
-//   PV    O'[d][g] += sum_t (code_V[t][d] - 8) (p_t scale_t), plus
-//         sum_t p_t (zero_t + 8 scale_t), on f16 MFMA 16x16x32 with the codes
-//         as exact centred f16 integers and the weights split into f16 high
-//         and low parts.
-// Lane (n16, kq) keeps query head g = n16, so the softmax state needs no
-// cross-lane exchange except for the per-tile maxima.  The four waves' states
-// are merged in LDS into one split partial (o, m, l).
-// Launch 2 -- log-sum-exp combine of the splits, then the inverse V rotation:
-// decode_combine_wave_kernel (one wave per (query head, sequence)) for up to 64 splits,
-// decode_combine_kernel (a 16-wave workgroup per (query head, sequence)) beyond.
+//   PV    O'[d][c] += sum_t code_V[t][d] (p_t scale_t) + sum_t p_t zero_t, on f16
+//         MFMA 16x16x32 with the codes placed in f16 mantissas (1 + code / 16 or
+//         / 64, the constant part taken out of the sums) and the weights split into
+//         f16 high and low parts.
+// Columns: G <= 8 query heads take two columns each, one per 16-token half of every
+// tile (F = 2); otherwise 16 columns of single heads, or, for the extend, query rows x
+// heads in two blocks of 16 per wave (F = 1).  The four waves' states are merged in LDS
+// into one split partial (o, m, l) -- or, when one split covers the rows, normalised,
+// rotated back and written as the output directly.
+// Launch 2 (more than one split) -- log-sum-exp combine of the splits, then the inverse
+// V rotation: decode_combine_wave_kernel (one wave per (row, query head)) for up to 64
+// splits, decode_combine_kernel (a 16-wave workgroup per (row, query head)) beyond.
 #include <hip/hip_runtime.h>
 
 #include "kvrq_encode.h"
