@@ -28,6 +28,10 @@
 // heads in two blocks of 16 per wave (F = 1).  The four waves' states are merged in LDS
 // into one split partial (o, m, l) -- or, when one split covers the rows, normalised,
 // rotated back and written as the output directly.
+// 2-bit tiles (mixed-precision caches) are loaded at half size and widened to the
+// byte-per-code layout as they are consumed.  In the fused decode step, the workgroup
+// whose split holds a sequence's last position first encodes and stores the new
+// token's K/V rows (the write kernel's encoding), then reads them back with the rest.
 // Launch 2 (more than one split) -- log-sum-exp combine of the splits, then the inverse
 // V rotation: decode_combine_wave_kernel (one wave per (row, query head)) for up to 64
 // splits, decode_combine_kernel (a 16-wave workgroup per (row, query head)) beyond.
