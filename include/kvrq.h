@@ -99,7 +99,8 @@ typedef struct {
     int32_t head_dim;      /* D, must be 128 */
     int32_t num_kv_heads;  /* Hkv >= 1 */
     int32_t page_size;     /* P tokens per page, power of two, 1..1024 */
-    int32_t num_pages;     /* pages in each pool, >= 1 */
+    int32_t num_pages;     /* pages in each pool, >= 1; num_pages * num_kv_heads *
+                              page_size must not exceed 2^32 */
     int32_t k_block;       /* 0, 16, 32, 64 or 128 */
     int32_t v_block;       /* 0, 16, 32, 64 or 128 */
     int32_t k_bits;        /* 0 or 4: INT4; 2: 2-bit */

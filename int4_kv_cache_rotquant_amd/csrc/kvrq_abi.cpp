@@ -65,8 +65,11 @@ kvrq_status check_desc(const kvrq_cache_desc *d)
         return fail(KVRQ_EUNSUPPORTED, "code widths (%d, %d) unsupported (0 or 4 = INT4, 2)",
                     d->k_bits, d->v_bits);
     const int64_t cells = int64_t(d->num_pages) * d->num_kv_heads * d->page_size;
-    if (cells > (int64_t(1) << 40))
-        return fail(KVRQ_EINVAL, "cache too large");
+    // (page, head, token) cells are 32-bit indexes in the kernels; 2^32 of them would
+    // take at least 288 GiB (72 B per cell with 2-bit codes)
+    if (cells > (int64_t(1) << 32))
+        return fail(KVRQ_EINVAL, "cache too large: num_pages * num_kv_heads * page_size = %lld > 2^32",
+                    (long long)cells);
     return KVRQ_OK;
 }
 

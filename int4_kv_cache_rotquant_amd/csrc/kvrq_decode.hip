@@ -37,6 +37,8 @@
 // splits, decode_combine_kernel (a 16-wave workgroup per (row, query head)) beyond.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kvrq_encode.h"
 #include "kvrq_internal.h"
 
@@ -146,6 +148,9 @@ constexpr int kRecentre = 8;
 constexpr uint32_t kOne2 = 0x3C003C00u;     // f16x2 {1, 1}
 constexpr uint32_t kMant47 = 0x00F000F0u;   // mantissa bits 4..7 of both halves
 
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
+
 // K codes become int8 MFMA operands: the even and the odd nibbles of a dword, masked in
 // place, are four bytes each.  Scores are integer dot products of codes with the query
 // rounded to a 21-bit grid (three int8 digits), exact in the int32 accumulators.
@@ -172,36 +177,37 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const f16x8 &a, const f16x8 &b, co
 //   F = 1 (9..16 query heads per KV head): a 16x16x64 MFMA covers 16 tokens x 16 heads
 //         x 64 k (32 channels, one nibble parity); lane (n16, kq) ends with the scores of
 //         head n16 for tokens 16 hf + 4 kq + r (8 per lane);
-//   F = 2 (up to 8 heads): the k range is split between two tokens: k < 32 belongs to
-//         token n16, k >= 32 to token n16 + 16, and B columns 0..7 / 8..15 read only
-//         their half, so one MFMA covers 32 tokens x 8 heads; lane (n16, kq) ends with
-//         the scores of head n16 % 8 for tokens 4 kq + r + 16 (n16 / 8) (4 per lane) and
-//         keeps its own softmax state for that half of the tile (merged at the end).
-// One 32-token tile as this lane loads it:
-//   kc[j]   F = 1: 16 code bytes of token 16 j + n16, bytes [16 kq, 16 kq + 16)
-//           F = 2: 16 code bytes of token n16 + 16 (kq / 2), bytes 32 (kq % 2) + 16 j
+//   F = 2 (up to 8 heads): the same MFMAs, one pair of nibble steps per 16-token half,
+//         but B columns 8..15 are zero in the first half's steps and columns 0..7 in the
+//         second's, so both halves accumulate into one result: 32 tokens x 8 heads;
+//         lane (n16, kq) ends with the scores of head n16 % 8 for tokens 4 kq + r + 16
+//         (n16 / 8) (4 per lane) and keeps its own softmax state for that half of the
+//         tile (merged at the end).
+// One 32-token tile as this lane loads it (every load instruction reads from one page, at
+// a scalar base and a per-lane offset that does not change from tile to tile):
+//   kc[j]   16 code bytes of token 16 j + n16, bytes [16 kq, 16 kq + 16)
 //   vc[j]   code dword n16 (channels 8 n16 .. 8 n16 + 7) of token 16 (j / 4) + 4 kq + j % 4
 //   par     lanes 0..31: (scale, zero) of K of token lane; lanes 32..63: V of token
 //           lane - 32; converted and shared through LDS when the tile is consumed
 // 2-bit pools (CB bit 0: K, bit 1: V) load half the bytes:
-//   kc[j].xy  F = 1: 8 code bytes of token 16 j + n16, bytes [8 kq, 8 kq + 8) (channels
+//   kc[j].xy  8 code bytes of token 16 j + n16, bytes [8 kq, 8 kq + 8) (channels
 //             32 kq .. 32 kq + 31 as for 4 bits)
-//   kc[0]     F = 2: 16 code bytes of token n16 + 16 (kq / 2), bytes 16 (kq % 2) + [0, 16)
-//             (channels 64 (kq % 2) .. + 63 as for 4 bits)
 //   vc[j]     the 16-bit code word n16 (channels 8 n16 .. 8 n16 + 7)
 // and widen them to the 4-bit layout when the tile is consumed (spread2), so the rest of
 // the pipeline is the same: a 2-bit code is a 4-bit code below 4 with the same meaning.
-struct Tile {
-    u32x4 kc[2];
-    uint32_t vc[8];
-    uint32_t par;
-};
-
 template <int CB> struct CodeWidths {
     static constexpr bool k2 = (CB & 1) != 0;
     static constexpr bool v2 = (CB & 2) != 0;
     static constexpr int k_row = k2 ? kRowCodeBytes / 2 : kRowCodeBytes;
     static constexpr int v_row = v2 ? kRowCodeBytes / 2 : kRowCodeBytes;
+};
+
+template <int CB>
+struct Tile {
+    using KWords = std::conditional_t<CodeWidths<CB>::k2, u32x2, u32x4>;
+    KWords kc[2];
+    uint32_t vc[8];
+    uint32_t par;
 };
 
 // Eight 2-bit codes (bits 2i of a 16-bit value) -> eight 4-bit codes (bits 4i).
@@ -210,6 +216,14 @@ __device__ __forceinline__ uint32_t spread2(uint32_t x)
     x = (x | (x << 8)) & 0x00FF00FFu;
     x = (x | (x << 4)) & 0x0F0F0F0Fu;
     return (x | (x << 2)) & 0x33333333u;
+}
+
+// The K code words of one half tile in the 4-bit layout (2-bit words widened).
+__device__ __forceinline__ u32x4 k_nibbles(const u32x4 &k) { return k; }
+__device__ __forceinline__ u32x4 k_nibbles(const u32x2 &k)
+{
+    return u32x4{spread2(k.x & 0xFFFFu), spread2(k.x >> 16), spread2(k.y & 0xFFFFu),
+                 spread2(k.y >> 16)};
 }
 
 // Issues the loads of the tile starting at t0 (< t_end).  A half tile that starts past
@@ -235,68 +249,114 @@ struct PageIds {
     }
 };
 
-template <int F, int CB>
-__device__ __forceinline__ void load_tile(Tile &T, const DecodeArgs &a, const PageIds &pid, int h,
-                                          int t0, int t_end, int lane)
+// Per-lane parts of the tile addresses, the same for every tile.
+struct LaneAddr {
+    uint32_t k;   // K code bytes within a (page, head) row block
+    uint32_t v;   // V code bytes within a (page, head) row block
+    int lane;
+
+    template <int CB>
+    __device__ __forceinline__ void init(int lane_)
+    {
+        using CW = CodeWidths<CB>;
+        lane = lane_;
+        const uint32_t n16 = lane & 15, kq = lane >> 4;
+        k = CW::k2 ? n16 * CW::k_row + 8 * kq : n16 * kRowCodeBytes + 16 * kq;
+        v = CW::v2 ? 4 * kq * CW::v_row + 2 * n16 : 4 * kq * kRowCodeBytes + 4 * n16;
+    }
+};
+
+// A buffer resource for one (page, head) row block: base in scalar registers, so each
+// load is that base plus the lane's 32-bit offset, with no 64-bit vector arithmetic per
+// tile (offsets stay far below the record limit).
+// The base is wave-uniform by construction; reading it through readfirstlane says so, so
+// the compiler never wraps the loads in a loop over distinct bases.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_block(const uint8_t *base)
+{
+    // (readfirstlane returns int: take both halves as unsigned 32-bit values, so the low
+    // half is not sign-extended into the high one)
+    const uint64_t u = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo),
+                                             (short)0, 0x7FFFFFFF, kBufferWord3);
+}
+
+// Loads of one (page, head) row block at a lane offset: through a buffer resource (BUF:
+// scalar base, the row step as the scalar offset) or as plain global loads.
+template <bool BUF>
+struct RowBlock {
+    const uint8_t *p;
+    __amdgpu_buffer_rsrc_t r;
+
+    __device__ __forceinline__ RowBlock(const uint8_t *base) : p(base)
+    {
+        if constexpr (BUF)
+            r = row_block(base);
+    }
+    template <typename T>
+    __device__ __forceinline__ T load(uint32_t lane_off, int row_off) const
+    {
+        if constexpr (!BUF)
+            return *reinterpret_cast<const T *>(p + lane_off + row_off);
+        else if constexpr (sizeof(T) == 16)
+            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, row_off, 0));
+        else if constexpr (sizeof(T) == 8)
+            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)lane_off, row_off, 0));
+        else if constexpr (sizeof(T) == 4)
+            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, (int)lane_off, row_off, 0));
+        else
+            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, (int)lane_off, row_off, 0));
+    }
+};
+
+// The decode takes buffer loads; the extend, at the register limit with its two column
+// blocks, plain loads (its scalar registers are needed elsewhere).
+template <int CB, bool BUF>
+__device__ __forceinline__ void load_tile(Tile<CB> &T, const DecodeArgs &a, const PageIds &pid, int h,
+                                          int t0, int t_end, const LaneAddr &la)
 {
     using CW = CodeWidths<CB>;
     const int P = 1 << a.page_log2;
-    const int n16 = lane & 15, kq = lane >> 4;
-    // (page, head) row bases of the two 16-token halves; uniform, so on the scalar unit
-    const uint8_t *kb[2], *vb[2];
-    const uint32_t *kp[2], *vp[2];
+    // (page, head) row blocks of the two 16-token halves; uniform, so on the scalar unit
+    // (cells, page * Hkv * P + token, are below 2^32)
+    uint32_t cell[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
         const int tb = hf && t0 + 16 >= t_end ? t0 : t0 + 16 * hf;
-        const int page = pid.page(tb >> a.page_log2);
-        const int64_t cell0 = ((int64_t)page * a.num_kv_heads + h) * P + (tb & (P - 1));
-        kb[hf] = a.k_codes + cell0 * CW::k_row;
-        vb[hf] = a.v_codes + cell0 * CW::v_row;
-        kp[hf] = a.k_params + cell0;
-        vp[hf] = a.v_params + cell0;
-    }
-    if constexpr (CW::k2 && F == 1) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const u32x2 w = *reinterpret_cast<const u32x2 *>(kb[hf] + n16 * CW::k_row + 8 * kq);
-            T.kc[hf].x = w.x;
-            T.kc[hf].y = w.y;
-        }
-    } else if constexpr (CW::k2) {
-        // the 64 channels of the F = 2 layout: 16 bytes, widened to kc[0], kc[1] on consume
-        T.kc[0] = *reinterpret_cast<const u32x4 *>((kq >> 1 ? kb[1] : kb[0]) + n16 * CW::k_row +
-                                                   16 * (kq & 1));
-    } else if constexpr (F == 1) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-            T.kc[hf] = *reinterpret_cast<const u32x4 *>(kb[hf] + n16 * kRowCodeBytes + 16 * kq);
-    } else {
-        const uint8_t *src = (kq >> 1 ? kb[1] : kb[0]) + n16 * kRowCodeBytes + 32 * (kq & 1);
-        T.kc[0] = *reinterpret_cast<const u32x4 *>(src);
-        T.kc[1] = *reinterpret_cast<const u32x4 *>(src + 16);
+        const uint32_t page = (uint32_t)pid.page(tb >> a.page_log2);
+        cell[hf] = (page * (uint32_t)a.num_kv_heads + (uint32_t)h) * (uint32_t)P +
+                   (uint32_t)(tb & (P - 1));
     }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
+        const RowBlock<BUF> kb(a.k_codes + (uint64_t)cell[hf] * CW::k_row);
+        T.kc[hf] = kb.template load<typename Tile<CB>::KWords>(la.k, 0);
+    }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const RowBlock<BUF> vb(a.v_codes + (uint64_t)cell[hf] * CW::v_row);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             if constexpr (CW::v2)
-                T.vc[4 * hf + r] = *reinterpret_cast<const uint16_t *>(
-                    vb[hf] + (uint32_t)((4 * kq + r) * CW::v_row + 2 * n16));
+                T.vc[4 * hf + r] = vb.template load<uint16_t>(la.v, r * CW::v_row);
             else
-                T.vc[4 * hf + r] = *reinterpret_cast<const uint32_t *>(
-                    vb[hf] + (uint32_t)((4 * kq + r) * kRowCodeBytes + 4 * n16));
+                T.vc[4 * hf + r] = vb.template load<uint32_t>(la.v, r * kRowCodeBytes);
         }
     }
-    const int ph = (lane >> 4) & 1;
-    T.par = *((lane < 32 ? (ph ? kp[1] : kp[0]) : (ph ? vp[1] : vp[0])) + (lane & 15));
+    // the parameter word of the lane: K (lanes 0..31) or V, first or second half
+    const bool ph = (la.lane & 16) != 0;
+    const uint32_t *kp0 = a.k_params + cell[0], *kp1 = a.k_params + cell[1];
+    const uint32_t *vp0 = a.v_params + cell[0], *vp1 = a.v_params + cell[1];
+    T.par = *((la.lane < 32 ? (ph ? kp1 : kp0) : (ph ? vp1 : vp0)) + (la.lane & 15));
 }
 
 // B operands of QK^T in lane order: the query rounded to integers q = round(q' 2^f)
 // (|q| <= 2^20, one f per KV head) and cut into int8 digits q = 2^16 hi + 2^8 mid + lo.
 //   F = 1: v[par][digit][lane], element byte e of lane (n16, kq): channel 32 kq + 2 e + par
 //          of head n16;
-//   F = 2: v[2 j + par][digit][lane]: channel 64 (kq % 2) + 32 j + 2 e + par of head n16 % 8
-//          for lanes with (n16 / 8) == (kq / 2), zero for the others.
+//   F = 2: v[2 j + par][digit][lane]: the same channel, of head n16 % 8, in the steps of
+//          half j for the columns of that half (n16 / 8 == j), zero for the others.
 template <int F>
 struct QOperand {
     i32x4 v[2 * F][3][64];
@@ -438,7 +498,7 @@ struct WaveState {
 // One tile for NB blocks of 16 MFMA columns (NB > 1: extend, several query rows per wave):
 // the parameters, the K operands and the V operands are built once and serve every block.
 template <int F, bool EXT, int CB, int NB>
-__device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile &T, int t0, int t_end,
+__device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile<CB> &T, int t0, int t_end,
                                              int lane, float kscale, const QOperand<F> *qop,
                                              ParLds &pl, const int (&col_len)[NB], int mask_from)
 {
@@ -481,10 +541,7 @@ __device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile &T,
     if constexpr (F == 1) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            u32x4 w = T.kc[hf];
-            if constexpr (CodeWidths<CB>::k2)
-                w = u32x4{spread2(T.kc[hf].x & 0xFFFFu), spread2(T.kc[hf].x >> 16),
-                          spread2(T.kc[hf].y & 0xFFFFu), spread2(T.kc[hf].y >> 16)};
+            const u32x4 w = k_nibbles(T.kc[hf]);
             const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
             const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
 #pragma unroll
@@ -501,15 +558,11 @@ __device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile &T,
             }
         }
     } else {
+        // the two halves' steps accumulate into one result (B zero outside each half)
         i32x4 dg[3] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            u32x4 w = T.kc[j];
-            if constexpr (CodeWidths<CB>::k2) {
-                const uint32_t d0 = j ? T.kc[0].z : T.kc[0].x, d1 = j ? T.kc[0].w : T.kc[0].y;
-                w = u32x4{spread2(d0 & 0xFFFFu), spread2(d0 >> 16), spread2(d1 & 0xFFFFu),
-                          spread2(d1 >> 16)};
-            }
+            const u32x4 w = k_nibbles(T.kc[j]);
             const i32x4 ev = __builtin_bit_cast(i32x4, w & kNibBytes);
             const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
 #pragma unroll
@@ -793,8 +846,8 @@ void decode_split_kernel(DecodeArgs a)
         const int n = ln & 15, q4 = ln >> 4;
         const int par = slot & 1, jj = slot >> 1;
         const int g = blk * 16 + (F == 2 ? (n & 7) : n);
-        const bool live = g < ncols && (F == 1 || (n >> 3) == (q4 >> 1));
-        const int ch0 = F == 2 ? 64 * (q4 & 1) + 32 * jj + par : 32 * q4 + par;
+        const bool live = g < ncols && (F == 1 || (n >> 3) == jj);
+        const int ch0 = 32 * q4 + par;
         uint32_t dig[3][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -852,6 +905,8 @@ void decode_split_kernel(DecodeArgs a)
     // ---- a7: page walk, one tile ahead of the math --------------------------------------
     const int32_t *ptab = a.page_table + (int64_t)s * a.max_pages;
     ParLds &pl = lds_par[wave];
+    LaneAddr la;
+    la.init<CB>(lane);
     // the range in chunks of at most 1024 tokens: starting 32-aligned, a chunk spans at most
     // 64 pages of 16 tokens, whose ids one register holds
     for (int cb = t_begin; cb < t_end; cb += 1024) {
@@ -864,9 +919,9 @@ void decode_split_kernel(DecodeArgs a)
         // same loads are in flight at every point of the loop and the wait before a tile
         // covers only that tile's loads.
         const int t_last = cb + (ce - 1 - cb) / kTile * kTile;
-        Tile A, B;
-        load_tile<F, CB>(A, a, pid, h, cb, ce, lane);
-        load_tile<F, CB>(B, a, pid, h, min(cb + kTile, t_last), ce, lane);
+        Tile<CB> A, B;
+        load_tile<CB, !EXT>(A, a, pid, h, cb, ce, la);
+        load_tile<CB, !EXT>(B, a, pid, h, min(cb + kTile, t_last), ce, la);
         int t0 = cb;
         while (true) {
             consume_tile<F, EXT, CB, NB>(st, A, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
@@ -875,7 +930,7 @@ void decode_split_kernel(DecodeArgs a)
                 st[b].tick();
             if (t0 + kTile >= ce)
                 break;
-            load_tile<F, CB>(A, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
+            load_tile<CB, !EXT>(A, a, pid, h, min(t0 + 2 * kTile, t_last), ce, la);
             t0 += kTile;
             consume_tile<F, EXT, CB, NB>(st, B, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
 #pragma unroll
@@ -883,7 +938,7 @@ void decode_split_kernel(DecodeArgs a)
                 st[b].tick();
             if (t0 + kTile >= ce)
                 break;
-            load_tile<F, CB>(B, a, pid, h, min(t0 + 2 * kTile, t_last), ce, lane);
+            load_tile<CB, !EXT>(B, a, pid, h, min(t0 + 2 * kTile, t_last), ce, la);
             t0 += kTile;
         }
     }
