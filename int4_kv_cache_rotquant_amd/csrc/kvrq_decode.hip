@@ -70,17 +70,68 @@ __device__ __forceinline__ float dpp_quad_swap2(float x)
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
 }
 
-// Query rotation: a quad holds one query row, lane ql the channels
-// [32 ql, 32 ql + 32); widths up to 16 in-lane, 32 and 64 across the quad.
+// DPP moves inside a 16-lane row: partner lane seg ^ 1, ^ 2, ^ 4, ^ 8.
+__device__ __forceinline__ float dpp_xor1(float x) { return dpp_quad_swap1(x); }
+__device__ __forceinline__ float dpp_xor2(float x) { return dpp_quad_swap2(x); }
+__device__ __forceinline__ float dpp_xor4(float x)
+{
+    // reverse the quad (lane ^ 3), then mirror the half row (lane ^ 7)
+    const int r = __builtin_amdgcn_mov_dpp(__float_as_int(x), 0x1B, 0xF, 0xF, true);
+    return __int_as_float(__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor8(float x) { return dpp_row_ror8(x); }
+
+template <int M>
+__device__ __forceinline__ float dpp_xor(float x)
+{
+    if constexpr (M == 1)
+        return dpp_xor1(x);
+    else if constexpr (M == 2)
+        return dpp_xor2(x);
+    else if constexpr (M == 4)
+        return dpp_xor4(x);
+    else
+        return dpp_xor8(x);
+}
+
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_xor1(x);
+    x += dpp_xor2(x);
+    x += dpp_xor4(x);
+    return x + dpp_xor8(x);
+}
+
+__device__ __forceinline__ float row16_max(float x)
+{
+    x = fmaxf(x, dpp_xor1(x));
+    x = fmaxf(x, dpp_xor2(x));
+    x = fmaxf(x, dpp_xor4(x));
+    return fmaxf(x, dpp_xor8(x));
+}
+
+// One butterfly stage of width 8 M across lanes seg and seg ^ M: the lower lane keeps
+// u + w, the upper one u - w.
+template <int M>
+__device__ __forceinline__ void butterfly_across(float (&x)[8], int seg)
+{
+    const float sgn = (seg & M) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        x[i] = __builtin_fmaf(x[i], sgn, dpp_xor<M>(x[i]));
+}
+
+// Query rotation: 16 lanes hold one query row, lane seg the channels [8 seg, 8 seg + 8);
+// widths 1, 2, 4 in-lane, 8 .. 64 across the row, in the order of increasing width.
 template <int B>
-__device__ __forceinline__ void rotate_query(float (&x)[32], int ql)
+__device__ __forceinline__ void rotate_query_row(float (&x)[8], int seg)
 {
     if constexpr (B > 1) {
-        constexpr int in_lane = B < 32 ? B : 32;
+        constexpr int in_lane = B < 8 ? B : 8;
 #pragma unroll
         for (int h = 1; h < in_lane; h <<= 1) {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
+            for (int i = 0; i < 8; ++i) {
                 if (i & h)
                     continue;
                 const float u = x[i], w = x[i + h];
@@ -88,20 +139,16 @@ __device__ __forceinline__ void rotate_query(float (&x)[32], int ql)
                 x[i + h] = u - w;
             }
         }
-        if constexpr (B >= 64) {
-            const float sgn = (ql & 1) ? -1.0f : 1.0f;
+        if constexpr (B >= 16)
+            butterfly_across<1>(x, seg);
+        if constexpr (B >= 32)
+            butterfly_across<2>(x, seg);
+        if constexpr (B >= 64)
+            butterfly_across<4>(x, seg);
+        if constexpr (B >= 128)
+            butterfly_across<8>(x, seg);
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-                x[i] = __builtin_fmaf(x[i], sgn, dpp_quad_swap1(x[i]));
-        }
-        if constexpr (B >= 128) {
-            const float sgn = (ql & 2) ? -1.0f : 1.0f;
-#pragma unroll
-            for (int i = 0; i < 32; ++i)
-                x[i] = __builtin_fmaf(x[i], sgn, dpp_quad_swap2(x[i]));
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
+        for (int i = 0; i < 8; ++i)
             x[i] *= InvSqrtF<B>::value;
     }
 }
@@ -772,104 +819,97 @@ void decode_split_kernel(DecodeArgs a)
     __shared__ float lds_m[kDecodeWaves][kSlots];
     __shared__ float lds_l[kDecodeWaves][kSlots];
     __shared__ float lds_qsum[kMaxGroup * NB];
-    __shared__ float lds_amax[NB];
-    __shared__ float lds_kscale;
-    float(*q_lds)[kHeadDim + 4] = reinterpret_cast<float(*)[kHeadDim + 4]>(&lds_o[0][0][0]);
+    __shared__ float lds_amax[kDecodeWaves];
 
-    // ---- a6: waves 0 .. NB-1 rotate the queries of this KV head (16 columns each), fold
-    // sm_scale * log2(e), and round them to one integer grid
-    const int g = wave * 16 + (lane >> 2), ql = lane & 3;
-    float x[32];
-    float amax = 0.0f, sum = 0.0f;
-    if (wave < NB) {
+    // ---- a6: the query rows of this KV head (16 lanes per row, 8 channels per lane): rotate
+    // them, fold sm_scale * log2(e), round them to one integer grid and cut them into the
+    // int8 digits of the QK^T B operands
+    const int seg = lane & 15;   // channels [8 seg, 8 seg + 8)
+    float x[NB][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int g = b * 16 + wave * 4 + (lane >> 4);
         if (g < ncols) {
             const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
                                      : (int64_t)s * a.num_q_heads + h * G + g;
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + qrow * kHeadDim + 32 * ql);
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(a.q + qrow * kHeadDim + 8 * seg);
+            const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u32x4 w = src[j];
-                const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    x[8 * j + 2 * m] = __uint_as_float(d[m] << 16);
-                    x[8 * j + 2 * m + 1] = __uint_as_float(d[m] & 0xFFFF0000u);
-                }
+            for (int m = 0; m < 4; ++m) {
+                x[b][2 * m] = __uint_as_float(d[m] << 16);
+                x[b][2 * m + 1] = __uint_as_float(d[m] & 0xFFFF0000u);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-                x[i] = 0.0f;
+            for (int i = 0; i < 8; ++i)
+                x[b][i] = 0.0f;
         }
-        rotate_query<BK>(x, ql);
+        rotate_query_row<BK>(x[b], seg);
+        float sum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            x[i] *= a.q_scale;
-            amax = fmaxf(amax, fabsf(x[i]));
-            sum += x[i];
+        for (int i = 0; i < 8; ++i) {
+            x[b][i] *= a.q_scale;
+            amax = fmaxf(amax, fabsf(x[b][i]));
+            sum += x[b][i];
         }
-        sum += dpp_quad_swap1(sum);
-        sum += dpp_quad_swap2(sum);
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1)
-            amax = fmaxf(amax, wave_xor(amax, o));
-        if (lane == 0)
-            lds_amax[wave] = amax;
-    }
-    if constexpr (NB > 1)
-        __syncthreads();
-    if (wave < NB) {
-        if constexpr (NB > 1) {
-            amax = lds_amax[0];
-#pragma unroll
-            for (int b = 1; b < NB; ++b)
-                amax = fmaxf(amax, lds_amax[b]);
-        }
-        // one power-of-two factor 2^f for all columns: max |q' 2^f| in [2^19, 2^20)
-        int e = 0;
-        if (amax > 0.0f)
-            frexpf(amax, &e);
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            q_lds[g][32 * ql + i] = ldexpf(x[i], 20 - e);
-        if (ql == 0 && g < kMaxGroup * NB)
+        sum = row16_sum(sum);
+        if (seg == 0 && g < kMaxGroup * NB)
             lds_qsum[g] = sum;
-        if (wave == 0 && lane == 0)
-            lds_kscale = ldexpf(1.0f, e - 20);
+    }
+    amax = col_max(row16_max(amax));
+    if (lane == 0)
+        lds_amax[wave] = amax;
+    // the B operands start as zeros: rows past the columns and, for F = 2, the other
+    // half's steps stay so
+    {
+        constexpr int kWords = (int)(sizeof(QOperand<F>) * NB / 16);
+        i32x4 *z = reinterpret_cast<i32x4 *>(&qop[0]);
+        for (int i = tid; i < kWords; i += 64 * kDecodeWaves)
+            z[i] = i32x4{0, 0, 0, 0};
     }
     __syncthreads();
-
-    // B operands of QK^T: int8 digits of the integer query in lane order
-    for (int i = tid; i < 2 * F * 64 * NB; i += 64 * kDecodeWaves) {
-        const int blk = i / (2 * F * 64), ib = i - blk * (2 * F * 64);
-        const int slot = ib >> 6, ln = ib & 63;   // slot = 2 j + par (F = 2) or par (F = 1)
-        const int n = ln & 15, q4 = ln >> 4;
-        const int par = slot & 1, jj = slot >> 1;
-        const int g = blk * 16 + (F == 2 ? (n & 7) : n);
-        const bool live = g < ncols && (F == 1 || (n >> 3) == jj);
-        const int ch0 = 32 * q4 + par;
-        uint32_t dig[3][4];
+    // one power-of-two factor 2^f for all columns: max |q' 2^f| in [2^19, 2^20)
+    amax = fmaxf(fmaxf(lds_amax[0], lds_amax[1]), fmaxf(lds_amax[2], lds_amax[3]));
+    int e = 0;
+    if (amax > 0.0f)
+        frexpf(amax, &e);
+    const float grid = ldexpf(1.0f, 20 - e);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            dig[0][j] = dig[1][j] = dig[2][j] = 0u;
-        if (live) {
+    for (int b = 0; b < NB; ++b) {
+        const int g = b * 16 + wave * 4 + (lane >> 4);
+        if (g < ncols) {
+            // q = round(q' 2^f) (|q| <= 2^20) from the bits of q' 2^f + 1.5 2^23, offset by
+            // 128 (1 + 2^8 + 2^16) so that its three low bytes are the balanced int8 digits
+            // + 128: q = 2^16 hi + 2^8 mid + lo, each digit in [-128, 127]
+            uint32_t u[8];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int32_t q = (int32_t)rintf(q_lds[g][ch0 + 2 * e]);
-                const int32_t lo = ((q + 128) & 255) - 128;
-                const int32_t r1 = (q - lo) >> 8;
-                const int32_t mid = ((r1 + 128) & 255) - 128;
-                const int32_t hi = (r1 - mid) >> 8;
-                const int sh = 8 * (e & 3);
-                dig[0][e >> 2] |= uint32_t(hi & 255) << sh;
-                dig[1][e >> 2] |= uint32_t(mid & 255) << sh;
-                dig[2][e >> 2] |= uint32_t(lo & 255) << sh;
+            for (int i = 0; i < 8; ++i)
+                u[i] = __float_as_uint(__builtin_fmaf(x[b][i], grid, 0x1.8p23f)) +
+                       (0x808080u - 0x4B400000u);
+            // element e of a lane's B operand is channel 32 kq + 2 e + par: this lane's
+            // channels of one parity are bytes 0..3 of its dword seg % 4 in lane
+            // column + 16 (seg / 4)
+            const int col = F == 2 ? g : g - b * 16;
+            const int ln = col + 16 * (seg >> 2);
+#pragma unroll
+            for (int par = 0; par < 2; ++par) {
+#pragma unroll
+                for (int dg = 0; dg < 3; ++dg) {
+                    const uint32_t k = 2 - dg;   // byte of the digit: hi 2, mid 1, lo 0
+                    const uint32_t lo = __builtin_amdgcn_perm(u[par + 2], u[par], 0x0C0C0400u + k * 0x101u);
+                    const uint32_t hi = __builtin_amdgcn_perm(u[par + 6], u[par + 4], 0x0C0C0400u + k * 0x101u);
+                    const int32_t word = (int32_t)((lo | (hi << 16)) ^ 0x80808080u);
+                    if constexpr (F == 2) {
+                        // the same digits in both halves' steps: half j at column g + 8 j
+                        reinterpret_cast<int32_t *>(&qop[0].v[par][dg][ln])[seg & 3] = word;
+                        reinterpret_cast<int32_t *>(&qop[0].v[2 + par][dg][ln + 8])[seg & 3] = word;
+                    } else {
+                        reinterpret_cast<int32_t *>(&qop[b].v[par][dg][ln])[seg & 3] = word;
+                    }
+                }
             }
         }
-#pragma unroll
-        for (int d = 0; d < 3; ++d)
-            qop[blk].v[slot][d][ln] = i32x4{int32_t(dig[d][0]), int32_t(dig[d][1]),
-                                            int32_t(dig[d][2]), int32_t(dig[d][3])};
     }
     const int n16 = lane & 15;
     const int kq = lane >> 4;
@@ -880,7 +920,7 @@ void decode_split_kernel(DecodeArgs a)
     const int mask_from = pos0 + 1;
     WaveState st[NB];
     // K lanes scale by 2^-f (the integer query's grid), V lanes by 1
-    const float kscale = lane < 32 ? lds_kscale : 1.0f;
+    const float kscale = lane < 32 ? ldexpf(1.0f, e - 20) : 1.0f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int gb = b * 16 + gl;
@@ -900,7 +940,7 @@ void decode_split_kernel(DecodeArgs a)
         for (int c = 0; c < 8; ++c)
             st[b].acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    __syncthreads();   // q_lds is reused below, qop is complete
+    __syncthreads();   // qop is complete
 
     // ---- a7: page walk, one tile ahead of the math --------------------------------------
     const int32_t *ptab = a.page_table + (int64_t)s * a.max_pages;
