@@ -809,9 +809,15 @@ void decode_split_kernel(DecodeArgs a)
     const int t_begin = wg_begin + (wave * n_tiles / kDecodeWaves) * kTile;
     const int t_end = min(wg_end, wg_begin + ((wave + 1) * n_tiles / kDecodeWaves) * kTile);
 
-    // rotated query rows in the prologue, the waves' partial states in the epilogue
-    // (F = 2: the two halves of each column are merged inside the wave first, so one slot
-    // per query head and wave)
+    // the first chunk's page ids are requested before the query prologue, so their latency
+    // overlaps it
+    const int32_t *ptab = a.page_table + (int64_t)s * a.max_pages;
+    PageIds pid;
+    if (t_begin < t_end)
+        pid.fill(a, ptab, t_begin >> a.page_log2, lane);
+
+    // the waves' partial states in the epilogue (F = 2: the two halves of each column are
+    // merged inside the wave first, so one slot per query head and wave)
     constexpr int kSlots = F == 2 ? 8 : 16;
     __shared__ float lds_o[kDecodeWaves][kSlots][kHeadDim + 4];
     __shared__ QOperand<F> qop[NB];
@@ -943,7 +949,6 @@ void decode_split_kernel(DecodeArgs a)
     __syncthreads();   // qop is complete
 
     // ---- a7: page walk, one tile ahead of the math --------------------------------------
-    const int32_t *ptab = a.page_table + (int64_t)s * a.max_pages;
     ParLds &pl = lds_par[wave];
     LaneAddr la;
     la.init<CB>(lane);
@@ -951,14 +956,14 @@ void decode_split_kernel(DecodeArgs a)
     // 64 pages of 16 tokens, whose ids one register holds
     for (int cb = t_begin; cb < t_end; cb += 1024) {
         const int ce = min(t_end, cb + 1024);
-        PageIds pid;
-        pid.fill(a, ptab, cb >> a.page_log2, lane);
         // two register tiles, each refilled with the tile two ahead right after it is
         // consumed (at most 128 VGPRs, so four waves share a SIMD).  The loads are
         // unconditional (a prefetch past the end re-reads the last tile, an L2 hit), so the
         // same loads are in flight at every point of the loop and the wait before a tile
         // covers only that tile's loads.
         const int t_last = cb + (ce - 1 - cb) / kTile * kTile;
+        if (cb != t_begin)
+            pid.fill(a, ptab, cb >> a.page_log2, lane);
         Tile<CB> A, B;
         load_tile<CB, !EXT>(A, a, pid, h, cb, ce, la);
         load_tile<CB, !EXT>(B, a, pid, h, min(cb + kTile, t_last), ce, la);
