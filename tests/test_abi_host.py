@@ -215,6 +215,12 @@ def test_cache_sizes(K):
     with pytest.raises(K.KvrqError) as e:
         K.kvrq_cache_sizes(_desc(K, k_bits=3))
     assert e.value.status == K.KVRQ_EUNSUPPORTED
+    # (page, head, token) cells are 32-bit indexes in the kernels: 2^32 cells at most
+    kb, vb, pb = K.kvrq_cache_sizes(_desc(K, num_kv_heads=64, page_size=1024, num_pages=1 << 16))
+    assert kb == (1 << 32) * 64
+    with pytest.raises(K.KvrqError) as e:
+        K.kvrq_cache_sizes(_desc(K, num_kv_heads=65, page_size=1024, num_pages=1 << 16))
+    assert e.value.status == K.KVRQ_EINVAL and "2^32" in str(e.value)
 
 
 def test_pool_identity_order_and_slots(K):
