@@ -56,11 +56,28 @@ MFMA_ATTENTION_PEAK_TFLOPS = 1.0 / (0.5 / 5000.0 + 0.5 / 2500.0)
 D = 128
 
 
+# Default (timed steps, warmup steps) per workload: the warmup keeps the GPU busy long enough
+# for its clocks to settle (a 5-step warmup read the chunked-prefill extend 18% slow and the
+# Qwen3-32B-like decode 7% slow), and the timed region lasts a few hundred milliseconds.
+DEFAULT_STEPS = {
+    "tiny": (1000, 1000),
+    "qwen3_4b_like": (3000, 3000),            # ~0.073 ms per step
+    "prefill_chunk": (4000, 4000),            # ~0.05 ms
+    "qwen3_32b_like_decode": (400, 400),      # ~0.65 ms
+    "long_context": (150, 150),               # ~1.9 ms
+    "chunked_prefill": (250, 250),            # ~1.3 ms
+    "small_batch_decode": (10000, 10000),     # ~0.02 ms
+}
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: per workload, about 0.2-0.4 s of GPU time)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: per workload, as long as the timed ones: "
+                         "MI355X clocks ramp up over the first few hundred milliseconds of load)")
     ap.add_argument("--workload", default="qwen3_4b_like", choices=sorted(W.WORKLOADS))
     ap.add_argument("--variant", default="bdr", choices=["bdr", "plain", "bf16", "fused"],
                     help="prefill_chunk: fused BDR write, plain INT4 write, or bf16 paged copy; "
@@ -81,6 +98,11 @@ def parse_args(argv=None):
     ap.add_argument("--profiled-args", default="",
                     help="with --parse-counters: the bench.py arguments the two --pmc runs used")
     args = ap.parse_args(argv)
+    steps, warmup = DEFAULT_STEPS[args.workload]
+    if args.steps is None:
+        args.steps = steps
+    if args.warmup is None:
+        args.warmup = warmup
     if args.counters is None:
         args.counters = os.path.join(ROOT, "profiles", f"hbm_counters.{workload_tag(args)}.json")
     return args
