@@ -593,15 +593,19 @@ __device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile<CB>
             const i32x4 od = __builtin_bit_cast(i32x4, (w >> 4) & kNibBytes);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                i32x4 dg[3];
+                // digits from the top: each partial sum moves up by 2^8 before the next
+                // digit's products are added, ending in the exact int32 dot product
+                i32x4 acc = i32x4{0, 0, 0, 0};
 #pragma unroll
                 for (int d = 0; d < 3; ++d) {
-                    dg[d] = mfma_i8(ev, qop[b].v[0][d][lane], i32x4{0, 0, 0, 0});
-                    dg[d] = mfma_i8(od, qop[b].v[1][d][lane], dg[d]);
+                    if (d)
+                        acc <<= 8;
+                    acc = mfma_i8(ev, qop[b].v[0][d][lane], acc);
+                    acc = mfma_i8(od, qop[b].v[1][d][lane], acc);
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    sc[b][4 * hf + r] = (float)((((dg[0][r] << 8) + dg[1][r]) << 8) + dg[2][r]);
+                    sc[b][4 * hf + r] = (float)acc[r];
             }
         }
     } else {
