@@ -1208,6 +1208,20 @@ __global__ __launch_bounds__(256) void decode_combine_wave_kernel(DecodeArgs a)
     const int g = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (g >= a.num_q_heads)
         return;
+    // the first four splits' outputs and every split's (m, l) are requested before the row's
+    // length is known, so one memory round trip serves rows of up to four splits; every row
+    // holds max_splits slots, so these loads stay inside the workspace whatever the length
+    const int64_t row0 = ((int64_t)s * a.num_q_heads + g) * a.max_splits;
+    const float *po = a.part_o + row0 * kHeadDim + 2 * lane;
+    constexpr int kEarly = 4;
+    float2 v0[kEarly];
+#pragma unroll
+    for (int k = 0; k < kEarly; ++k)
+        if (k < a.max_splits)
+            v0[k] = *reinterpret_cast<const float2 *>(po + (int64_t)k * kHeadDim);
+    float2 ml = make_float2(-INFINITY, 0.0f);
+    if (lane < a.max_splits)
+        ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * (row0 + lane));
     const int L = row_length(a, s);
     float *out = a.out + ((int64_t)s * a.num_q_heads + g) * kHeadDim;
     if (L <= 0) {
@@ -1215,25 +1229,21 @@ __global__ __launch_bounds__(256) void decode_combine_wave_kernel(DecodeArgs a)
         return;
     }
     const int n = (L + a.split_tokens - 1) / a.split_tokens;   // 1..64
-    const int64_t row0 = ((int64_t)s * a.num_q_heads + g) * a.max_splits;
-    float m = -INFINITY, l = 0.0f;
-    if (lane < n) {
-        const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * (row0 + lane));
-        m = ml.x;
-        l = ml.y;
-    }
-    float M = m;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        M = fmaxf(M, wave_xor(M, o));
+    const float m = lane < n ? ml.x : -INFINITY, l = lane < n ? ml.y : 0.0f;
+    // wave-wide max and sum by row permutes (no LDS round trips)
+    const float M = col_max(row16_max(m));
     const float wj = lane < n ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-    float lsum = wj * l;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        lsum += wave_xor(lsum, o);
-    const float *po = a.part_o + row0 * kHeadDim + 2 * lane;
+    const float lsum = col_sum(row16_sum(wj * l));
     float o0 = 0.0f, o1 = 0.0f;
-    int i = 0;
+#pragma unroll
+    for (int k = 0; k < kEarly; ++k) {
+        if (k < n) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), k));
+            o0 = fmaf(w, v0[k].x, o0);
+            o1 = fmaf(w, v0[k].y, o1);
+        }
+    }
+    int i = kEarly;
     for (; i + 4 <= n; i += 4) {
         float2 v[4];
 #pragma unroll
