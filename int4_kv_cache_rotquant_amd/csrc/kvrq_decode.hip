@@ -51,28 +51,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-template <int B> struct InvSqrtF;
-template <> struct InvSqrtF<16> { static constexpr float value = 0x1p-2f; };
-template <> struct InvSqrtF<32> { static constexpr float value = 0x1.6a09e6p-3f; };
-template <> struct InvSqrtF<64> { static constexpr float value = 0x1p-3f; };
-template <> struct InvSqrtF<128> { static constexpr float value = 0x1.6a09e6p-4f; };
-
-__device__ __forceinline__ float dpp_quad_swap1(float x)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-}
 __device__ __forceinline__ float dpp_row_ror8(float x)
 {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float dpp_quad_swap2(float x)
-{
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-}
 
 // DPP moves inside a 16-lane row: partner lane seg ^ 1, ^ 2, ^ 4, ^ 8.
-__device__ __forceinline__ float dpp_xor1(float x) { return dpp_quad_swap1(x); }
-__device__ __forceinline__ float dpp_xor2(float x) { return dpp_quad_swap2(x); }
+__device__ __forceinline__ float dpp_xor1(float x) { return quad_swap1(x); }
+__device__ __forceinline__ float dpp_xor2(float x) { return quad_swap2(x); }
 __device__ __forceinline__ float dpp_xor4(float x)
 {
     // reverse the quad (lane ^ 3), then mirror the half row (lane ^ 7)
@@ -149,7 +135,7 @@ __device__ __forceinline__ void rotate_query_row(float (&x)[8], int seg)
             butterfly_across<8>(x, seg);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            x[i] *= InvSqrtF<B>::value;
+            x[i] *= InvSqrt<B>::value;
     }
 }
 
@@ -701,8 +687,8 @@ __device__ __forceinline__ void inverse_rotate_pair(float &o0, float &o1, int la
             o0 = upper ? p0 - o0 : o0 + p0;
             o1 = upper ? p1 - o1 : o1 + p1;
         }
-        o0 *= InvSqrtF<BV>::value;
-        o1 *= InvSqrtF<BV>::value;
+        o0 *= InvSqrt<BV>::value;
+        o1 *= InvSqrt<BV>::value;
     }
 }
 
