@@ -720,18 +720,18 @@ __device__ __forceinline__ void write_new_rows(const DecodeArgs &a, int s, int h
     for (int j = 0; j < 4; ++j)
         bf16x8_to_f32(reinterpret_cast<const u32x4 *>(src)[j], x + 8 * j);
     if (!is_v) {
-        encode_row<BK, true>(x, slot, a.k_codes_w, a.k_params_w, a.num_slots, a.num_kv_heads,
+        encode_row<BK, 0>(x, slot, a.k_codes_w, a.k_params_w, a.num_slots, a.num_kv_heads,
                              a.page_log2, h, ql, a.k_bits);
         return;
     }
     uint8_t *vc = a.v_codes_w;
     uint32_t *vp = a.v_params_w;
     switch (a.v_block) {
-    case 16: encode_row<16, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
-    case 32: encode_row<32, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
-    case 64: encode_row<64, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
-    case 128: encode_row<128, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
-    default: encode_row<0, true>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
+    case 16: encode_row<16, 0>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
+    case 32: encode_row<32, 0>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
+    case 64: encode_row<64, 0>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
+    case 128: encode_row<128, 0>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
+    default: encode_row<0, 0>(x, slot, vc, vp, a.num_slots, a.num_kv_heads, a.page_log2, h, ql, a.v_bits); break;
     }
 }
 

@@ -86,17 +86,18 @@ __device__ __forceinline__ void rotate_row(float (&x)[32], int ql)
 }
 
 // Rotate, quantise and store one row held in x; called by all four lanes of the quad.
-// bits = 4: 15 levels, two codes per byte, 64-byte rows; bits = 2: 3 levels, four codes
-// per byte (channel d at bit 2 (d % 4) of byte d / 4), 32-byte rows.  With NARROW false
-// only 4 bits are compiled (bits is ignored), so the INT4 kernels carry no 2-bit code.
-template <int B, bool NARROW = false>
+// 4 bits: 15 levels, two codes per byte, 64-byte rows; 2 bits: 3 levels, four codes per
+// byte (channel d at bit 2 (d % 4) of byte d / 4), 32-byte rows.  BITS fixes the width at
+// compile time (4 or 2); BITS = 0 takes it from `bits` at run time.
+template <int B, int BITS = 4>
 __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t *__restrict__ codes,
                                            uint32_t *__restrict__ params, int64_t num_slots,
                                            int num_kv_heads, int page_log2, int h, int ql,
                                            int bits = 4)
 {
 #pragma clang fp contract(off)
-    const bool two = NARROW && bits == 2;
+    static_assert(BITS == 4 || BITS == 2 || BITS == 0, "code widths: 4, 2, or run time");
+    const bool two = BITS == 2 || (BITS == 0 && bits == 2);
     rotate_row<B>(x, ql);
 
     float mn = x[0], mx = x[0];

@@ -59,7 +59,7 @@ __device__ __forceinline__ void load_row(RowLoad &R, const uint16_t *src_base, i
 // heads of the same tokens (whole 2 KB-per-token input rows at once).  The loop is
 // unrolled over the two tensors, so each half is compiled for its own block size, and
 // K and V work is spread evenly over the waves.
-template <int BK, int BV, bool NARROW>
+template <int BK, int BV, int KBITS, int VBITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWriteWavesPerSimd)))
 void rotquant_write_kernel(WriteArgs a)
 {
@@ -97,16 +97,16 @@ void rotquant_write_kernel(WriteArgs a)
             bf16x8_to_f32(RK.raw[j], x + 8 * j);
         int32_t slot = RK.valid ? RK.slot : -1;
         issue(RK, a.k, a.k_stride, pf);
-        encode_row<BK, NARROW>(x, slot, a.k_codes, a.k_params, a.num_slots, a.num_kv_heads,
-                               a.page_log2, h, ql, a.k_bits);
+        encode_row<BK, KBITS>(x, slot, a.k_codes, a.k_params, a.num_slots, a.num_kv_heads,
+                              a.page_log2, h, ql);
 
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             bf16x8_to_f32(RV.raw[j], x + 8 * j);
         slot = RV.valid ? RV.slot : -1;
         issue(RV, a.v, a.v_stride, pf);
-        encode_row<BV, NARROW>(x, slot, a.v_codes, a.v_params, a.num_slots, a.num_kv_heads,
-                               a.page_log2, h, ql, a.v_bits);
+        encode_row<BV, VBITS>(x, slot, a.v_codes, a.v_params, a.num_slots, a.num_kv_heads,
+                              a.page_log2, h, ql);
         if (!more)
             break;
         pair = next;
@@ -169,11 +169,16 @@ unsigned write_grid(const WriteArgs &a)
 template <int BK, int BV>
 hipError_t launch_bk_bv(const WriteArgs &a, hipStream_t s)
 {
-    // INT4 pools take the kernel without 2-bit code; a 2-bit pool the one that branches
-    if (a.k_bits == 2 || a.v_bits == 2)
-        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, true>), dim3(write_grid(a)), dim3(256), 0, s, a);
+    // the code widths are template arguments, so each kernel carries one encoder per tensor
+    const dim3 grid(write_grid(a));
+    if (a.k_bits == 2 && a.v_bits == 2)
+        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 2, 2>), grid, dim3(256), 0, s, a);
+    else if (a.k_bits == 2)
+        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 2, 4>), grid, dim3(256), 0, s, a);
+    else if (a.v_bits == 2)
+        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 4, 2>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, false>), dim3(write_grid(a)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 4, 4>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
