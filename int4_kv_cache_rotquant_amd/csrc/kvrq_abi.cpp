@@ -131,10 +131,15 @@ kvrq::DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max
         // tokens per wave: enough (sequence, KV head, split) workgroups to fill the chip,
         // at least 8 tiles per wave so the per-workgroup query set-up and the combine stay
         // small (measured: 1024-token splits beat 512 and 256 on 16 x 1-4k sequences), at
-        // most 1024 (one register of page ids)
+        // most 1024 (one register of page ids) ...
         const int64_t work = int64_t(num_seqs) * num_kv_heads * std::max<int32_t>(max_seq_len, 1);
         int64_t wt = work / 8192;
         wt = std::max<int64_t>(256, std::min<int64_t>(1024, wt));
+        // ... but no more than 64 splits, which one wave per output row combines (a 1M-token
+        // sequence: 16k-token splits measured 5% faster than 4k ones and their 256-way
+        // combine); longer ranges are walked in 1024-token chunks
+        wt = std::max<int64_t>(wt, (int64_t(max_seq_len) + 64 * kvrq::kDecodeWaves - 1) /
+                                       (64 * kvrq::kDecodeWaves));
         wt = (wt + kvrq::kTile - 1) / kvrq::kTile * kvrq::kTile;
         split_tokens = (int32_t)(wt * kvrq::kDecodeWaves);
     }
