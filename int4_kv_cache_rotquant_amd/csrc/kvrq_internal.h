@@ -78,6 +78,8 @@ struct DecodeArgs {
     int32_t max_pages;
     int32_t split_tokens;
     int32_t max_splits;
+    // decode grid order: 0 = (split, KV head, sequence), 1 = (sequence, KV head, split)
+    int32_t seq_major = 0;
     float q_scale;              // sm_scale * log2(e)
     // extend (chunked prefill) only; qo_start == nullptr for the decode.  The output
     // rows are then query rows: q, out [total_q][Hq][128], part_* [total_q][Hq][splits]
@@ -111,5 +113,7 @@ int launch_device_copy(void *dst, const void *src, size_t bytes, void *stream);
 // decode, or extend when a.qo_start is set
 int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream);
 const char *hip_error_string(int err);
+// compute units of the current device (read once per process; 256 if the query fails)
+int device_cus();
 
 }  // namespace kvrq

@@ -152,13 +152,7 @@ __global__ __launch_bounds__(256) void device_copy_kernel(u32x4 *__restrict__ ds
 // then walks several tiles so its next loads overlap its current arithmetic.
 unsigned write_grid(const WriteArgs &a)
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-    }
+    const int cus = device_cus();
     // one wave per (K, V) tile pair at most, four waves per workgroup
     const int64_t pairs = (a.num_tokens + kWriteTile - 1) / kWriteTile * a.num_kv_heads;
     const int64_t wgs = (pairs + 3) / 4;
@@ -196,6 +190,19 @@ hipError_t launch_bv(int v_block, const WriteArgs &a, hipStream_t s)
 }
 
 }  // namespace
+
+int device_cus()
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus = n;
+    }
+    return cus;
+}
 
 int launch_rotquant_write(int k_block, int v_block, const WriteArgs &a, void *stream)
 {
