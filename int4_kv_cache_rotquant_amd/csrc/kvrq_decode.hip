@@ -10,8 +10,10 @@
 // orthonormal, hence its own inverse).
 //
 // Launch 1 -- decode_split_kernel, one workgroup of four 64-lane waves per
-// (split, KV head, sequence) -- for the extend, per (row block, KV head, split); the
-// waves share the split's 32-token tiles evenly, the next tiles' loads in flight while
+// (split, KV head, sequence) (sequences vary fastest when the whole grid is resident, so
+// a sequence's workgroups share one XCD) -- for the extend, per (row block, KV head,
+// split).  The four waves first prepare the query operands together (16 lanes per row),
+// then share the split's 32-token tiles evenly, the next tiles' loads in flight while
 // one is consumed:
 //   QK^T  S[t][c] = sum_d code_K[t][d] q[d][c] on int8 MFMA 16x16x64: A = the
 //         INT4 codes as bytes, B = the rotated queries of the MFMA columns rounded to
