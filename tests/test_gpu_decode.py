@@ -6,7 +6,8 @@ Covers the tiny case (G=1), the Qwen3-4B-like layer (G=4, 16 ragged sequences, p
 scattered), the high-concurrency shape (G=8, 256 log-normal sequences, sampled
 sequences checked), the 1M-token long context (G=8, K and V rotated, one KV head
 checked), split-count sweeps, page-table permutation invariance, GQA group sizes
-1..16, page sizes 16..128, every block pair, lengths 0, 1, 15..33 and tail tiles.
+1..16, page sizes 16..128, every block pair, lengths 0, 1, 15..33 and tail tiles, and
+caches of degenerate rows (zero and tiny scales, spiked keys) in decode and extend.
 """
 import math
 
@@ -258,3 +259,60 @@ def test_single_split_writes_the_output(K, G, vb):
     got = out.cpu().numpy()
     assert np.all(got[0] == 0.0)
     decode_compare(got, _ref(orc, q, tab, L, Hkv, 16, 128, vb), f"single split G{G} vb{vb}")
+
+
+def _degenerate_rows(rng, T, Hkv):
+    """K and V rows of every degenerate kind the quantiser has, mixed with ordinary ones:
+    all zero, constant (scale 0), a range far below the values (tiny scale), on the code
+    grid, and K rows with one large channel (peaked scores that move the softmax maximum
+    mid-sequence)."""
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    kind = rng.integers(0, 6, size=T)
+    for t in range(T):
+        if kind[t] == 1:
+            k[t] = 0.0
+            v[t] = 0.0
+        elif kind[t] == 2:
+            k[t] = 1.5
+            v[t] = -2.0
+        elif kind[t] == 3:
+            k[t] = 1.0 + 1e-3 * np.arange(D) / D
+            v[t] = 3.0 - 1e-3 * np.arange(D) / D
+        elif kind[t] == 4:
+            v[t] = -1.0 + (np.arange(D) % 16) / 8.0
+        elif kind[t] == 5:
+            k[t, :, int(rng.integers(0, D))] = 40.0 * (1 + t % 3)
+    return W.f32_to_bf16_bits(k), W.f32_to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("G,kb,vb", [(4, 128, 64), (8, 0, 0), (16, 64, 128)])
+def test_degenerate_rows(K, G, kb, vb):
+    """Decode and extend over caches full of zero-scale, tiny-scale and spiked rows."""
+    import torch
+    Hkv, P = 2, 16
+    lens = np.array([37, 300, 129, 1], np.int32)
+    rng = np.random.default_rng(77 + G)
+    paging = W.assign_pages(np.random.default_rng(78), list(lens), P)
+    T = int(lens.sum())
+    k, v = _degenerate_rows(rng, T, Hkv)
+    slots = np.concatenate([paging.slots(s, 0, int(L)) for s, L in enumerate(lens)])
+    cache = K.PagedInt4Cache(paging.num_pages, Hkv, P, kb, vb, fill=0)
+    K.kv_rotquant_write(cache, bf16_dev(k), bf16_dev(v), to_dev(slots))
+    orc = oracle.Cache(paging.num_pages, Hkv, P, fill=0)
+    oracle.write(orc, k, v, slots, kb, vb)
+    tab = paging.page_table()
+    arrays = (orc.k_codes, orc.v_codes, orc.k_params, orc.v_params)
+    q = W.f32_to_bf16_bits(rng.standard_normal((len(lens), Hkv * G, D)).astype(np.float32))
+    for split in (0, 128):
+        out = _run(K, cache, q, tab, lens, split=split)
+        decode_compare(out, _ref(orc, q, tab, lens, Hkv, P, kb, vb), f"degenerate decode G{G} split {split}")
+    # extend: the last rows of each sequence (up to 40) as a chunk
+    nq = np.minimum(lens, 40)
+    qo = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    qx = W.f32_to_bf16_bits(rng.standard_normal((int(qo[-1]), Hkv * G, D)).astype(np.float32))
+    out = K.kv_int4_paged_extend(cache, bf16_dev(qx), to_dev(qo), to_dev(tab), to_dev(lens),
+                                 int(lens.max()), int(nq.max()))
+    torch.cuda.synchronize()
+    ref = oracle.extend(qx, arrays, qo, tab, lens, Hkv, P, kb, vb)
+    decode_compare(out.cpu().numpy(), ref, f"degenerate extend G{G}")
