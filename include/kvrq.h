@@ -313,8 +313,8 @@ KVRQ_API kvrq_status kvrq_bf16_paged_write(const kvrq_cache_desc *d, void *k_cac
                                   const int32_t *slot_mapping, void *stream);
 
 /* Plain device copy of `bytes` bytes (multiple of 16, both pointers 16-byte
- * aligned): the streaming kernel used to measure achievable HBM bandwidth
- * and to calibrate byte counters. */
+ * aligned; one 16-byte element per lane): the streaming kernel used to measure
+ * achievable HBM bandwidth and to calibrate byte counters. */
 KVRQ_API kvrq_status kvrq_device_copy(void *dst, const void *src, size_t bytes, void *stream);
 
 #ifdef __cplusplus
