@@ -437,21 +437,20 @@ struct WaveState {
     // ---- a9: online softmax (base 2) of one tile's scores, the PV weights as f16 high and
     // low B operands
     template <int F>
+    // smax: the largest V scale among the lane's tokens (the same for every column block)
     __device__ __forceinline__ void softmax(float (&sc)[8 / F], const float (&sv)[8 / F],
-                                            const float (&zv)[8 / F], int lane, f16x8 &bh,
-                                            f16x8 &bl)
+                                            const float (&zv)[8 / F], float smax, int lane,
+                                            f16x8 &bh, f16x8 &bl)
     {
         constexpr int NS = 8 / F;            // scores per lane
         const int sub = F == 2 ? ((lane & 15) >> 3) : 0;
         // Most tiles change nothing: the maximum moves only when a score exceeds it by more
         // than kLazyMax, the weight exponent only when a V scale reaches slim = 2^(6 - E).
         // Lanes test their own scores; the column reductions run only when some lane asks.
-        float tmax = sc[0], smax = sv[0];
+        float tmax = sc[0];
 #pragma unroll
-        for (int i = 1; i < NS; ++i) {
+        for (int i = 1; i < NS; ++i)
             tmax = fmaxf(tmax, sc[i]);
-            smax = max_raw(smax, sv[i]);
-        }
         float alpha = 1.0f;
         if (__builtin_amdgcn_ballot_w64(tmax > m + kLazyMax || smax >= slim)) {
             tmax = col_max(tmax);
@@ -616,6 +615,10 @@ __device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile<CB>
     }
 
     f16x8 bh[NB], bl[NB];
+    float smax = sv[0];
+#pragma unroll
+    for (int i = 1; i < NS; ++i)
+        smax = max_raw(smax, sv[i]);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -630,7 +633,7 @@ __device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile<CB>
                     sc[b][i] = t0 + 16 * (i >> 2) + kq4 + (i & 3) < col_len[b] ? sc[b][i] : -INFINITY;
             }
         }
-        st[b].template softmax<F>(sc[b], sv, zv, lane, bh[b], bl[b]);
+        st[b].template softmax<F>(sc[b], sv, zv, smax, lane, bh[b], bl[b]);
     }
 
     // ---- PV: A = V codes (rows: channel 8 n16 + b, k: the 8 tokens), B = weights -------
