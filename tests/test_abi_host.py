@@ -116,6 +116,13 @@ def test_decode_validation(K):
     small = size.value
     ws(_desc(K), split=128)
     assert size.value > small
+    # the automatic split keeps at most 64 splits (one wave combines them): a 1M-token
+    # sequence takes 16,384-token splits, partials of 128 + 2 floats per (row, head, split)
+    assert ws(_desc(K), S=1, maxlen=1 << 20) == K.KVRQ_OK
+    assert size.value == 1 * 64 * 64 * (128 + 2) * 4
+    # a forced split size is kept as given
+    assert ws(_desc(K), S=1, maxlen=1 << 20, split=4096) == K.KVRQ_OK
+    assert size.value == 1 * 64 * 256 * (128 + 2) * 4
 
     def dec(desc=None, q=0x1000, S=2, Hq=64, tab=0x2000, maxp=400, lens=0x3000, maxlen=5000,
             scale=0.0, split=0, out=0x4000, wsp=0x5000, wsb=1 << 30):
