@@ -846,6 +846,34 @@ void decode_split_kernel(DecodeArgs a)
             for (int i = 0; i < 8; ++i)
                 x[b][i] = 0.0f;
         }
+    }
+    // With the query rows on their way, touch the wave's first two tiles: one dword of every
+    // 128-byte line of their K and V code blocks (lanes 0..31 K, 32..63 V), so the lines
+    // travel to the L2 while the prologue runs and the tile loads after it find them there.
+    // The value is only waited for after the prologue.  (Decode only: the extend's long
+    // workgroups gain nothing from it.)
+    uint32_t touch = 0;
+    if (!EXT && t_begin < t_end) {
+        using CW = CodeWidths<CB>;
+        const int P = 1 << a.page_log2;
+        int pg[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            pg[j] = pid.page(min(t_begin + 16 * j, t_end - 1) >> a.page_log2);
+        const int j = (lane >> 3) & 3;   // half tile: tile j / 2, half j % 2
+        const int tok = min(t_begin + 16 * j, t_end - 1) & ~15;
+        const int page = j == 0 ? pg[0] : j == 1 ? pg[1] : j == 2 ? pg[2] : pg[3];
+        const bool is_k = lane < 32;
+        const int row = is_k ? CW::k_row : CW::v_row;
+        const int lines = 16 * row / 128;   // 128-byte lines of a 16-token block: 8 or 4
+        const uint8_t *blk = (is_k ? a.k_codes : a.v_codes) +
+                             ((uint64_t)((uint32_t)page * (uint32_t)a.num_kv_heads + (uint32_t)h) * P +
+                              (uint32_t)(tok & (P - 1))) * row;
+        touch = *reinterpret_cast<const uint32_t *>(blk + 128 * ((lane & 7) % lines));
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int g = b * 16 + wave * 4 + (lane >> 4);
         rotate_query_row<BK>(x[b], seg);
         float sum = 0.0f;
 #pragma unroll
@@ -942,6 +970,7 @@ void decode_split_kernel(DecodeArgs a)
             st[b].acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     __syncthreads();   // qop is complete
+    asm volatile("" ::"v"(touch));   // the touch loads have landed by now
 
     // ---- a7: page walk, one tile ahead of the math --------------------------------------
     ParLds &pl = lds_par[wave];
