@@ -851,9 +851,11 @@ void decode_split_kernel(DecodeArgs a)
     // 128-byte line of their K and V code blocks (lanes 0..31 K, 32..63 V), so the lines
     // travel to the L2 while the prologue runs and the tile loads after it find them there.
     // The value is only waited for after the prologue.  (Decode only: the extend's long
-    // workgroups gain nothing from it.)
+    // workgroups gain nothing from it.  Not in the workgroup of a fused step that writes the
+    // new token's rows: its reads must all follow those stores.)
     uint32_t touch = 0;
-    if (!EXT && t_begin < t_end) {
+    const bool writer = a.new_slots != nullptr && split == (L - 1) / a.split_tokens;
+    if (!EXT && !writer && t_begin < t_end) {
         using CW = CodeWidths<CB>;
         const int P = 1 << a.page_log2;
         int pg[4];
