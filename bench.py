@@ -237,7 +237,7 @@ class Setup:
         self.out = torch.empty((w.num_seqs, Hq, D), dtype=torch.float32, device=self.dev)
         n = K.kv_int4_paged_decode_workspace(self.sets[0][0], w.num_seqs, Hq, self.maxlen,
                                              self.args.split_tokens)
-        self.ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        self.ws = torch.zeros(n, dtype=torch.uint8, device=self.dev)
         self.kernels = {"kv_rotquant_write": self.write_bytes(T, Hkv),
                         "kv_int4_paged_decode": self.decode_bytes(w.seq_lens, Hkv, Hq, w.page_size)}
         self.tokens_per_step = T + int(w.seq_lens.sum())
@@ -318,7 +318,7 @@ class Setup:
         self.maxlen = int(w.seq_lens.max()) + n_steps
         self.out = torch.empty((S, Hq, D), dtype=torch.float32, device=self.dev)
         n = K.kv_int4_paged_decode_workspace(self.cache, S, Hq, self.maxlen, self.args.split_tokens)
-        self.ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        self.ws = torch.zeros(n, dtype=torch.uint8, device=self.dev)
         mid = w.seq_lens + n_steps // 2
         if self.args.variant == "fused":
             self.kernels = {"kv_int4_paged_decode_step": self.write_bytes(S, Hkv)
@@ -373,7 +373,7 @@ class Setup:
         self.lens = self.dev_i32([L])
         self.out = torch.empty((1, Hq, D), dtype=torch.float32, device=self.dev)
         n = K.kv_int4_paged_decode_workspace(self.cache, 1, Hq, L, self.args.split_tokens)
-        self.ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        self.ws = torch.zeros(n, dtype=torch.uint8, device=self.dev)
         self.kernels = {"kv_rotquant_write": self.write_bytes(C, Hkv),
                         "kv_int4_paged_decode": self.decode_bytes([L], Hkv, Hq, P)}
         self.launch_count = {"kv_rotquant_write": L // C, "kv_int4_paged_decode": 1}
@@ -418,7 +418,7 @@ class Setup:
         self.maxlen = int(w.seq_lens.max())
         self.out = torch.empty((T, Hq, D), dtype=torch.float32, device=self.dev)
         n = K.kv_int4_paged_extend_workspace(self.cache, S, Hq, T, C, self.maxlen, self.args.split_tokens)
-        self.ws = torch.empty(n, dtype=torch.uint8, device=self.dev)
+        self.ws = torch.zeros(n, dtype=torch.uint8, device=self.dev)
         # attended (row, key) pairs: row i of a chunk at position prefix + i sees prefix + i + 1
         pairs = int(sum(C * int(L) + C * (C + 1) // 2 for L in prefix))
         self.kernels = {"kv_rotquant_write": self.write_bytes(T, Hkv),

@@ -214,12 +214,21 @@ KVRQ_API kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, in
  *   out             device fp32 [num_seqs][num_q_heads][head_dim]
  *   workspace       device scratch of workspace_bytes >= the size reported by
  *                   kv_int4_paged_decode_workspace (16-byte aligned; unused,
- *                   and may be NULL, when that size is 0)
+ *                   and may be NULL, when that size is 0).  Its first 64 KiB
+ *                   are split counters that must be zero before the first
+ *                   call that uses the workspace (allocate it zero-filled, or
+ *                   clear it once); every decode, decode-step and extend call
+ *                   leaves them zero, so a workspace reused call after call
+ *                   on one stream needs no further clearing.  Calls that may
+ *                   overlap in time need workspaces of their own.
  * Computes, per sequence s and query head g (KV head h):
  *   q' = H_bK q,  score_t = sm_scale * q'.(code_t * scale_t + zero_t),
  *   o' = sum_t softmax(score)_t (V code_t * scale_t + zero_t),  out = H_bV o'.
- * Two launches on `stream` (split-K partials, then the combine), or one when a
- * single split covers max_seq_len. */
+ * One launch on `stream` when a single split covers max_seq_len, or when
+ * every split workgroup fits on the device at once, there are at most 16
+ * splits and num_seqs * num_kv_heads <= 16384: the last split of each
+ * (sequence, KV head) to finish merges the partials (the counters elect it).
+ * Otherwise two launches: the split-K partials, then the combine. */
 KVRQ_API kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
                                  const void *q, int32_t num_seqs, int32_t num_q_heads,
                                  const int32_t *page_table, int32_t max_pages_per_seq,
@@ -248,8 +257,9 @@ KVRQ_API kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_c
  * written but not attended), and new_slots[s] equal to the slot the page
  * table gives for position seq_lens[s] - 1 (otherwise the decode reads
  * whatever that position holds).
- * Output and workspace are those of kv_int4_paged_decode with the same
- * arguments (kv_int4_paged_decode_workspace gives the size). */
+ * Output, workspace (zero-filled before its first use) and launches are
+ * those of kv_int4_paged_decode with the same arguments
+ * (kv_int4_paged_decode_workspace gives the size). */
 KVRQ_API kvrq_status kv_int4_paged_decode_step(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
                                                const void *k_new, const void *v_new,
                                                int64_t k_token_stride, int64_t v_token_stride,
@@ -288,7 +298,9 @@ KVRQ_API kvrq_status kv_int4_paged_extend_workspace(const kvrq_cache_desc *d, in
  *   out             device fp32 [total_q][num_q_heads][head_dim]
  * Row i of sequence s sits at position p = seq_lens[s] - n_s + i and its
  * output is the decode of the sequence's first p + 1 tokens with that row's
- * query (tokens after p are masked).  Two launches on `stream`. */
+ * query (tokens after p are masked).  Two launches on `stream` (one when the
+ * key range is not split).  The workspace is laid out as the decode's: its
+ * first 64 KiB are left as they are, so one workspace can serve both. */
 KVRQ_API kvrq_status kv_int4_paged_extend(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
                                           const void *q, int32_t total_q, int32_t num_seqs,
                                           int32_t num_q_heads, const int32_t *qo_start,

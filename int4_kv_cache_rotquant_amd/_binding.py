@@ -186,7 +186,11 @@ def kv_int4_paged_decode_workspace(cache: PagedInt4Cache, num_seqs: int, num_q_h
 def kv_int4_paged_decode(cache: PagedInt4Cache, q, page_table, seq_lens, max_seq_len: int,
                          out=None, sm_scale: float = 0.0, split_tokens: int = 0, workspace=None,
                          stream=None):
-    """Paged INT4 decode of bf16 ``q`` [S][Hq][128]; returns fp32 ``out`` [S][Hq][128]."""
+    """Paged INT4 decode of bf16 ``q`` [S][Hq][128]; returns fp32 ``out`` [S][Hq][128].
+
+    A ``workspace`` passed in must have been zero-filled before its first use (its leading
+    split counters); the calls leave it so.  Without one, a zeroed workspace is allocated.
+    """
     import torch
     S, Hq, D = q.shape
     if q.dtype != torch.bfloat16 or not q.is_contiguous() or D != HEAD_DIM:
@@ -199,7 +203,7 @@ def kv_int4_paged_decode(cache: PagedInt4Cache, q, page_table, seq_lens, max_seq
         out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
     if workspace is None:
         n = kv_int4_paged_decode_workspace(cache, S, Hq, max_seq_len, split_tokens)
-        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=q.device)
     _check(lib().kv_int4_paged_decode(
         ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(q), S, Hq, _ptr(page_table),
         int(page_table.shape[1]), _ptr(seq_lens), int(max_seq_len), float(sm_scale), int(split_tokens),
@@ -230,7 +234,7 @@ def kv_int4_paged_decode_step(cache: PagedInt4Cache, k_new, v_new, new_slots, q,
         out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
     if workspace is None:
         n = kv_int4_paged_decode_workspace(cache, S, Hq, max_seq_len, split_tokens)
-        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=q.device)
     _check(lib().kv_int4_paged_decode_step(
         ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(k_new), _ptr(v_new),
         k_new.stride(0), v_new.stride(0), _ptr(new_slots), _ptr(q), S, Hq, _ptr(page_table),
@@ -271,7 +275,7 @@ def kv_int4_paged_extend(cache: PagedInt4Cache, q, qo_start, page_table, seq_len
     if workspace is None:
         n = kv_int4_paged_extend_workspace(cache, S, Hq, total_q, max_q_len, max_seq_len,
                                            split_tokens)
-        workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(max(n, 16), dtype=torch.uint8, device=q.device)
     _check(lib().kv_int4_paged_extend(
         ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(q), total_q, S, Hq,
         _ptr(qo_start), _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens),

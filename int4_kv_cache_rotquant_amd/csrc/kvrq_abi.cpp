@@ -148,13 +148,15 @@ kvrq::DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max
     return p;
 }
 
-// Split partials; none when a single split writes the output itself.
+// The split counters, then the split partials; nothing when a single split writes the
+// output itself.  Decode and extend lay a workspace out alike, so one workspace serves both
+// (the extend leaves the counters alone).
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const kvrq::DecodePlan &p)
 {
     if (p.max_splits == 1)
         return 0;
     const size_t rows = size_t(num_seqs) * num_q_heads * p.max_splits;
-    return rows * (kvrq::kHeadDim + 2) * sizeof(float);
+    return kvrq::kCounterBytes + rows * (kvrq::kHeadDim + 2) * sizeof(float);
 }
 
 kvrq_status check_decode_shape(const kvrq_cache_desc *d, int32_t num_seqs, int32_t num_q_heads,
@@ -525,8 +527,14 @@ kvrq_status decode_impl(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, c
     a.seq_lens = seq_lens;
     a.out = out;
     const size_t rows = size_t(num_seqs) * num_q_heads * plan.max_splits;
-    a.part_o = static_cast<float *>(workspace);
-    a.part_ml = a.part_o + rows * kvrq::kHeadDim;
+    if (plan.max_splits > 1) {
+        a.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + kvrq::kCounterBytes);
+        a.part_ml = a.part_o + rows * kvrq::kHeadDim;
+        // counters for every (sequence, KV head): the launch may then merge the partials in
+        // the split kernel (where that pays) instead of a combine launch
+        if (int64_t(num_seqs) * d->num_kv_heads <= kvrq::kSplitCounters)
+            a.counters = static_cast<int32_t *>(workspace);
+    }
     a.num_seqs = num_seqs;
     a.num_pages = d->num_pages;
     a.max_seq_len = max_seq_len;
@@ -659,8 +667,10 @@ KVRQ_API kvrq_status kv_int4_paged_extend(const kvrq_cache_desc *d, const kvrq_c
     a.seq_lens = seq_lens;
     a.out = out;
     const size_t rows = size_t(total_q) * num_q_heads * plan.max_splits;
-    a.part_o = static_cast<float *>(workspace);
-    a.part_ml = a.part_o + rows * kvrq::kHeadDim;
+    if (plan.max_splits > 1) {
+        a.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + kvrq::kCounterBytes);
+        a.part_ml = a.part_o + rows * kvrq::kHeadDim;
+    }
     a.num_seqs = num_seqs;
     a.num_pages = d->num_pages;
     a.max_seq_len = max_seq_len;

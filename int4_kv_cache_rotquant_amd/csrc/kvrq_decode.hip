@@ -709,6 +709,87 @@ __device__ __forceinline__ void inverse_rotate_pair_rt(float &o0, float &o1, int
     }
 }
 
+// ---- a10 by one wave for one output row of up to 64 splits, whose partials start at slot
+// base (lane j holds split j's maximum and normaliser, lane l the channels 2 l, 2 l + 1)
+constexpr int kCombineEarly = 4;
+
+// A float pair of the partials.  COH: read at device scope, past this XCD's L2, for
+// partials that other workgroups of the same launch wrote at device scope.
+template <bool COH>
+__device__ __forceinline__ float2 load_pair(const float *p)
+{
+    if constexpr (COH) {
+        const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+    } else {
+        return *reinterpret_cast<const float2 *>(p);
+    }
+}
+
+// The first kCombineEarly splits' outputs and every split's (m, l) are requested together;
+// each row holds max_splits slots, so these loads stay inside the workspace whatever the
+// row's length.
+template <bool COH>
+__device__ __forceinline__ void combine_loads(const DecodeArgs &a, int64_t base, int lane,
+                                              float2 (&v0)[kCombineEarly], float2 &ml)
+{
+    const float *po = a.part_o + base * kHeadDim + 2 * lane;
+#pragma unroll
+    for (int k = 0; k < kCombineEarly; ++k)
+        v0[k] = k < a.max_splits ? load_pair<COH>(po + (int64_t)k * kHeadDim) : make_float2(0.0f, 0.0f);
+    ml = make_float2(-INFINITY, 0.0f);
+    if (lane < a.max_splits)
+        ml = load_pair<COH>(a.part_ml + 2 * (base + lane));
+}
+
+// The log-sum-exp merge of the row's n (1..64) splits: the weights come from two wave
+// reductions by row permutes, the outputs are summed with each split's weight broadcast
+// from its lane.  o0, o1: the normalised output, still in the rotated basis.
+template <bool COH>
+__device__ __forceinline__ void combine_merge(const DecodeArgs &a, int64_t base, int n, int lane,
+                                              const float2 (&v0)[kCombineEarly], float2 ml,
+                                              float &o0, float &o1)
+{
+    const float *po = a.part_o + base * kHeadDim + 2 * lane;
+    const float m = lane < n ? ml.x : -INFINITY, l = lane < n ? ml.y : 0.0f;
+    const float M = col_max(row16_max(m));
+    const float wj = lane < n ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+    const float lsum = col_sum(row16_sum(wj * l));
+    o0 = 0.0f;
+    o1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kCombineEarly; ++k) {
+        if (k < n) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), k));
+            o0 = fmaf(w, v0[k].x, o0);
+            o1 = fmaf(w, v0[k].y, o1);
+        }
+    }
+    int i = kCombineEarly;
+    for (; i + 4 <= n; i += 4) {
+        float2 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            v[k] = load_pair<COH>(po + (int64_t)(i + k) * kHeadDim);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), i + k));
+            o0 = fmaf(w, v[k].x, o0);
+            o1 = fmaf(w, v[k].y, o1);
+        }
+    }
+    for (; i < n; ++i) {
+        const float2 v = load_pair<COH>(po + (int64_t)i * kHeadDim);
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), i));
+        o0 = fmaf(w, v.x, o0);
+        o1 = fmaf(w, v.y, o1);
+    }
+    const float inv_l = 1.0f / lsum;
+    o0 *= inv_l;
+    o1 *= inv_l;
+}
+
 // Fused decode step: lanes 0-3 encode the new K row of (sequence s, KV head h) and lanes
 // 4-7 its V row, exactly as the write kernel does, into the slot given for it.
 template <int BK>
@@ -776,8 +857,9 @@ void decode_split_kernel(DecodeArgs a)
     }
     const int wg_begin = split * a.split_tokens;
     if (wg_begin >= L) {
-        // a single split writes the output itself: an empty sequence gets zero rows
-        if (a.max_splits == 1 && !EXT) {
+        // without a combine launch the splits write the output themselves: split 0 of an
+        // empty sequence gives it zero rows
+        if (!EXT && split == 0 && (a.max_splits == 1 || a.counters != nullptr)) {
             float4 *o = reinterpret_cast<float4 *>(
                 a.out + ((int64_t)s * a.num_q_heads + (int64_t)h * G) * kHeadDim);
             for (int i = threadIdx.x; i < G * kHeadDim / 4; i += blockDim.x)
@@ -1015,7 +1097,10 @@ void decode_split_kernel(DecodeArgs a)
     }
 
     // ---- the waves' (and, for F = 2, the two halves') partial states of this split, one
-    // block of 16 columns at a time through the same LDS
+    // block of 16 columns at a time through the same LDS.  The output rows are written here
+    // when this is the row's only split and no combine launch follows (one split in the
+    // launch, or a short row under the in-kernel combine).
+    const bool direct = a.max_splits == 1 || (!EXT && a.counters != nullptr && L <= a.split_tokens);
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
         const int cb0 = blk * 16;                 // first column of the block
@@ -1065,10 +1150,10 @@ void decode_split_kernel(DecodeArgs a)
             }
         }
         __syncthreads();
-        if (a.max_splits == 1) {
-            // the only split: merge the waves, normalise, undo the V rotation and write
-            // the output rows here (no combine launch); wave w takes columns w, w + 4, ...,
-            // lane l channels 2 l and 2 l + 1
+        if (direct) {
+            // the row's only split: merge the waves, normalise, undo the V rotation and
+            // write the output rows here; wave w takes columns w, w + 4, ..., lane l
+            // channels 2 l and 2 l + 1
             for (int gc = wave; gc < nc; gc += kDecodeWaves) {
                 float M = lds_m[0][gc];
 #pragma unroll
@@ -1111,10 +1196,58 @@ void decode_split_kernel(DecodeArgs a)
             const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
                                      : (int64_t)s * a.num_q_heads + h * G + g;
             const int64_t row = qrow * a.max_splits + split;
-            a.part_o[row * kHeadDim + d] = acc;
-            if (d == 0) {
-                a.part_ml[2 * row] = M;
-                a.part_ml[2 * row + 1] = lsum;
+            if (!EXT && a.counters != nullptr) {
+                // device-scope stores: they pass this XCD's L2, so the split that merges
+                // in this launch reads them from any XCD
+                __hip_atomic_store(a.part_o + row * kHeadDim + d, acc, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                if (d == 0) {
+                    __hip_atomic_store(a.part_ml + 2 * row, M, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(a.part_ml + 2 * row + 1, lsum, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+            } else {
+                a.part_o[row * kHeadDim + d] = acc;
+                if (d == 0) {
+                    a.part_ml[2 * row] = M;
+                    a.part_ml[2 * row + 1] = lsum;
+                }
+            }
+        }
+    }
+    if constexpr (!EXT) {
+        if (a.counters != nullptr && !direct) {
+            // a10 in this launch: each split's partials (device-scope stores) have completed
+            // before it counts itself in; the split that counts last reads them all at
+            // device scope, merges them and clears the counter for the next call.  (No
+            // device-scope fence: on this chip it writes back and invalidates the whole L2
+            // of the XCD, the other workgroups' tiles included.)
+            __shared__ int lds_last;
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            int32_t *cnt = a.counters + (int64_t)s * a.num_kv_heads + h;
+            const int n = (L + a.split_tokens - 1) / a.split_tokens;
+            if (tid == 0)
+                lds_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                           n - 1;
+            __syncthreads();
+            if (!lds_last)
+                return;
+            if (tid == 0)
+                __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // the lane index afresh from the exec mask: keeping the kernel's own live up to
+            // here costs a spill
+            const int cl = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+            for (int g = wave; g < G; g += kDecodeWaves) {
+                const int64_t qrow = (int64_t)s * a.num_q_heads + h * G + g;
+                float2 v0[kCombineEarly], ml;
+                combine_loads<true>(a, qrow * a.max_splits, cl, v0, ml);
+                float o0, o1;
+                combine_merge<true>(a, qrow * a.max_splits, n, cl, v0, ml, o0, o1);
+                inverse_rotate_pair_rt(o0, o1, cl, a.v_block);
+                *reinterpret_cast<float2 *>(a.out + qrow * kHeadDim + 2 * cl) =
+                    make_float2(o0, o1);
             }
         }
     }
@@ -1219,9 +1352,7 @@ __global__ __launch_bounds__(1024) void decode_combine_kernel(DecodeArgs a)
 }
 
 // ---- a10 for up to 64 splits: one wave per (sequence, query head) ---------------------
-// Lane j holds split j's maximum and normaliser, so the log-sum-exp weights come from
-// two wave reductions; the partial outputs are then summed with each split's weight
-// broadcast from its lane.  No barrier, four query heads per workgroup.
+// Four query heads per workgroup, no barrier.
 template <int BV>
 __global__ __launch_bounds__(256) void decode_combine_wave_kernel(DecodeArgs a)
 {
@@ -1230,20 +1361,11 @@ __global__ __launch_bounds__(256) void decode_combine_wave_kernel(DecodeArgs a)
     const int g = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (g >= a.num_q_heads)
         return;
-    // the first four splits' outputs and every split's (m, l) are requested before the row's
-    // length is known, so one memory round trip serves rows of up to four splits; every row
-    // holds max_splits slots, so these loads stay inside the workspace whatever the length
-    const int64_t row0 = ((int64_t)s * a.num_q_heads + g) * a.max_splits;
-    const float *po = a.part_o + row0 * kHeadDim + 2 * lane;
-    constexpr int kEarly = 4;
-    float2 v0[kEarly];
-#pragma unroll
-    for (int k = 0; k < kEarly; ++k)
-        if (k < a.max_splits)
-            v0[k] = *reinterpret_cast<const float2 *>(po + (int64_t)k * kHeadDim);
-    float2 ml = make_float2(-INFINITY, 0.0f);
-    if (lane < a.max_splits)
-        ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * (row0 + lane));
+    // the partials are requested before the row's length is known, so one memory round
+    // trip serves rows of up to four splits
+    const int64_t base = ((int64_t)s * a.num_q_heads + g) * a.max_splits;
+    float2 v0[kCombineEarly], ml;
+    combine_loads<false>(a, base, lane, v0, ml);
     const int L = row_length(a, s);
     float *out = a.out + ((int64_t)s * a.num_q_heads + g) * kHeadDim;
     if (L <= 0) {
@@ -1251,42 +1373,8 @@ __global__ __launch_bounds__(256) void decode_combine_wave_kernel(DecodeArgs a)
         return;
     }
     const int n = (L + a.split_tokens - 1) / a.split_tokens;   // 1..64
-    const float m = lane < n ? ml.x : -INFINITY, l = lane < n ? ml.y : 0.0f;
-    // wave-wide max and sum by row permutes (no LDS round trips)
-    const float M = col_max(row16_max(m));
-    const float wj = lane < n ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-    const float lsum = col_sum(row16_sum(wj * l));
-    float o0 = 0.0f, o1 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kEarly; ++k) {
-        if (k < n) {
-            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), k));
-            o0 = fmaf(w, v0[k].x, o0);
-            o1 = fmaf(w, v0[k].y, o1);
-        }
-    }
-    int i = kEarly;
-    for (; i + 4 <= n; i += 4) {
-        float2 v[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            v[k] = *reinterpret_cast<const float2 *>(po + (int64_t)(i + k) * kHeadDim);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), i + k));
-            o0 = fmaf(w, v[k].x, o0);
-            o1 = fmaf(w, v[k].y, o1);
-        }
-    }
-    for (; i < n; ++i) {
-        const float2 v = *reinterpret_cast<const float2 *>(po + (int64_t)i * kHeadDim);
-        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), i));
-        o0 = fmaf(w, v.x, o0);
-        o1 = fmaf(w, v.y, o1);
-    }
-    const float inv_l = 1.0f / lsum;
-    o0 *= inv_l;
-    o1 *= inv_l;
+    float o0, o1;
+    combine_merge<false>(a, base, n, lane, v0, ml, o0, o1);
     inverse_rotate_pair<BV>(o0, o1, lane);
     *reinterpret_cast<float2 *>(out + 2 * lane) = make_float2(o0, o1);
 }
@@ -1309,6 +1397,14 @@ void launch_f1_widths(const DecodeArgs &a, const dim3 &grid, hipStream_t s)
     }
 }
 
+// The decode's split grid fits on the device at once (four workgroups per CU; two for the
+// 16-column kernel).
+bool one_round(const DecodeArgs &a)
+{
+    const int64_t wgs = (int64_t)a.max_splits * a.num_kv_heads * a.num_seqs;
+    return wgs <= (int64_t)device_cus() * (a.group > 8 ? 2 : 4);
+}
+
 template <int BK>
 hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
 {
@@ -1325,9 +1421,7 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
     // fastest, so that the long sequences' splits do not all come last (Qwen3-32B-like:
     // 639 us, against 728 with sequences fastest).
     DecodeArgs b = a;
-    const int64_t wgs = (int64_t)a.max_splits * a.num_kv_heads * a.num_seqs;
-    const int64_t resident = (int64_t)device_cus() * (a.group > 8 ? 2 : 4);
-    b.seq_major = wgs <= resident && a.max_splits <= 65535 ? 1 : 0;
+    b.seq_major = one_round(a) && a.max_splits <= 65535 ? 1 : 0;
     const dim3 grid = b.seq_major
         ? dim3((unsigned)a.num_seqs, (unsigned)a.num_kv_heads, (unsigned)a.max_splits)
         : dim3((unsigned)a.max_splits, (unsigned)a.num_kv_heads, (unsigned)a.num_seqs);
@@ -1361,11 +1455,21 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t s)
 
 }  // namespace
 
-int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream)
+int launch_decode(int k_block, int v_block, const DecodeArgs &args, void *stream)
 {
-    if (a.num_seqs == 0 || a.num_rows == 0)
+    if (args.num_seqs == 0 || args.num_rows == 0)
         return 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // The in-kernel combine pays where launch latency dominates: a grid resident in one
+    // round, of at most kInKernelCombineSplits splits per row (the Qwen3-4B-like decode
+    // 19.4 -> 18.4 us, the small-batch fused step 21.3 -> 17.6 us).  Otherwise the combine
+    // launch: in a grid of several rounds each workgroup would hold its slot until its
+    // stores and its count complete (Qwen3-32B-like: 663 us against 640), and one workgroup
+    // merging 64 splits per head is slower than the combine's one wave per head (1M
+    // tokens: 227 us against 222).
+    DecodeArgs a = args;
+    if (a.counters != nullptr && !(a.max_splits <= kInKernelCombineSplits && one_round(a)))
+        a.counters = nullptr;
     hipError_t e;
     switch (k_block) {
     case 0: e = launch_split<0>(a, s); break;
@@ -1375,7 +1479,8 @@ int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream)
     case 128: e = launch_split<128>(a, s); break;
     default: return hipErrorInvalidValue;
     }
-    if (e != hipSuccess || a.max_splits == 1)   // one split writes the output itself
+    // one split, or the in-kernel combine: the splits write the output themselves
+    if (e != hipSuccess || a.max_splits == 1 || a.counters != nullptr)
         return e;
     switch (v_block) {
     case 0: return launch_combine<0>(a, s);

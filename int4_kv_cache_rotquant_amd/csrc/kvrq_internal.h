@@ -19,6 +19,11 @@ constexpr int kWriteWgsPerCu = kWriteWavesPerSimd;
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave
 constexpr int kDecodeWaves = 4;     // waves per decode workgroup, each on its own token range
 constexpr int kExtendBlocks = 2;    // extend: 16-column blocks per wave (query rows x heads)
+// split workspaces start with this many int32 split counters (used by the decode when
+// sequences x KV heads fits them and a row has at most 64 splits); the partials follow
+constexpr int kSplitCounters = 16384;
+constexpr size_t kCounterBytes = size_t(kSplitCounters) * 4;
+constexpr int kInKernelCombineSplits = 16;   // most splits per row merged inside the split launch
 
 struct WriteArgs {
     const uint16_t *k;          // bf16 bits
@@ -66,8 +71,12 @@ struct DecodeArgs {
     const int32_t *page_table;  // [S][max_pages]
     const int32_t *seq_lens;    // [S]
     float *out;                 // [S][Hq][128]
-    float *part_o;              // [S][Hq][max_splits][128]
-    float *part_ml;             // [S][Hq][max_splits][2]
+    // decode with 2..kInKernelCombineSplits splits in a grid resident at once: one counter
+    // per (sequence, KV head), zero on entry and on exit; the split workgroup that counts
+    // last merges the partials (no combine launch)
+    int32_t *counters = nullptr;
+    float *part_o = nullptr;    // [S][Hq][max_splits][128]
+    float *part_ml = nullptr;   // [S][Hq][max_splits][2]
     int32_t num_seqs;
     int32_t num_pages;          // page ids outside [0, num_pages) read page 0 instead
     int32_t max_seq_len;        // longer seq_lens entries are clamped to it

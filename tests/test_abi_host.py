@@ -117,12 +117,14 @@ def test_decode_validation(K):
     ws(_desc(K), split=128)
     assert size.value > small
     # the automatic split keeps at most 64 splits (one wave combines them): a 1M-token
-    # sequence takes 16,384-token splits, partials of 128 + 2 floats per (row, head, split)
+    # sequence takes 16,384-token splits; 64 KiB of split counters, then partials of
+    # 128 + 2 floats per (row, head, split)
+    counters = 16384 * 4
     assert ws(_desc(K), S=1, maxlen=1 << 20) == K.KVRQ_OK
-    assert size.value == 1 * 64 * 64 * (128 + 2) * 4
+    assert size.value == counters + 1 * 64 * 64 * (128 + 2) * 4
     # a forced split size is kept as given
     assert ws(_desc(K), S=1, maxlen=1 << 20, split=4096) == K.KVRQ_OK
-    assert size.value == 1 * 64 * 256 * (128 + 2) * 4
+    assert size.value == counters + 1 * 64 * 256 * (128 + 2) * 4
 
     def dec(desc=None, q=0x1000, S=2, Hq=64, tab=0x2000, maxp=400, lens=0x3000, maxlen=5000,
             scale=0.0, split=0, out=0x4000, wsp=0x5000, wsb=1 << 30):
@@ -170,8 +172,9 @@ def test_extend_validation(K):
                                                 split, ctypes.byref(size))
 
     assert ws() == K.KVRQ_OK and size.value > 0
-    base = size.value
-    assert ws(total_q=80) == K.KVRQ_OK and size.value == 2 * base   # per query row and head
+    # the decode's layout: 64 KiB of split counters (left alone), then the partials
+    base = size.value - 16384 * 4
+    assert ws(total_q=80) == K.KVRQ_OK and size.value == 16384 * 4 + 2 * base   # per query row and head
     assert ws(Hq=60) == K.KVRQ_EINVAL
     assert ws(total_q=-1) == K.KVRQ_EINVAL
     assert ws(max_q=0) == K.KVRQ_EINVAL                 # rows but no row per sequence

@@ -6,8 +6,10 @@ Covers the tiny case (G=1), the Qwen3-4B-like layer (G=4, 16 ragged sequences, p
 scattered), the high-concurrency shape (G=8, 256 log-normal sequences, sampled
 sequences checked), the 1M-token long context (G=8, K and V rotated, one KV head
 checked), split-count sweeps, page-table permutation invariance, GQA group sizes
-1..16, page sizes 16..128, every block pair, lengths 0, 1, 15..33 and tail tiles, and
-caches of degenerate rows (zero and tiny scales, spiked keys) in decode and extend.
+1..16, page sizes 16..128, every block pair, lengths 0, 1, 15..33 and tail tiles,
+caches of degenerate rows (zero and tiny scales, spiked keys) in decode and extend, the
+in-kernel combine over calls that share one workspace, and the combine launch it falls
+back to.
 """
 import math
 
@@ -259,6 +261,49 @@ def test_single_split_writes_the_output(K, G, vb):
     got = out.cpu().numpy()
     assert np.all(got[0] == 0.0)
     decode_compare(got, _ref(orc, q, tab, L, Hkv, 16, 128, vb), f"single split G{G} vb{vb}")
+
+
+@pytest.mark.parametrize("G", [4, 16])
+def test_in_kernel_combine_reuses_its_workspace(K, G):
+    """Up to 64 splits are merged inside the split launch: the last split of each (sequence,
+    KV head) to finish, elected by a counter at the head of the workspace, combines the
+    partials; a row of one split writes itself and an empty row gets zeros.  Three calls
+    share one zero-filled workspace, each with fresh queries: every output matches the
+    oracle (the output starts as NaN, so a row nobody writes fails) and the counters are
+    zero again after every call."""
+    import torch
+    lens = [0, 1, 128, 129, 300, 700, 1000, 1025]   # 0, 1, 1, 2, 3, 6, 8 and 9 splits
+    Hkv = 2
+    cache, orc, q, tab, L = _build(K, lens, Hkv, Hkv * G, 16, 64, 128, seed=950 + G)
+    maxlen = int(L.max())
+    n = K.kv_int4_paged_decode_workspace(cache, len(lens), Hkv * G, maxlen, 128)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(951 + G)
+    for call in range(3):
+        qc = q if call == 0 else W.f32_to_bf16_bits(rng.standard_normal(q.shape).astype(np.float32))
+        out = torch.full((len(lens), Hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
+        K.kv_int4_paged_decode(cache, bf16_dev(qc), to_dev(tab), to_dev(L), maxlen, out=out,
+                               split_tokens=128, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:16384 * 4].count_nonzero()) == 0, f"counters left set after call {call}"
+        got = out.cpu().numpy()
+        assert np.all(got[0] == 0.0)
+        decode_compare(got, _ref(orc, qc, tab, L, Hkv, 16, 64, 128), f"in-kernel combine G{G} call {call}")
+
+
+def test_combine_launch_beyond_the_counters(K):
+    """More (sequence, KV head) pairs than the workspace holds counters (2,050 sequences x
+    8 KV heads = 16,400 > 16,384): the separate combine launch merges the splits.  Lengths
+    0..200 in splits of 128; 64 sampled sequences checked against the oracle."""
+    rng = np.random.default_rng(960)
+    S, Hkv = 2050, 8
+    lens = rng.integers(0, 201, S)
+    lens[:4] = [0, 128, 129, 200]
+    cache, orc, q, tab, L = _build(K, lens, Hkv, Hkv, 16, 128, 128, seed=961, k_out=False)
+    out = _run(K, cache, q, tab, L, split=128)
+    idx = np.concatenate([np.arange(4), np.sort(rng.choice(np.arange(4, S), 60, replace=False))])
+    ref = _ref(orc, q[idx].copy(), tab[idx].copy(), L[idx].copy(), Hkv, 16, 128, 128)
+    decode_compare(out[idx], ref, "combine launch beyond the counters")
 
 
 def _degenerate_rows(rng, T, Hkv):
