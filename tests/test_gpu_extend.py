@@ -120,3 +120,33 @@ def test_every_prefix_as_a_decode(K):
     arrays = (orc.k_codes, orc.v_codes, orc.k_params, orc.v_params)
     decode_compare(dec, oracle.decode(q[rows], arrays, ptab, plens, 2, 16, 0, 0), "prefix decodes")
     assert np.max(np.abs(dec - ext[rows])) < DECODE_ATOL
+
+
+def test_one_workspace_for_decode_and_extend(K):
+    """One zero-filled workspace serves decode and extend calls in turn: the extend writes
+    its partials after the decode's split counters and leaves those alone, so decode,
+    extend, decode all match the oracle and the counters are zero after each call (the
+    decode here merges its 12 splits inside the split launch)."""
+    import torch
+    lens, news = [1500, 700], [96, 31]
+    cache, orc, q, qo, tab, L = _build(K, lens, news, 1, 8, 16, 128, 0, seed=80)
+    arrays = (orc.k_codes, orc.v_codes, orc.k_params, orc.v_params)
+    maxlen, total_q, max_q = int(L.max()), int(qo[-1]), int(max(news))
+    nd = K.kv_int4_paged_decode_workspace(cache, len(lens), 8, maxlen, 128)
+    ne = K.kv_int4_paged_extend_workspace(cache, len(lens), 8, total_q, max_q, maxlen, 128)
+    ws = torch.zeros(max(nd, ne), dtype=torch.uint8, device="cuda")
+    qd = q[qo[1:] - 1].copy()
+    dref = oracle.decode(qd, arrays, tab, L, 1, 16, 128, 0)
+    eref = _ref(orc, q, qo, tab, L, 1, 16, 128, 0)
+    for step in ("decode", "extend", "decode"):
+        if step == "decode":
+            out = K.kv_int4_paged_decode(cache, bf16_dev(qd), to_dev(tab), to_dev(L), maxlen,
+                                         split_tokens=128, workspace=ws)
+            ref = dref
+        else:
+            out = K.kv_int4_paged_extend(cache, bf16_dev(q), to_dev(qo), to_dev(tab), to_dev(L),
+                                         maxlen, max_q, split_tokens=128, workspace=ws)
+            ref = eref
+        torch.cuda.synchronize()
+        assert int(ws[:16384 * 4].count_nonzero()) == 0, f"counters left set after the {step}"
+        decode_compare(out.cpu().numpy(), ref, f"shared workspace: {step}")
