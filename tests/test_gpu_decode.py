@@ -291,12 +291,15 @@ def test_in_kernel_combine_reuses_its_workspace(K, G):
         decode_compare(got, _ref(orc, qc, tab, L, Hkv, 16, 64, 128), f"in-kernel combine G{G} call {call}")
 
 
-def test_combine_launch_beyond_the_counters(K):
-    """More (sequence, KV head) pairs than the workspace holds counters (2,050 sequences x
-    8 KV heads = 16,400 > 16,384): the separate combine launch merges the splits.  Lengths
-    0..200 in splits of 128; 64 sampled sequences checked against the oracle."""
-    rng = np.random.default_rng(960)
-    S, Hkv = 2050, 8
+@pytest.mark.parametrize("S", [600, 2050])
+def test_combine_launch_beyond_the_counters(K, S):
+    """The separate combine launch merges the splits of a grid too large for one round
+    (600 sequences x 8 KV heads x 2 splits: counters exist, the launcher leaves them
+    unused) and of more (sequence, KV head) pairs than the workspace holds counters
+    (2,050 x 8 = 16,400 > 16,384).  Lengths 0..200 in splits of 128; 64 sampled sequences
+    checked against the oracle."""
+    rng = np.random.default_rng(960 + S)
+    Hkv = 8
     lens = rng.integers(0, 201, S)
     lens[:4] = [0, 128, 129, 200]
     cache, orc, q, tab, L = _build(K, lens, Hkv, Hkv, 16, 128, 128, seed=961, k_out=False)
