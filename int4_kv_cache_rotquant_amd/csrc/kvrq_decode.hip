@@ -34,9 +34,12 @@
 // byte-per-code layout as they are consumed.  In the fused decode step, the workgroup
 // whose split holds a sequence's last position first encodes and stores the new
 // token's K/V rows (the write kernel's encoding), then reads them back with the rest.
-// Launch 2 (more than one split) -- log-sum-exp combine of the splits, then the inverse
-// V rotation: decode_combine_wave_kernel (one wave per (row, query head)) for up to 64
-// splits, decode_combine_kernel (a 16-wave workgroup per (row, query head)) beyond.
+// The log-sum-exp combine of the splits, then the inverse V rotation: in the split launch
+// when its grid is resident at once and a row has at most 16 splits (the last split of
+// each (sequence, KV head) to finish, elected by a counter in the workspace, merges
+// them); otherwise launch 2: decode_combine_wave_kernel (one wave per (row, query head))
+// for up to 64 splits, decode_combine_kernel (a 16-wave workgroup per (row, query head))
+// beyond.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
