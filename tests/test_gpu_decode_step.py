@@ -58,7 +58,7 @@ def _step_slots(paging, lens, i):
 
 
 def _check_step(K, caches, orc, paging, lens, new, Hkv, P, kb, vb, split, label, i=0,
-                slot_override=None):
+                slot_override=None, workspaces=(None, None)):
     import torch
     kn, vn, q = new
     L = np.array([int(x) + i if x > 0 else 0 for x in lens], np.int32)
@@ -67,9 +67,11 @@ def _check_step(K, caches, orc, paging, lens, new, Hkv, P, kb, vb, split, label,
     maxlen = int(max(L.max(), 1))
     fused, ref = caches
     out_f = K.kv_int4_paged_decode_step(fused, bf16_dev(kn), bf16_dev(vn), to_dev(slots), bf16_dev(q),
-                                        to_dev(tab), to_dev(L), maxlen, split_tokens=split)
+                                        to_dev(tab), to_dev(L), maxlen, split_tokens=split,
+                                        workspace=workspaces[0])
     K.kv_rotquant_write(ref, bf16_dev(kn), bf16_dev(vn), to_dev(slots))
-    out_r = K.kv_int4_paged_decode(ref, bf16_dev(q), to_dev(tab), to_dev(L), maxlen, split_tokens=split)
+    out_r = K.kv_int4_paged_decode(ref, bf16_dev(q), to_dev(tab), to_dev(L), maxlen, split_tokens=split,
+                                   workspace=workspaces[1])
     torch.cuda.synchronize()
     for a, b, name in zip(gpu_cache_arrays(fused), gpu_cache_arrays(ref), ("kc", "vc", "kp", "vp")):
         assert np.array_equal(a, b), (label, name, int((a != b).sum()))
@@ -111,3 +113,23 @@ def test_negative_slot_writes_nothing(K):
     page, off = divmod(int(_step_slots(paging, lens, 0)[1]), P)
     assert np.array_equal(before[0][page, :, off], after[0][page, :, off])
     assert np.array_equal(before[2][page, :, off], after[2][page, :, off])
+
+
+def test_steps_in_a_row_on_one_workspace(K):
+    """The serving loop: four fused steps in a row, each on the same zero-filled workspace
+    (and the reference decode on another), rows of 0 to 9 splits of 128 tokens merged
+    inside the split launch; every step matches the separate write and decode bit for bit
+    and the oracle within 2e-3, and leaves the split counters at zero."""
+    import torch
+    Hkv, Hq, P, kb, vb = 2, 8, 16, 64, 128
+    lens = [0, 1, 127, 128, 300, 1021]
+    steps = 4
+    caches, orc, paging, news = _setup(K, lens, Hkv, Hq, P, kb, vb, seed=11, steps=steps)
+    n = K.kv_int4_paged_decode_workspace(caches[0], len(lens), Hq, max(lens) + steps, 128)
+    ws = (torch.zeros(n, dtype=torch.uint8, device="cuda"),
+          torch.zeros(n, dtype=torch.uint8, device="cuda"))
+    for i in range(steps):
+        _check_step(K, caches, orc, paging, lens, news[i], Hkv, P, kb, vb, 128, f"shared step {i}",
+                    i=i, workspaces=ws)
+        for w in ws:
+            assert int(w[:16384 * 4].count_nonzero()) == 0, f"counters left set after step {i}"
