@@ -65,6 +65,9 @@ def lib() -> ctypes.CDLL:
         L.kvrq_oracle_fwht_f32.restype = None
         L.kvrq_oracle_rotate_f64.argtypes = [P, P, i32, i32]
         L.kvrq_oracle_rotate_f64.restype = None
+        L.kvrq_oracle_codes_from_params.argtypes = [P, i32, i32, ctypes.c_uint16, ctypes.c_uint16,
+                                                    P, P]
+        L.kvrq_oracle_codes_from_params.restype = i32
         L.kvrq_oracle_quant_row.argtypes = [P, i32, i32, i32, P, P, P, P]
         L.kvrq_oracle_quant_row.restype = i32
         L.kvrq_oracle_write.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, P, P, i64,
@@ -78,6 +81,17 @@ def lib() -> ctypes.CDLL:
         L.kvrq_oracle_extend.restype = i32
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> int:
+    """Threads the oracle's OpenMP loops use from this thread on (its runtime's
+    omp_set_num_threads); returns the count in force."""
+    lib()
+    gomp = ctypes.CDLL("libgomp.so.1")
+    gomp.omp_set_num_threads.argtypes = [ctypes.c_int]
+    gomp.omp_get_max_threads.restype = ctypes.c_int
+    gomp.omp_set_num_threads(max(1, int(n)))
+    return int(gomp.omp_get_max_threads())
 
 
 def _p(a: Optional[np.ndarray]):
@@ -137,6 +151,20 @@ def quant_row(x_bf16: np.ndarray, b: int, bits: int = 4):
     if rc:
         raise ValueError("bad row shape")
     return codes, params, vpre, y
+
+
+def codes_from_params(y: np.ndarray, params, bits: int = 4):
+    """Codes of the rotated fp32 row ``y`` under given (s16, z16) bits (the write's steps 6-7
+    with those parameters) -> (codes uint8[D*bits/8], vpre f32[D])."""
+    y = np.ascontiguousarray(y, np.float32)
+    D = y.shape[0]
+    codes = np.zeros(D * bits // 8, np.uint8)
+    vpre = np.zeros(D, np.float32)
+    rc = lib().kvrq_oracle_codes_from_params(_p(y), D, bits, int(params[0]), int(params[1]),
+                                             _p(codes), _p(vpre))
+    if rc:
+        raise ValueError("bad row shape")
+    return codes, vpre
 
 
 class Cache:

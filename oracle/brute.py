@@ -52,6 +52,27 @@ def fwht_f32_vec(x: np.ndarray, b: int) -> np.ndarray:
     return (blocks * r).reshape(y.shape)
 
 
+def codes_for_params(y: np.ndarray, s16_bits, z16_bits, bits: int = 4):
+    """Rotated fp32 rows [..., D] and binary16 (scale, zero) bit patterns [...] -> (codes uint8
+    [..., D*bits/8], vpre f32): the quantiser's last steps for parameters given from outside."""
+    levels = (1 << bits) - 1
+    s16 = np.asarray(s16_bits, np.uint16).view(np.float16)
+    z16 = np.asarray(z16_bits, np.uint16).view(np.float16)
+    sf = s16.astype(np.float32)[..., None]
+    zf = z16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        inv = np.float32(1.0) / sf
+        v = (np.asarray(y, np.float32) - zf) * inv
+    zero = (s16.view(np.uint16) & 0x7FFF) == 0
+    v = np.where(zero[..., None], np.float32(0.0), v).astype(np.float32)
+    q = np.clip(np.rint(v), 0, levels).astype(np.uint8)
+    per = 8 // bits
+    codes = np.zeros(q.shape[:-1] + (q.shape[-1] // per,), np.uint8)
+    for j in range(per):
+        codes |= (q[..., j::per] << (bits * j)).astype(np.uint8)
+    return codes, v
+
+
 def quantize_rows(x_bf16: np.ndarray, b: int, bits: int = 4):
     """Rows [..., D] -> (codes uint8 [..., D*bits/8], s16 bits, z16 bits, vpre f32); 2^bits - 1
     levels, channel d at bit (d*bits) % 8 of byte d*bits/8."""
@@ -60,21 +81,10 @@ def quantize_rows(x_bf16: np.ndarray, b: int, bits: int = 4):
     mn = y.min(axis=-1) + np.float32(0.0)
     mx = y.max(axis=-1) + np.float32(0.0)
     scale32 = (mx - mn) / np.float32(levels)
-    s16 = scale32.astype(np.float16)
-    z16 = mn.astype(np.float16)
-    sf = s16.astype(np.float32)[..., None]
-    zf = z16.astype(np.float32)[..., None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        inv = np.float32(1.0) / sf
-        v = (y - zf) * inv
-    zero = (s16.view(np.uint16) & 0x7FFF) == 0
-    v = np.where(zero[..., None], np.float32(0.0), v).astype(np.float32)
-    q = np.clip(np.rint(v), 0, levels).astype(np.uint8)
-    per = 8 // bits
-    codes = np.zeros(q.shape[:-1] + (q.shape[-1] // per,), np.uint8)
-    for j in range(per):
-        codes |= (q[..., j::per] << (bits * j)).astype(np.uint8)
-    return codes, s16.view(np.uint16), z16.view(np.uint16), v
+    s16 = scale32.astype(np.float16).view(np.uint16)
+    z16 = mn.astype(np.float16).view(np.uint16)
+    codes, v = codes_for_params(y, s16, z16, bits)
+    return codes, s16, z16, v
 
 
 def unpack_codes(codes: np.ndarray, bits: int) -> np.ndarray:

@@ -191,6 +191,48 @@ ORACLE_API void kvrq_oracle_rotate_f64(const double *x, double *y, int n, int b)
 /* write                                                                   */
 /* ---------------------------------------------------------------------- */
 
+/* Steps 6 and 7 of the write for given parameters: the codes of the D rotated fp32 values
+ * y under the binary16 scale s16 and zero z16 (s16 == +-0: all codes 0), packed as below.
+ * quant_row calls it with the parameters it derives; a checker calls it with another
+ * encoder's parameters to re-derive the codes those parameters imply.
+ *   codes   D*bits/8 bytes; vpre optional, D fp32 pre-round values (0 when s16 == 0) */
+ORACLE_API int kvrq_oracle_codes_from_params(const float *y, int D, int bits, uint16_t s16,
+                                             uint16_t z16, uint8_t *codes, float *vpre)
+{
+    if (D > 1024 || D % 8 || (bits != 4 && bits != 2))
+        return 1;
+    const float levels = (float)((1 << bits) - 1);
+    uint8_t q[1024];
+    if ((s16 & 0x7FFFu) == 0) {
+        for (int d = 0; d < D; ++d) {
+            q[d] = 0;
+            if (vpre)
+                vpre[d] = 0.0f;
+        }
+    } else {
+        const float sf = kvrq_oracle_f16_to_f32(s16);
+        const float zf = kvrq_oracle_f16_to_f32(z16);
+        const float inv = 1.0f / sf;
+        for (int d = 0; d < D; ++d) {
+            float t = y[d] - zf;
+            float v = t * inv;
+            float r = rintf(v);
+            if (r < 0.0f)
+                r = 0.0f;
+            if (r > levels)
+                r = levels;
+            q[d] = (uint8_t)r;
+            if (vpre)
+                vpre[d] = v;
+        }
+    }
+    for (int i = 0; i < D * bits / 8; ++i)
+        codes[i] = 0;
+    for (int d = 0; d < D; ++d)
+        codes[d * bits / 8] |= (uint8_t)(q[d] << ((d * bits) % 8));
+    return 0;
+}
+
 /* Quantise one row of D bf16 values with rotation block b to `bits` bits (4, or 2 for
  * the 2-bit variant the pages leave open: wispaper.ai blog, section 5, limitations).
  *   codes   D*bits/8 bytes; channel d sits at bit (d*bits) % 8 of byte d*bits/8
@@ -225,35 +267,7 @@ ORACLE_API int kvrq_oracle_quant_row(const uint16_t *x, int D, int b, int bits, 
     const uint16_t z16 = kvrq_oracle_f32_to_f16(mn);
     params[0] = s16;
     params[1] = z16;
-
-    uint8_t q[1024];
-    if ((s16 & 0x7FFFu) == 0) {
-        for (int d = 0; d < D; ++d) {
-            q[d] = 0;
-            if (vpre)
-                vpre[d] = 0.0f;
-        }
-    } else {
-        const float sf = kvrq_oracle_f16_to_f32(s16);
-        const float zf = kvrq_oracle_f16_to_f32(z16);
-        const float inv = 1.0f / sf;
-        for (int d = 0; d < D; ++d) {
-            float t = y[d] - zf;
-            float v = t * inv;
-            float r = rintf(v);
-            if (r < 0.0f)
-                r = 0.0f;
-            if (r > levels)
-                r = levels;
-            q[d] = (uint8_t)r;
-            if (vpre)
-                vpre[d] = v;
-        }
-    }
-    for (int i = 0; i < D * bits / 8; ++i)
-        codes[i] = 0;
-    for (int d = 0; d < D; ++d)
-        codes[d * bits / 8] |= (uint8_t)(q[d] << ((d * bits) % 8));
+    kvrq_oracle_codes_from_params(y, D, bits, s16, z16, codes, vpre);
     if (y_out)
         for (int d = 0; d < D; ++d)
             y_out[d] = y[d];

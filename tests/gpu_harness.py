@@ -17,6 +17,8 @@ import workloads as W
 D = 128
 BOUNDARY_REL = 1e-6      # excusal window for codes near a rounding boundary
 DECODE_ATOL = 2e-3       # attention output tolerance (absolute, fp32 accumulate)
+ROW_RTOL = 1e-3          # per output row: ||err|| <= ROW_RTOL ||ref|| + ROW_FLOOR
+ROW_FLOOR = 1e-4
 
 
 def log(msg: str) -> None:
@@ -48,11 +50,25 @@ def gpu_cache_arrays(cache) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndar
             cache.k_params.cpu().numpy().view(np.uint16), cache.v_params.cpu().numpy().view(np.uint16))
 
 
-def _nibbles(b: np.ndarray) -> np.ndarray:
-    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int64)
-    out[..., 0::2] = b & 15
-    out[..., 1::2] = b >> 4
+def _codes(b: np.ndarray, bits: int) -> np.ndarray:
+    """Packed code rows [..., D*bits/8] -> integer codes [..., D] (channel d at bit
+    (d*bits) % 8 of byte d*bits/8)."""
+    per = 8 // bits
+    out = np.empty(b.shape[:-1] + (per * b.shape[-1],), np.int64)
+    for j in range(per):
+        out[..., j::per] = (b >> (bits * j)) & ((1 << bits) - 1)
     return out
+
+
+def _count_codes(report, qg, qr, vpre):
+    """Differing codes of one row; a code is excused only if it differs by one and the
+    pre-round value lies within 1e-6 relative of the boundary between the two codes."""
+    for d in np.nonzero(qg != qr)[0]:
+        report["code_mismatch"] += 1
+        k = min(qg[d], qr[d])
+        if abs(int(qg[d]) - int(qr[d])) == 1 and \
+                abs(float(vpre[d]) - (k + 0.5)) <= BOUNDARY_REL * (k + 0.5):
+            report["code_excused"] += 1
 
 
 def compare_write(gpu: Tuple[np.ndarray, ...], orc: oracle.Cache, rows_src: Dict[str, np.ndarray],
@@ -60,7 +76,8 @@ def compare_write(gpu: Tuple[np.ndarray, ...], orc: oracle.Cache, rows_src: Dict
     """Compare whole pools byte for byte.  A differing code is excused (and counted) only if it
     differs by one and the oracle's pre-round value lies within 1e-6 relative of the boundary
     between the two codes; a differing fp16 parameter is excused only if the oracle's fp32
-    value lies within 1e-6 relative of the fp16 rounding midpoint between the two values."""
+    value lies within 1e-6 relative of the fp16 rounding midpoint between the two values, and
+    that row's codes are then checked against the oracle's codes for the GPU's parameters."""
     names = ("k", "v")
     ref = (orc.k_codes, orc.v_codes, orc.k_params, orc.v_params)
     report = {"code_mismatch": 0, "code_excused": 0, "param_mismatch": 0, "param_excused": 0,
@@ -68,10 +85,13 @@ def compare_write(gpu: Tuple[np.ndarray, ...], orc: oracle.Cache, rows_src: Dict
     if all(np.array_equal(g, r) for g, r in zip(gpu, ref)):
         return report
     P = orc.P
+    bits_of = {"k": orc.k_bits, "v": orc.v_bits}
     slot_to_t = {int(s): t for t, s in enumerate(slots) if s >= 0}
     for ti, name in enumerate(names):
         gc, gp = gpu[ti], gpu[2 + ti]
         rc, rp = ref[ti], ref[2 + ti]
+        bits = bits_of[name]
+        levels = np.float32((1 << bits) - 1)
         bad_cells = np.argwhere(np.any(gc != rc, axis=-1) | np.any(gp != rp, axis=-1))
         for page, h, off in bad_cells:
             slot = int(page) * P + int(off)
@@ -80,11 +100,12 @@ def compare_write(gpu: Tuple[np.ndarray, ...], orc: oracle.Cache, rows_src: Dict
                 report["placement_mismatch"] += 1
                 continue
             x = rows_src[name][t, h]
-            codes, params, vpre, y = oracle.quant_row(x, blocks[ti])
+            codes, params, vpre, y = oracle.quant_row(x, blocks[ti], bits)
+            qg = _codes(gc[page, h, off][None], bits)[0]
             if not np.array_equal(gp[page, h, off], params):
                 report["param_mismatch"] += 1
                 mn, mx = np.float32(y.min()), np.float32(y.max())
-                vals = (np.float32((mx - mn) / np.float32(15)), mn)
+                vals = (np.float32((mx - mn) / levels), mn)
                 ok = True
                 for j in range(2):
                     if gp[page, h, off, j] == params[j]:
@@ -94,15 +115,11 @@ def compare_write(gpu: Tuple[np.ndarray, ...], orc: oracle.Cache, rows_src: Dict
                     mid = (a + b) / 2
                     ok &= abs(float(vals[j]) - mid) <= BOUNDARY_REL * abs(mid)
                 report["param_excused"] += int(ok)
+                # the codes must be those the GPU's own parameters give (oracle rerun)
+                codes_g, vpre_g = oracle.codes_from_params(y, gp[page, h, off], bits)
+                _count_codes(report, qg, _codes(codes_g[None], bits)[0], vpre_g)
                 continue
-            qg = _nibbles(gc[page, h, off][None])[0]
-            qr = _nibbles(rc[page, h, off][None])[0]
-            for d in np.nonzero(qg != qr)[0]:
-                report["code_mismatch"] += 1
-                k = min(qg[d], qr[d])
-                if abs(int(qg[d]) - int(qr[d])) == 1 and \
-                        abs(float(vpre[d]) - (k + 0.5)) <= BOUNDARY_REL * (k + 0.5):
-                    report["code_excused"] += 1
+            _count_codes(report, qg, _codes(rc[page, h, off][None], bits)[0], vpre)
     return report
 
 
@@ -140,8 +157,20 @@ def run_write_case(K, k_bits: np.ndarray, v_bits: np.ndarray, slots: np.ndarray,
 
 
 def decode_compare(out_gpu: np.ndarray, out_ref: np.ndarray, label: str, atol: float = DECODE_ATOL):
+    """Attention outputs: every element within ``atol`` (2e-3, the contract), and every output
+    row (the D channels of one query head) within ROW_RTOL of its own norm plus ROW_FLOOR.
+    The kernel's own rounding (a 21-bit query grid, ~22-bit PV weights, fp32 sums) leaves
+    errors of 1e-6..4e-5 on O(0.1..1) rows, so the row bound is some 20x above what it does
+    while a regression of the arithmetic by that much fails it."""
     err = np.abs(out_gpu.astype(np.float64) - out_ref)
-    log(f"[{label}] decode max|err| = {err.max():.3e} (tolerance {atol})")
+    rows_e = np.sqrt((err.reshape(-1, err.shape[-1]) ** 2).sum(-1))
+    rows_r = np.sqrt((np.asarray(out_ref, np.float64).reshape(-1, err.shape[-1]) ** 2).sum(-1))
+    rel = rows_e / np.maximum(rows_r, 1e-30)
+    log(f"[{label}] decode max|err| = {err.max():.3e} (tolerance {atol}), max row rel "
+        f"{rel.max():.3e}")
     assert np.isfinite(out_gpu).all(), label
     assert err.max() <= atol, (label, err.max(), np.unravel_index(err.argmax(), err.shape))
+    bad = rows_e > ROW_RTOL * rows_r + ROW_FLOOR
+    assert not bad.any(), (label, "row error", int(bad.argmax()), float(rows_e[bad.argmax()]),
+                           float(rows_r[bad.argmax()]))
     return float(err.max())

@@ -200,3 +200,36 @@ def test_rotation_lowers_quantisation_error_on_outliers(oracle_mod):
     assert err[128] < err[0] / 4
     assert err[64] < err[0] / 4
     assert err[16] < err[0]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_codes_from_given_params(oracle_mod, bits):
+    """The write's last steps under parameters from elsewhere (what a checker needs when an
+    encoder's fp16 scale or zero lands one ulp off at a rounding midpoint): equal to the numpy
+    re-derivation for the row's own parameters and for every one-ulp neighbour of them, and
+    exact on a row built on the grid of arbitrary given parameters."""
+    import oracle.brute as br
+    rng = np.random.default_rng(60 + bits)
+    x = W.make_rows(rng, 64, 1, W.OutlierSpec.random(rng, 1))[:, 0]
+    for b in (0, 64):
+        for row in x[:16]:
+            codes, params, _, y = oracle_mod.quant_row(row, b, bits)
+            got, _ = oracle_mod.codes_from_params(y, params, bits)
+            assert np.array_equal(got, codes)
+            for ds, dz in ((1, 0), (-1, 0), (0, 1), (0, -1), (1, 1)):
+                p = (int(params[0]) + ds, int(params[1]) + dz)
+                got, vpre = oracle_mod.codes_from_params(y, p, bits)
+                ref, vref = br.codes_for_params(y, np.uint16(p[0]), np.uint16(p[1]), bits)
+                assert np.array_equal(got, ref) and np.array_equal(vpre, vref)
+    # on the grid of s = 0.375, z = -2.5 (both exact binary16): y = z + c s gives back c
+    levels = (1 << bits) - 1
+    c = rng.integers(0, levels + 1, size=D)
+    y = (np.float32(-2.5) + c.astype(np.float32) * np.float32(0.375)).astype(np.float32)
+    s16 = int(np.float16(0.375).view(np.uint16))
+    z16 = int(np.float16(-2.5).view(np.uint16))
+    got, vpre = oracle_mod.codes_from_params(y, (s16, z16), bits)
+    assert np.array_equal(br.unpack_codes(got[None], bits)[0], c)
+    assert np.array_equal(vpre, c.astype(np.float32))
+    # a zero scale gives all-zero codes
+    got, vpre = oracle_mod.codes_from_params(y, (0, z16), bits)
+    assert np.all(got == 0) and np.all(vpre == 0)
