@@ -9,15 +9,16 @@ walk, de-quantised attention, split-K combine, inverse V rotation).
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--variant ...]
 
 Workloads (sizes of the SAW-INT4 serving shapes; synthetic data):
-  qwen3_4b_like          (default) Hq=32, Hkv=8, 16 sequences of U{1024..4096}
-                         tokens, page 16 scattered, K block 64, V plain; a step
-                         writes every token, then decodes every sequence
+  qwen3_32b_like_decode  (default) Hq=64, Hkv=8, 256 log-normal sequences
+                         (~2.94M tokens), page 16 scattered, K block 128, V
+                         plain; a step writes 1 token per sequence and decodes
+                         all sequences over L+1; --variant fused does both in
+                         one kv_int4_paged_decode_step call
+  qwen3_4b_like          Hq=32, Hkv=8, 16 sequences of U{1024..4096} tokens,
+                         page 16 scattered, K block 64, V plain; a step writes
+                         every token, then decodes every sequence
   prefill_chunk          32768-token chunk write, Hkv=8, page 64 scattered;
                          --variant bdr (K block --k-block) | plain | bf16
-  qwen3_32b_like_decode  Hq=64, Hkv=8, 256 log-normal sequences (~2.94M
-                         tokens), page 16; a step writes 1 token per sequence
-                         and decodes all sequences over L+1; --variant fused
-                         does both in one kv_int4_paged_decode_step call
   small_batch_decode     the same step for 4 sequences of 4096 tokens, Hq=32,
                          Hkv=8 (latency-bound; --variant fused as above)
   long_context           1M-token sequence, Hq=64, Hkv=8, page 64, blocks
@@ -25,13 +26,16 @@ Workloads (sizes of the SAW-INT4 serving shapes; synthetic data):
   chunked_prefill        Hq=32, Hkv=8, 8 sequences with cached prefixes, each
                          extended by a 1024-token chunk: write + causal extend
 
-Prints ONE JSON line.  ``value`` is KV tokens/s over the timed steps (tokens
-written plus tokens attended, each token = all KV heads of K and V), wall
-clock between two device synchronisations, inputs already in HBM.  The
-``roofline`` object covers the kernel with the largest share of the step
-time: algorithmic bytes per launch / its mean launch time from HIP events on
-its stream.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the
-same workload (rank 0, N=1 only).
+Prints ONE JSON line.  ``value`` is KV tokens/s over the timed steps: the KV
+tokens the step's decode attends (each token = all KV heads of K and V; the
+step's own write included in the time), or, for a step with no decode, the
+tokens it writes; wall clock between two device synchronisations, inputs
+already in HBM.  ``rates`` gives each kernel's own rate from HIP events on its
+stream: the write's tokens written / write time and the decode's tokens
+attended / decode time.  The ``roofline`` object covers the kernel with the
+largest share of the step time: algorithmic bytes per launch / its mean launch
+time.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload in the same unit (rank 0, N=1 only).
 """
 from __future__ import annotations
 
@@ -78,7 +82,7 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default: per workload, as long as the timed ones: "
                          "MI355X clocks ramp up over the first few hundred milliseconds of load)")
-    ap.add_argument("--workload", default="qwen3_4b_like", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--workload", default="qwen3_32b_like_decode", choices=sorted(W.WORKLOADS))
     ap.add_argument("--variant", default="bdr", choices=["bdr", "plain", "bf16", "fused"],
                     help="prefill_chunk: fused BDR write, plain INT4 write, or bf16 paged copy; "
                          "qwen3_32b_like_decode: fused = write + decode in one call")
@@ -88,6 +92,8 @@ def parse_args(argv=None):
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle threads (0: every core of the process's affinity)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="(accepted for older scripts: the 1 GiB copy probe always runs)")
     ap.add_argument("--counters", default=None,
@@ -240,7 +246,8 @@ class Setup:
         self.ws = torch.zeros(n, dtype=torch.uint8, device=self.dev)
         self.kernels = {"kv_rotquant_write": self.write_bytes(T, Hkv),
                         "kv_int4_paged_decode": self.decode_bytes(w.seq_lens, Hkv, Hq, w.page_size)}
-        self.tokens_per_step = T + int(w.seq_lens.sum())
+        self.rate_tokens = {"kv_rotquant_write": T, "kv_int4_paged_decode": int(w.seq_lens.sum())}
+        self.tokens_per_step = int(w.seq_lens.sum())
         self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                        "num_seqs": w.num_seqs, "tokens_written": T,
                        "tokens_attended": int(w.seq_lens.sum()), "page_size": w.page_size,
@@ -280,6 +287,7 @@ class Setup:
         name = "kvrq_bf16_paged_write" if variant == "bf16" else "kv_rotquant_write"
         nbytes = T * (Hkv * 2 * (2 * D + 2 * D) + 4) if variant == "bf16" else self.write_bytes(T, Hkv)
         self.kernels = {name: nbytes}
+        self.rate_tokens = {name: T}
         self.tokens_per_step = T
         self.config = {"workload": w.name, "variant": variant, "num_kv_heads": Hkv, "head_dim": D,
                        "tokens_written": T, "page_size": w.page_size, "k_block": kb, "v_block": 0}
@@ -319,17 +327,22 @@ class Setup:
         self.out = torch.empty((S, Hq, D), dtype=torch.float32, device=self.dev)
         n = K.kv_int4_paged_decode_workspace(self.cache, S, Hq, self.maxlen, self.args.split_tokens)
         self.ws = torch.zeros(n, dtype=torch.uint8, device=self.dev)
-        mid = w.seq_lens + n_steps // 2
+        # timed step i decodes over seq_lens + j + 1 (j = i mod n_steps): the algorithmic bytes
+        # and tokens are averaged over exactly the timed steps
+        js = [(self.args.warmup + i) % n_steps for i in range(self.args.steps)]
+        dec_bytes = float(np.mean([self.decode_bytes(w.seq_lens + j + 1, Hkv, Hq, P) for j in js]))
+        attended = float(np.mean([int(w.seq_lens.sum()) + S * (j + 1) for j in js]))
         if self.args.variant == "fused":
-            self.kernels = {"kv_int4_paged_decode_step": self.write_bytes(S, Hkv)
-                            + self.decode_bytes(mid, Hkv, Hq, P)}
+            self.kernels = {"kv_int4_paged_decode_step": round(self.write_bytes(S, Hkv) + dec_bytes)}
+            self.rate_tokens = {"kv_int4_paged_decode_step": attended}
         else:
             self.kernels = {"kv_rotquant_write": self.write_bytes(S, Hkv),
-                            "kv_int4_paged_decode": self.decode_bytes(mid, Hkv, Hq, P)}
-        self.tokens_per_step = S + int(mid.sum())
+                            "kv_int4_paged_decode": round(dec_bytes)}
+            self.rate_tokens = {"kv_rotquant_write": S, "kv_int4_paged_decode": attended}
+        self.tokens_per_step = attended
         self.n_steps_max = n_steps
         self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
-                       "num_seqs": S, "tokens_written": S, "tokens_attended_mid": int(mid.sum()),
+                       "num_seqs": S, "tokens_written": S, "tokens_attended_mean": round(attended),
                        "page_size": P, "k_block": kb, "v_block": w.v_block,
                        "variant": "fused" if self.args.variant == "fused" else "write+decode"}
 
@@ -377,7 +390,8 @@ class Setup:
         self.kernels = {"kv_rotquant_write": self.write_bytes(C, Hkv),
                         "kv_int4_paged_decode": self.decode_bytes([L], Hkv, Hq, P)}
         self.launch_count = {"kv_rotquant_write": L // C, "kv_int4_paged_decode": 1}
-        self.tokens_per_step = 2 * L
+        self.rate_tokens = {"kv_rotquant_write": C, "kv_int4_paged_decode": L}
+        self.tokens_per_step = L
         self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                        "context": L, "chunk": C, "page_size": P, "k_block": w.k_block,
                        "v_block": w.v_block}
@@ -427,6 +441,7 @@ class Setup:
                                                     + np.ceil(w.seq_lens / P).sum() * 4)}
         # QK^T and PV: 2 D flops each per (row, head, key)
         self.kernel_flops = {"kv_int4_paged_extend": pairs * Hq * 4 * D}
+        self.rate_tokens = {"kv_rotquant_write": T, "kv_int4_paged_extend": T}
         self.tokens_per_step = T
         self.unit = "prefill tokens/s"
         self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
@@ -458,7 +473,8 @@ class Setup:
         self.lens = self.dev_i32(w.seq_lens)
         self.kernels = {"kv_rotquant_write": self.write_bytes(64, 1),
                         "kv_int4_paged_decode": self.decode_bytes([64], 1, 1, 16)}
-        self.tokens_per_step = 128
+        self.rate_tokens = {"kv_rotquant_write": 64, "kv_int4_paged_decode": 64}
+        self.tokens_per_step = 64
         self.config = {"workload": w.name, "num_q_heads": 1, "num_kv_heads": 1, "head_dim": D,
                        "tokens_written": 64, "tokens_attended": 64, "page_size": 16,
                        "k_block": 128, "v_block": 128}
@@ -477,22 +493,25 @@ class Setup:
 
 # ------------------------------------------------------------------ CPU oracle baseline
 def cpu_baseline(args):
-    """Time the oracle (as it stands) on a bounded sample of the same workload."""
+    """Time the oracle (as it stands) on a bounded sample of the same workload, in the unit of
+    ``value``: KV tokens attended per second of write + decode (tokens written per second for
+    the write-only workload, prefill tokens per second for the extend)."""
     import oracle
     oracle.build(force=False)
-    cores = len(os.sched_getaffinity(0))
+    cores = oracle.set_threads(args.cpu_threads or len(os.sched_getaffinity(0)))
     w = W.WORKLOADS[args.workload]()
     kb = args.k_block if args.k_block is not None else w.k_block
     if args.workload == "prefill_chunk" and args.variant == "plain":
         kb = 0
     rng = w.rng(77)
+    threads = f"OMP threads={cores}"
     if args.workload == "chunked_prefill":
-        return cpu_baseline_extend(args, w, kb, rng, cores)
+        return cpu_baseline_extend(args, w, kb, rng, cores, threads)
+    if args.workload in ("qwen3_32b_like_decode", "small_batch_decode"):
+        return cpu_baseline_steps(args, w, kb, rng, cores, threads)
     # sample: up to 8 sequences (long context: 65536 tokens) of the workload's own shapes
     if args.workload == "long_context":
         lens = np.array([65536])
-    elif args.workload in ("qwen3_32b_like_decode", "small_batch_decode"):
-        lens = w.seq_lens[:4]
     else:
         lens = w.seq_lens[:8]
     paging = W.assign_pages(rng, list(lens), w.page_size)
@@ -513,15 +532,49 @@ def cpu_baseline(args):
             oracle.decode(q, (cache.k_codes, cache.v_codes, cache.k_params, cache.v_params), tab,
                           lens.astype(np.int32), w.num_kv_heads, w.page_size, kb, w.v_block)
         t_total += time.perf_counter() - t0
-        tokens += T * (2 if decode else 1)
+        tokens += T       # each token written once and (with a decode) attended once
         reps += 1
     what = f"{reps} x (write {T} tokens" + (f" + decode {len(lens)} sequences)" if decode else ")")
     return {"value": tokens / t_total, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{what}, {args.workload} shapes, OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', cores)}",
+            "sample": f"{what}, {args.workload} shapes, {threads}", "seconds": round(t_total, 3)}
+
+
+def cpu_baseline_steps(args, w, kb, rng, cores, threads):
+    """Decode steps on a sample of the workload's sequences (their prefixes written untimed):
+    each timed rep writes one new token per sampled sequence and decodes the sampled sequences
+    over it, as a GPU step does for all of them."""
+    import oracle
+    lens = w.seq_lens[:4].astype(np.int64)
+    steps = int(w.notes["steps"])
+    paging = W.assign_pages(rng, [int(L) + steps for L in lens], w.page_size)
+    cache = oracle.Cache(paging.num_pages, w.num_kv_heads, w.page_size, k_bits=args.k_bits,
+                         v_bits=args.v_bits)
+    for s, L in enumerate(lens):
+        oracle.write(cache, W.make_rows(rng, int(L), w.num_kv_heads, w.k_out),
+                     W.make_rows(rng, int(L), w.num_kv_heads, w.v_out), paging.slots(s, 0, int(L)),
+                     kb, w.v_block)
+    q = W.f32_to_bf16_bits(rng.standard_normal((len(lens), w.num_q_heads, D)).astype(np.float32))
+    tab = paging.page_table()
+    reps, t_total, tokens = 0, 0.0, 0
+    while t_total < args.cpu_seconds and reps < steps:
+        k = W.make_rows(rng, len(lens), w.num_kv_heads, w.k_out)
+        v = W.make_rows(rng, len(lens), w.num_kv_heads, w.v_out)
+        slots = np.array([paging.slots(s, int(L) + reps, 1)[0] for s, L in enumerate(lens)], np.int32)
+        cur = (lens + reps + 1).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.write(cache, k, v, slots, kb, w.v_block)
+        oracle.decode(q, (cache.k_codes, cache.v_codes, cache.k_params, cache.v_params), tab, cur,
+                      w.num_kv_heads, w.page_size, kb, w.v_block)
+        t_total += time.perf_counter() - t0
+        tokens += int(cur.sum())
+        reps += 1
+    return {"value": tokens / t_total, "unit": "KV tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} steps x (write 1 token + decode) of {len(lens)} sequences of "
+                      f"{args.workload} ({int(lens.sum())} cached tokens), {threads}",
             "seconds": round(t_total, 3)}
 
 
-def cpu_baseline_extend(args, w, kb, rng, cores):
+def cpu_baseline_extend(args, w, kb, rng, cores, threads):
     """Oracle write of a chunk + causal extend, on the workload's first sequence with a
     256-token chunk (prefix as in the workload)."""
     import oracle
@@ -548,7 +601,7 @@ def cpu_baseline_extend(args, w, kb, rng, cores):
         reps += 1
     return {"value": reps * C / t_total, "unit": "prefill tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} x (write {C} tokens + extend {C} rows over {L} tokens), "
-                      f"chunked_prefill shapes, OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', cores)}",
+                      f"chunked_prefill shapes, {threads}",
             "seconds": round(t_total, 3)}
 
 
@@ -705,6 +758,13 @@ def main():
 
     ms_per_step = elapsed / args.steps * 1e3
     value = s.tokens_per_step * args.steps / elapsed
+    # each kernel's own rate: tokens it writes (write) or attends (decode, extend) per second
+    rates = {}
+    for name in names:
+        pk = per_kernel[name]
+        rates[name] = {"tokens_per_launch": round(s.rate_tokens[name]),
+                       "tokens_per_s": round(s.rate_tokens[name] / (pk["mean_us"] * 1e-6), 1),
+                       "hbm_frac": round(pk["algorithmic_gbps"] / HBM_PEAK_GBPS, 4)}
     result = {
         "metric": "KV tokens/s and achieved HBM GB/s (% of peak) for rotquant write + INT4 decode",
         "value": round(value, 1),
@@ -716,11 +776,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp32 compute, int4+fp16 cache",
+        "dtype": "bf16 in; write fp32; decode int8 MFMA (int4 codes x 21-bit query grid, exact "
+                 "i32) + f16 MFMA (PV, hi/lo weights), fp32 accumulate; int4 + fp16 cache",
         "data": "synthetic (seeded N(0,1) with outlier channels; no model weights)",
         "config": dict(s.config, **({"k_bits": args.k_bits, "v_bits": args.v_bits}
                                     if (args.k_bits, args.v_bits) != (4, 4) else {})),
         "kernels": per_kernel,
+        "rates": rates,
         "roofline": roofline,
         "hbm_gbps_step": round(sum(per_kernel[n]["algorithmic_bytes"] * per_kernel[n]["launches_per_step"]
                                    for n in names) / (ms_per_step * 1e-3) / 1e9, 1),
