@@ -71,6 +71,10 @@ extern "C" {
 
 typedef int32_t kvrq_status;
 
+/* split_tokens value of the decode calls that selects the balanced grid (see
+ * kv_int4_paged_decode). */
+#define KVRQ_SPLIT_BALANCED (-1)
+
 enum {
     KVRQ_OK = 0,
     KVRQ_EINVAL = 1,        /* null pointer, negative size, bad alignment, bad shape */
@@ -190,9 +194,9 @@ KVRQ_API kvrq_status kv_rotquant_write(const kvrq_cache_desc *d, const kvrq_cach
 
 /* Workspace bytes kv_int4_paged_decode needs for num_seqs sequences of at
  * most max_seq_len tokens with num_q_heads query heads and the given
- * split_tokens (0 = automatic, as in the decode call).  0 when a single split
- * covers max_seq_len: the split kernel then writes the output itself and the
- * workspace may be NULL. */
+ * split_tokens (0 = automatic, KVRQ_SPLIT_BALANCED, or a split size, as in the
+ * decode call).  0 when a single split covers max_seq_len: the split kernel
+ * then writes the output itself and the workspace may be NULL. */
 KVRQ_API kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, int32_t num_seqs,
                                            int32_t num_q_heads, int32_t max_seq_len,
                                            int32_t split_tokens, size_t *bytes);
@@ -209,8 +213,19 @@ KVRQ_API kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, in
  *                   zero row
  *   max_seq_len     host bound on every L, used to plan the splits
  *   sm_scale        softmax scale; <= 0 selects 1/sqrt(head_dim)
- *   split_tokens    tokens per split-K partition (one workgroup of four
- *                   waves); 0 = automatic, otherwise a multiple of 128
+ *   split_tokens    how the (sequence, KV head, token) work is cut:
+ *                   0 = automatic; a multiple of 128 = split workgroups of that
+ *                   many tokens (four waves each); KVRQ_SPLIT_BALANCED = the
+ *                   balanced grid: one resident round of workgroups, each
+ *                   taking an equal share of every sequence's 32-token tiles
+ *                   in (sequence, KV head, tile) order (at most 1024
+ *                   sequences and 16384 sequence x KV head pairs, else
+ *                   KVRQ_EUNSUPPORTED).  The automatic choice is the balanced
+ *                   grid when num_seqs * num_kv_heads * max_seq_len reaches
+ *                   2^22 tokens (work for several rounds of split
+ *                   workgroups) and the shape fits it; otherwise splits of
+ *                   4 x clamp(S * Hkv * max_seq_len / 8192, 256, 1024) tokens,
+ *                   raised to keep at most 64 splits
  *   out             device fp32 [num_seqs][num_q_heads][head_dim]
  *   workspace       device scratch of workspace_bytes >= the size reported by
  *                   kv_int4_paged_decode_workspace (16-byte aligned; unused,
@@ -224,11 +239,12 @@ KVRQ_API kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, in
  * Computes, per sequence s and query head g (KV head h):
  *   q' = H_bK q,  score_t = sm_scale * q'.(code_t * scale_t + zero_t),
  *   o' = sum_t softmax(score)_t (V code_t * scale_t + zero_t),  out = H_bV o'.
- * One launch on `stream` when a single split covers max_seq_len, or when
- * every split workgroup fits on the device at once, there are at most 16
- * splits and num_seqs * num_kv_heads <= 16384: the last split of each
- * (sequence, KV head) to finish merges the partials (the counters elect it).
- * Otherwise two launches: the split-K partials, then the combine. */
+ * One launch on `stream` for the balanced grid, when a single split covers
+ * max_seq_len, or when every split workgroup fits on the device at once,
+ * there are at most 16 splits and num_seqs * num_kv_heads <= 16384: the last
+ * workgroup of each (sequence, KV head) to finish merges the partials (the
+ * counters elect it).  Otherwise two launches: the split-K partials, then the
+ * combine. */
 KVRQ_API kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
                                  const void *q, int32_t num_seqs, int32_t num_q_heads,
                                  const int32_t *page_table, int32_t max_pages_per_seq,

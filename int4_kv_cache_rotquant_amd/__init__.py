@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     KVRQ_EUNSUPPORTED,
     KVRQ_EWORKSPACE,
     KVRQ_OK,
+    KVRQ_SPLIT_BALANCED,
     KvrqError,
     LIB_PATH,
     PagedInt4Cache,

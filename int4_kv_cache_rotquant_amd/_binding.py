@@ -7,7 +7,6 @@ The functions keep the C names; tensors stand in for the raw pointers.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Tuple
 
@@ -15,6 +14,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libkvrq.so")
 
 KVRQ_OK, KVRQ_EINVAL, KVRQ_EUNSUPPORTED, KVRQ_ENOPAGES, KVRQ_EHIP, KVRQ_EWORKSPACE = range(6)
+KVRQ_SPLIT_BALANCED = -1      # split_tokens of the decode calls: the balanced grid
 HEAD_DIM = 128
 
 
@@ -345,11 +345,3 @@ class Pool:
         _check(lib().kvrq_page_table(self._h, tab.ctypes.data_as(ctypes.c_void_p),
                                      lens.ctypes.data_as(ctypes.c_void_p)))
         return tab, lens
-
-
-def ceil_div(a: int, b: int) -> int:
-    return -(-a // b)
-
-
-def log2_int(x: int) -> int:
-    return int(math.log2(x))

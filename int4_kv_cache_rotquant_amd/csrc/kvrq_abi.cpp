@@ -116,17 +116,45 @@ kvrq_status hip_status(int err, const char *what)
     return fail(KVRQ_EHIP, "%s: %s", what, kvrq::hip_error_string(err));
 }
 
-// Decode split plan.  A workgroup of kDecodeWaves waves takes split_tokens
-// consecutive tokens of one (sequence, KV head), each wave a quarter.  The
-// automatic size gives every wave split_tokens/4 = clamp(S * Hkv * max_len /
-// 8192, 64, 1024) tokens (a multiple of 32): an upper bound of the work spread
-// over ~8192 waves, several per SIMD, while each wave still streams enough
-// tiles to hide its prologue and the split partials stay a few percent of the
-// cache bytes.
+// The balanced decode (one resident round of workgroups sharing the tiles equally) serves an
+// automatic plan with enough work for several rounds of split workgroups; a split grid pays
+// where the work is small (one round, little tail) or the split size is forced.
+constexpr int64_t kBalancedMinTokens = int64_t(1) << 22;
+
+// The balanced decode can serve the shape: its tile prefix sums fit LDS and int32, and every
+// (sequence, KV head) has a counter.
+bool balanced_fits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len)
+{
+    const int64_t tiles = (int64_t(max_seq_len) + kvrq::kTile - 1) / kvrq::kTile;
+    return num_seqs <= kvrq::kBalancedMaxSeqs &&
+           int64_t(num_seqs) * num_kv_heads <= kvrq::kSplitCounters &&
+           int64_t(num_seqs) * tiles < (int64_t(1) << 31);
+}
+
+bool use_balanced(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t split_tokens)
+{
+    if (split_tokens == KVRQ_SPLIT_BALANCED)
+        return true;   // checked to fit by check_decode_shape
+    return split_tokens == 0 && balanced_fits(num_seqs, num_kv_heads, max_seq_len) &&
+           int64_t(num_seqs) * num_kv_heads * max_seq_len >= kBalancedMinTokens;
+}
+
+// Decode plan.  Balanced where use_balanced says so; otherwise split workgroups: a workgroup
+// of kDecodeWaves waves takes split_tokens consecutive tokens of one (sequence, KV head), each
+// wave a quarter.  The automatic size gives every wave split_tokens/4 = clamp(S * Hkv *
+// max_len / 8192, 256, 1024) tokens (a multiple of 32): an upper bound of the work spread over
+// ~8192 waves, several per SIMD, while each wave still streams enough tiles to hide its
+// prologue and the split partials stay a few percent of the cache bytes.
 kvrq::DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                              int32_t split_tokens)
 {
     kvrq::DecodePlan p;
+    if (use_balanced(num_seqs, num_kv_heads, max_seq_len, split_tokens)) {
+        p.split_tokens = 0;
+        p.max_splits = 0;
+        p.balanced_wgs = kvrq::kBalancedMaxWgs;   // sized for the most; the launch takes fewer
+        return p;
+    }
     if (split_tokens <= 0) {
         // tokens per wave: enough (sequence, KV head, split) workgroups to fill the chip,
         // at least 8 tiles per wave so the per-workgroup query set-up and the combine stay
@@ -148,11 +176,31 @@ kvrq::DecodePlan plan_decode(int32_t num_seqs, int32_t num_kv_heads, int32_t max
     return p;
 }
 
+// Groups of the balanced decode: Hkv workgroups each, at most kBalancedMaxWgs workgroups in
+// all (at least one group).
+int32_t balanced_groups_max(int32_t num_kv_heads)
+{
+    return std::max<int32_t>(1, kvrq::kBalancedMaxWgs / num_kv_heads);
+}
+
+// Partial slots of the balanced decode: (group + sequence) * Hkv + KV head.
+size_t balanced_slots(int32_t num_seqs, int32_t num_kv_heads)
+{
+    return (size_t(balanced_groups_max(num_kv_heads)) + size_t(num_seqs)) * num_kv_heads;
+}
+
 // The split counters, then the split partials; nothing when a single split writes the
 // output itself.  Decode and extend lay a workspace out alike, so one workspace serves both
 // (the extend leaves the counters alone).
-size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const kvrq::DecodePlan &p)
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, const kvrq::DecodePlan &p,
+                              int32_t num_kv_heads = 1)
 {
+    if (p.balanced_wgs > 0) {
+        // partial slots: (group + sequence) * Hkv + KV head, G query heads each
+        const size_t slots = balanced_slots(num_seqs, num_kv_heads);
+        const size_t rows = slots * size_t(num_q_heads / num_kv_heads);
+        return kvrq::kCounterBytes + rows * (kvrq::kHeadDim + 2) * sizeof(float);
+    }
     if (p.max_splits == 1)
         return 0;
     const size_t rows = size_t(num_seqs) * num_q_heads * p.max_splits;
@@ -176,9 +224,14 @@ kvrq_status check_decode_shape(const kvrq_cache_desc *d, int32_t num_seqs, int32
         return fail(KVRQ_EUNSUPPORTED, "decode needs page_size >= 16 (got %d)", d->page_size);
     if (max_seq_len < 0)
         return fail(KVRQ_EINVAL, "max_seq_len must be >= 0");
-    if (split_tokens < 0 || split_tokens % (kvrq::kTile * kvrq::kDecodeWaves))
-        return fail(KVRQ_EINVAL, "split_tokens must be 0 or a positive multiple of %d",
-                    kvrq::kTile * kvrq::kDecodeWaves);
+    if (split_tokens == KVRQ_SPLIT_BALANCED) {
+        if (!balanced_fits(num_seqs, d->num_kv_heads, max_seq_len))
+            return fail(KVRQ_EUNSUPPORTED, "the balanced decode takes at most %d sequences and %d "
+                        "(sequence, KV head) pairs", kvrq::kBalancedMaxSeqs, kvrq::kSplitCounters);
+    } else if (split_tokens < 0 || split_tokens % (kvrq::kTile * kvrq::kDecodeWaves)) {
+        return fail(KVRQ_EINVAL, "split_tokens must be 0, KVRQ_SPLIT_BALANCED or a positive "
+                    "multiple of %d", kvrq::kTile * kvrq::kDecodeWaves);
+    }
     if (num_seqs > 65535)
         return fail(KVRQ_EUNSUPPORTED, "num_seqs above 65535");
     return KVRQ_OK;
@@ -195,6 +248,8 @@ kvrq_status check_extend_shape(const kvrq_cache_desc *d, int32_t num_seqs, int32
                                int32_t total_q, int32_t max_q_len, int32_t max_seq_len,
                                int32_t split_tokens)
 {
+    if (split_tokens == KVRQ_SPLIT_BALANCED)
+        return fail(KVRQ_EUNSUPPORTED, "the extend has no balanced grid (split_tokens -1)");
     kvrq_status st = check_decode_shape(d, num_seqs, num_q_heads, max_seq_len, split_tokens);
     if (st)
         return st;
@@ -464,7 +519,8 @@ kvrq_status kv_int4_paged_decode_workspace(const kvrq_cache_desc *d, int32_t num
     if (!bytes)
         return fail(KVRQ_EINVAL, "bytes is NULL");
     *bytes = decode_workspace_bytes(num_seqs, num_q_heads,
-                                    plan_decode(num_seqs, d->num_kv_heads, max_seq_len, split_tokens));
+                                    plan_decode(num_seqs, d->num_kv_heads, max_seq_len, split_tokens),
+                                    d->num_kv_heads);
     return KVRQ_OK;
 }
 
@@ -508,13 +564,13 @@ kvrq_status decode_impl(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, c
     if (!std::isfinite(sm_scale))
         return fail(KVRQ_EINVAL, "sm_scale must be finite");
     const kvrq::DecodePlan plan = plan_decode(num_seqs, d->num_kv_heads, max_seq_len, split_tokens);
-    const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, plan);
+    const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, plan, d->num_kv_heads);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(KVRQ_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : size_t(0));
     if (need > 0 && !aligned(workspace, 16))
         return fail(KVRQ_EINVAL, "workspace must be 16-byte aligned");
-    if (plan.max_splits > 65535 * 64)
+    if (plan.balanced_wgs == 0 && plan.max_splits > 65535 * 64)
         return fail(KVRQ_EUNSUPPORTED, "too many splits");
 
     kvrq::DecodeArgs a;
@@ -526,8 +582,22 @@ kvrq_status decode_impl(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, c
     a.page_table = page_table;
     a.seq_lens = seq_lens;
     a.out = out;
-    const size_t rows = size_t(num_seqs) * num_q_heads * plan.max_splits;
-    if (plan.max_splits > 1) {
+    if (plan.balanced_wgs > 0) {
+        const size_t slots = balanced_slots(num_seqs, d->num_kv_heads);
+        const size_t rows = slots * size_t(num_q_heads / d->num_kv_heads);
+        a.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + kvrq::kCounterBytes);
+        a.part_ml = a.part_o + rows * kvrq::kHeadDim;
+        a.counters = static_cast<int32_t *>(workspace);
+        // one resident round, in whole groups of Hkv workgroups
+        const int32_t groups = std::max<int32_t>(1, std::min<int32_t>(
+            kvrq::decode_resident_wgs(num_q_heads / d->num_kv_heads) / d->num_kv_heads,
+            balanced_groups_max(d->num_kv_heads)));
+        a.balanced_wgs = groups * d->num_kv_heads;
+        // pairs that span many groups (few sequences: the long-context decode) are merged by
+        // a combine launch, 32 partials at a time; otherwise by their last workgroup
+        a.balanced_combine = int64_t(num_seqs) * 8 <= groups ? 1 : 0;
+    } else if (plan.max_splits > 1) {
+        const size_t rows = size_t(num_seqs) * num_q_heads * plan.max_splits;
         a.part_o = reinterpret_cast<float *>(static_cast<char *>(workspace) + kvrq::kCounterBytes);
         a.part_ml = a.part_o + rows * kvrq::kHeadDim;
         // counters for every (sequence, KV head): the launch may then merge the partials in

@@ -189,6 +189,12 @@ constexpr uint32_t kMant47 = 0x00F000F0u;   // mantissa bits 4..7 of both halves
 // Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
 
+// Cache policy of the tile loads: the default.  A plain streaming read runs faster with
+// non-temporal loads on MI355X (7.0 against 6.3 TB/s), but the decode's page walk measured
+// slower with them (the Qwen3-32B-like decode 641 -> 657 us, the 1M-token one 223 -> 242 us),
+// and the extend, which re-reads a sequence's tiles from the L2, much slower.
+constexpr int kTileLoadAux = 0;
+
 // K codes become int8 MFMA operands: the even and the odd nibbles of a dword, masked in
 // place, are four bytes each.  Scores are integer dot products of codes with the query
 // rounded to a 21-bit grid (three int8 digits), exact in the int32 accumulators.
@@ -267,23 +273,44 @@ __device__ __forceinline__ u32x4 k_nibbles(const u32x2 &k)
 // Issues the loads of the tile starting at t0 (< t_end).  A half tile that starts past
 // the end re-reads the first half's rows: every load is in bounds and unconditional, and
 // tokens past the end are removed by their parameters (zero) and score bias (-inf).
-// Page ids of up to 64 consecutive pages of a sequence, one per lane, so a tile's pages
-// come from readlane instead of a scalar load whose latency every tile would wait for.
+// Page ids of a window of 128 consecutive pages of a sequence, two per lane, so a tile's
+// pages come from readlane instead of a scalar load whose latency every tile would wait for.
+// The window moves on by 64 pages when a tile reaches past it; the ids of the new upper half
+// are requested then, 64 pages before any tile needs them.
 struct PageIds {
-    int first;   // page index held by lane 0 (uniform)
+    int first;   // page index held by lane 0 of `id` (uniform)
     int id;      // lane j: page id of page index first + j (out-of-range ids read as 0)
+    int next;    // lane j: page id of page index first + 64 + j
 
+    __device__ __forceinline__ static int get(const DecodeArgs &a, const int32_t *ptab, int k)
+    {
+        const int v = k < a.max_pages ? ptab[k] : 0;
+        return (unsigned)v < (unsigned)a.num_pages ? v : 0;
+    }
     __device__ __forceinline__ void fill(const DecodeArgs &a, const int32_t *ptab, int first_page,
                                          int lane)
     {
         first = first_page;
-        const int k = first_page + lane;
-        const int v = k < a.max_pages ? ptab[k] : 0;
-        id = (unsigned)v < (unsigned)a.num_pages ? v : 0;
+        id = get(a, ptab, first_page + lane);
+        next = get(a, ptab, first_page + 64 + lane);
+    }
+    // page indexes up to `last` become reachable (callers ask in increasing order, at most
+    // a few pages past the window)
+    __device__ __forceinline__ void reach(const DecodeArgs &a, const int32_t *ptab, int last,
+                                          int lane)
+    {
+        if (last - first >= 128) {
+            first += 64;
+            id = next;
+            next = get(a, ptab, first + 64 + lane);
+        }
     }
     __device__ __forceinline__ int page(int page_index) const
     {
-        return __builtin_amdgcn_readlane(id, page_index - first);
+        const int j = page_index - first;
+        const int lo = __builtin_amdgcn_readlane(id, j & 63);
+        const int hi = __builtin_amdgcn_readlane(next, j & 63);
+        return j < 64 ? lo : hi;
     }
 };
 
@@ -338,13 +365,13 @@ struct RowBlock {
         if constexpr (!BUF)
             return *reinterpret_cast<const T *>(p + lane_off + row_off);
         else if constexpr (sizeof(T) == 16)
-            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, row_off, 0));
+            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, row_off, kTileLoadAux));
         else if constexpr (sizeof(T) == 8)
-            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)lane_off, row_off, 0));
+            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)lane_off, row_off, kTileLoadAux));
         else if constexpr (sizeof(T) == 4)
-            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, (int)lane_off, row_off, 0));
+            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, (int)lane_off, row_off, kTileLoadAux));
         else
-            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, (int)lane_off, row_off, 0));
+            return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, (int)lane_off, row_off, kTileLoadAux));
     }
 };
 
@@ -356,6 +383,11 @@ __device__ __forceinline__ void load_tile(Tile<CB> &T, const DecodeArgs &a, cons
 {
     using CW = CodeWidths<CB>;
     const int P = 1 << a.page_log2;
+    // The tile's loads stay together, in this order, after the code before the call: loads
+    // moved across the consumption of the tile before would leave the in-order load counter
+    // unable to tell the two tiles in flight apart, and the wait before each tile would then
+    // wait for both (measured: the page walk streamed ~10% slower).
+    __builtin_amdgcn_sched_barrier(0);
     // (page, head) row blocks of the two 16-token halves; uniform, so on the scalar unit
     // (cells, page * Hkv * P + token, are below 2^32)
     uint32_t cell[2];
@@ -387,6 +419,7 @@ __device__ __forceinline__ void load_tile(Tile<CB> &T, const DecodeArgs &a, cons
     const uint32_t *kp0 = a.k_params + cell[0], *kp1 = a.k_params + cell[1];
     const uint32_t *vp0 = a.v_params + cell[0], *vp1 = a.v_params + cell[1];
     T.par = *((la.lane < 32 ? (ph ? kp1 : kp0) : (ph ? vp1 : vp0)) + (la.lane & 15));
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // B operands of QK^T in lane order: the query rounded to integers q = round(q' 2^f)
@@ -678,6 +711,66 @@ __device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile<CB>
     }
 }
 
+// ---- a7..a9: one wave's page walk over the tokens [t_begin, t_end), two register tiles in
+// flight: each is refilled with the tile two ahead right after it is consumed, so the same
+// loads are outstanding at every tile and the wait before a tile covers that tile's loads
+// only.  The loop has one exit and issues both prefetches in every pass (a prefetch past the
+// last tile re-reads it, an L2 hit): a path into the loop head with one tile in flight would
+// make the compiler wait for both tiles everywhere.  The page-id window moves along with the
+// prefetches, so the pipeline runs through the whole range without draining.
+template <int F, bool EXT, int CB, int NB, bool BUF>
+__device__ __forceinline__ void walk_tiles(WaveState (&st)[NB], const DecodeArgs &a, PageIds &pid,
+                                           const int32_t *ptab, int h, int t_begin, int t_end,
+                                           int lane, float kscale, const QOperand<F> *qop,
+                                           ParLds &pl, const int (&col_len)[NB], int mask_from)
+{
+    const int n = (t_end - t_begin + kTile - 1) / kTile;
+    if (n <= 0)
+        return;
+    LaneAddr la;
+    la.init<CB>(lane);
+    const int last = t_begin + (n - 1) * kTile;   // start of the last tile
+    // the largest page index a tile starting at t reads
+    auto top_page = [&](int t) { return (min(t + kTile, t_end) - 1) >> a.page_log2; };
+    Tile<CB> A, B;
+    load_tile<CB, BUF>(A, a, pid, h, t_begin, t_end, la);
+    {
+        const int tb = min(t_begin + kTile, last);
+        pid.reach(a, ptab, top_page(tb), lane);
+        load_tile<CB, BUF>(B, a, pid, h, tb, t_end, la);
+    }
+    int i = 0;
+    for (; i + 2 < n; i += 2) {
+        const int ta = t_begin + i * kTile;
+        consume_tile<F, EXT, CB, NB>(st, A, ta, t_end, lane, kscale, qop, pl, col_len, mask_from);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            st[b].tick();
+        pid.reach(a, ptab, top_page(ta + 2 * kTile), lane);
+        load_tile<CB, BUF>(A, a, pid, h, ta + 2 * kTile, t_end, la);
+        consume_tile<F, EXT, CB, NB>(st, B, ta + kTile, t_end, lane, kscale, qop, pl, col_len,
+                                     mask_from);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            st[b].tick();
+        const int tb = min(ta + 3 * kTile, last);
+        pid.reach(a, ptab, top_page(tb), lane);
+        load_tile<CB, BUF>(B, a, pid, h, tb, t_end, la);
+    }
+    consume_tile<F, EXT, CB, NB>(st, A, t_begin + i * kTile, t_end, lane, kscale, qop, pl, col_len,
+                                 mask_from);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        st[b].tick();
+    if (i + 1 < n) {
+        consume_tile<F, EXT, CB, NB>(st, B, t_begin + (i + 1) * kTile, t_end, lane, kscale, qop, pl,
+                                     col_len, mask_from);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+            st[b].tick();
+    }
+}
+
 // Inverse V rotation of one output row held as channels (2 lane, 2 lane + 1) by the
 // 64 lanes of a wave: width 1 in-lane, widths 2.. across lanes.
 template <int BV>
@@ -795,9 +888,8 @@ __device__ __forceinline__ void combine_merge(const DecodeArgs &a, int64_t base,
 
 // Fused decode step: lanes 0-3 encode the new K row of (sequence s, KV head h) and lanes
 // 4-7 its V row, exactly as the write kernel does, into the slot given for it.
-template <int BK>
-__device__ __forceinline__ void write_new_rows(const DecodeArgs &a, int s, int h,
-                                               int lane)
+template <int BK, typename Args>
+__device__ __forceinline__ void write_new_rows(Args &a, int s, int h, int lane)
 {
     const int ql = lane & 3;
     const bool is_v = lane >= 4;
@@ -825,7 +917,7 @@ __device__ __forceinline__ void write_new_rows(const DecodeArgs &a, int s, int h
 }
 
 template <int BK, int F, bool EXT, int CB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? 4 : 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? kSplitWavesF2 : 2)))
 void decode_split_kernel(DecodeArgs a)
 {
     static_assert(!EXT || F == 1, "extend columns use the 16-column layout");
@@ -845,10 +937,14 @@ void decode_split_kernel(DecodeArgs a)
         s = blockIdx.x / a.blocks_per_seq;
         const int lb = blockIdx.x - s * a.blocks_per_seq;
         const int q0 = a.qo_start[s], n = a.qo_start[s + 1] - q0;
-        if (lb * a.rows_per_block >= n)
+        // qo_start is device data the host cannot check: a block whose rows fall outside
+        // [0, total_q) does nothing, and a block is cut at total_q, so q, out and the
+        // partials are only ever addressed inside their rows
+        if (q0 < 0 || lb * a.rows_per_block >= n || q0 + lb * a.rows_per_block >= a.num_rows)
             return;
-        const int nrows = min(a.rows_per_block, n - lb * a.rows_per_block);
         row0 = q0 + lb * a.rows_per_block;
+        const int nrows = min(min(a.rows_per_block, n - lb * a.rows_per_block),
+                              a.num_rows - (int)row0);
         pos0 = min(a.seq_lens[s], a.max_seq_len) - n + lb * a.rows_per_block;
         L = pos0 + nrows;
         ncols = nrows * G;
@@ -1059,45 +1155,9 @@ void decode_split_kernel(DecodeArgs a)
     __syncthreads();   // qop is complete
     asm volatile("" ::"v"(touch));   // the touch loads have landed by now
 
-    // ---- a7: page walk, one tile ahead of the math --------------------------------------
-    ParLds &pl = lds_par[wave];
-    LaneAddr la;
-    la.init<CB>(lane);
-    // the range in chunks of at most 1024 tokens: starting 32-aligned, a chunk spans at most
-    // 64 pages of 16 tokens, whose ids one register holds
-    for (int cb = t_begin; cb < t_end; cb += 1024) {
-        const int ce = min(t_end, cb + 1024);
-        // two register tiles, each refilled with the tile two ahead right after it is
-        // consumed (at most 128 VGPRs, so four waves share a SIMD).  The loads are
-        // unconditional (a prefetch past the end re-reads the last tile, an L2 hit), so the
-        // same loads are in flight at every point of the loop and the wait before a tile
-        // covers only that tile's loads.
-        const int t_last = cb + (ce - 1 - cb) / kTile * kTile;
-        if (cb != t_begin)
-            pid.fill(a, ptab, cb >> a.page_log2, lane);
-        Tile<CB> A, B;
-        load_tile<CB, !EXT>(A, a, pid, h, cb, ce, la);
-        load_tile<CB, !EXT>(B, a, pid, h, min(cb + kTile, t_last), ce, la);
-        int t0 = cb;
-        while (true) {
-            consume_tile<F, EXT, CB, NB>(st, A, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                st[b].tick();
-            if (t0 + kTile >= ce)
-                break;
-            load_tile<CB, !EXT>(A, a, pid, h, min(t0 + 2 * kTile, t_last), ce, la);
-            t0 += kTile;
-            consume_tile<F, EXT, CB, NB>(st, B, t0, ce, lane, kscale, qop, pl, col_len, mask_from);
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-                st[b].tick();
-            if (t0 + kTile >= ce)
-                break;
-            load_tile<CB, !EXT>(B, a, pid, h, min(t0 + 2 * kTile, t_last), ce, la);
-            t0 += kTile;
-        }
-    }
+    // ---- a7..a9: the page walk
+    walk_tiles<F, EXT, CB, NB, !EXT>(st, a, pid, ptab, h, t_begin, t_end, lane, kscale, qop,
+                                     lds_par[wave], col_len, mask_from);
 
     // ---- the waves' (and, for F = 2, the two halves') partial states of this split, one
     // block of 16 columns at a time through the same LDS.  The output rows are written here
@@ -1256,6 +1316,548 @@ void decode_split_kernel(DecodeArgs a)
     }
 }
 
+// ---- the balanced decode ------------------------------------------------------------------
+// One resident round of workgroups in NG groups of Hkv, one workgroup per KV head of a group.
+// Group j takes the tile columns [T j / NG, T (j + 1) / NG) of the (sequence, 32-token tile)
+// space in that order (T tile columns in all), and its workgroup h walks them for KV head h.
+// Every workgroup streams the same number of bytes, so none waits for a long sequence at the
+// end (a grid of per-split workgroups in several rounds leaves the chip part idle while its
+// last round drains: ~8% of the Qwen3-32B-like decode), and the Hkv workgroups of a group read
+// the Hkv row blocks of the same pages at the same time, from one XCD (their launch indices
+// differ by NG, a multiple of the 8 XCDs): the pages stay a contiguous read for the memory,
+// and the parameter lines that neighbouring heads share are fetched once.
+// A workgroup walks its share as segments, one sequence each: a segment that holds all tiles
+// of its (sequence, KV head) pair writes the output itself; otherwise it leaves a partial at
+// slot (j + s) Hkv + h (a pair's partials sit Hkv slots apart, and the slots of different
+// pairs never overlap), merged either by the last of the pair's workgroups to finish (elected
+// by a counter) or, when pairs span many groups, by a combine launch.
+
+// Largest share index whose share starts at or before tile x (shares start at floor(w T / N)).
+__device__ __forceinline__ int share_of(int64_t x, int64_t T, int N)
+{
+    int w = (int)(x * N / T);
+    while (w + 1 < N && (int64_t)(w + 1) * T / N <= x)
+        ++w;
+    return w;
+}
+
+// Merge of one pair's n partials (slots slot0 + k stride, k < n) for query head g of its
+// group: one wave, lane l with channels 2 l, 2 l + 1; device-scope loads (other workgroups of
+// the launch wrote the partials).  o0, o1: the normalised output, still in the rotated basis.
+__device__ __forceinline__ void merge_slots(const float *part_o, const float *part_ml, int64_t G,
+                                            int64_t slot0, int64_t stride, int n, int g, int lane,
+                                            float &o0, float &o1)
+{
+    auto row = [&](int k) { return (slot0 + k * stride) * G + g; };
+    float M = -INFINITY;
+    for (int k = lane; k < n; k += 64)
+        M = fmaxf(M, load_pair<true>(part_ml + 2 * row(k)).x);
+    M = col_max(row16_max(M));
+    float lsum = 0.0f;
+    for (int k = lane; k < n; k += 64) {
+        const float2 ml = load_pair<true>(part_ml + 2 * row(k));
+        lsum += __builtin_amdgcn_exp2f(ml.x - M) * ml.y;
+    }
+    lsum = col_sum(row16_sum(lsum));
+    o0 = 0.0f;
+    o1 = 0.0f;
+    int k = 0;
+    for (; k + 4 <= n; k += 4) {
+        float2 ml[4], v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ml[j] = load_pair<true>(part_ml + 2 * row(k + j));
+            v[j] = load_pair<true>(part_o + row(k + j) * kHeadDim + 2 * lane);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float wj = __builtin_amdgcn_exp2f(ml[j].x - M);
+            o0 = fmaf(wj, v[j].x, o0);
+            o1 = fmaf(wj, v[j].y, o1);
+        }
+    }
+    for (; k < n; ++k) {
+        const float2 ml = load_pair<true>(part_ml + 2 * row(k));
+        const float2 v = load_pair<true>(part_o + row(k) * kHeadDim + 2 * lane);
+        const float wj = __builtin_amdgcn_exp2f(ml.x - M);
+        o0 = fmaf(wj, v.x, o0);
+        o1 = fmaf(wj, v.y, o1);
+    }
+    const float inv_l = 1.0f / lsum;
+    o0 *= inv_l;
+    o1 *= inv_l;
+}
+
+// The kernel arguments seen through the kernarg segment, re-read where they are used: the
+// balanced decode loops over segments, and arguments kept in registers from one segment's
+// prologue to the next would stay live through the tile loop and spill.
+typedef __attribute__((address_space(4))) const DecodeArgs KArgs;
+
+__device__ __forceinline__ KArgs &kargs()
+{
+    KArgs *p = (KArgs *)(__builtin_amdgcn_kernarg_segment_ptr());
+    asm volatile("" : "+s"(p));
+    return *p;
+}
+
+// Tiles per sequence, prefix-summed into tiles[0..kBalancedMaxSeqs] (tiles[s] = tiles of the
+// sequences before s; entries from num_seqs on hold the total).  Called by all NT threads of
+// a workgroup (each a run of kBalancedMaxSeqs / NT sequences); wsum holds NT / 64 ints; ends
+// with a barrier.
+template <int NT>
+__device__ __forceinline__ void tile_prefix(int *tiles, int *wsum, int tid, int lane, int wave)
+{
+    KArgs &k = kargs();
+    const int S = k.num_seqs;
+    constexpr int kPer = kBalancedMaxSeqs / NT;
+    int loc[kPer];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int s = tid * kPer + j;
+        int n = 0;
+        if (s < S) {
+            const int L = min(k.seq_lens[s], k.max_seq_len);
+            n = L > 0 ? (L + kTile - 1) / kTile : 0;
+        }
+        loc[j] = n;
+        sum += n;
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off)
+            incl += y;
+    }
+    if (lane == 63)
+        wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int i = 0; i < wave; ++i)
+        run += wsum[i];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        tiles[tid * kPer + j] = run;
+        run += loc[j];
+    }
+    if (tid == NT - 1)
+        tiles[kBalancedMaxSeqs] = run;
+    __syncthreads();
+}
+
+template <int BK, int F, int CB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(F == 2 ? kBalancedWavesF2 : 2)))
+void decode_balanced_kernel(DecodeArgs a)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    constexpr int kSlots = F == 2 ? 8 : 16;
+    __shared__ float lds_o[kDecodeWaves][kSlots][kHeadDim + 4];
+    __shared__ QOperand<F> qop[1];
+    __shared__ ParLds lds_par[kDecodeWaves];
+    __shared__ float lds_m[kDecodeWaves][kSlots];
+    __shared__ float lds_l[kDecodeWaves][kSlots];
+    __shared__ float lds_qsum[kMaxGroup];
+    __shared__ float lds_amax[kDecodeWaves];
+    __shared__ int lds_tiles[kBalancedMaxSeqs + 1];   // tiles of the sequences before s
+    __shared__ int lds_wsum[kDecodeWaves];
+    __shared__ int lds_last;
+    // the current segment (sequence, first tile, end tile), reloaded after the tile loop so
+    // that none of it stays in registers while the tiles stream
+    __shared__ int lds_seg[3];
+    __shared__ int lds_next;   // first tile column of the next segment
+
+    tile_prefix<64 * kDecodeWaves>(lds_tiles, lds_wsum, tid, lane, wave);
+    // empty sequences get zero rows (they hold no tiles)
+    for (int s = blockIdx.x; s < kargs().num_seqs; s += gridDim.x) {
+        KArgs &k = kargs();
+        if (min(k.seq_lens[s], k.max_seq_len) <= 0) {
+            float4 *o = reinterpret_cast<float4 *>(k.out + (int64_t)s * k.num_q_heads * kHeadDim);
+            for (int i = tid; i < k.num_q_heads * kHeadDim / 4; i += blockDim.x)
+                o[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+    // this workgroup: KV head h of group j; fewer tile columns than groups: one each
+    const int NG = gridDim.x / kargs().num_kv_heads;
+    const int h = blockIdx.x / NG;
+    const int j = blockIdx.x - h * NG;
+    {
+        const int T = lds_tiles[kargs().num_seqs];
+        const int N = min(NG, T);
+        if (j >= N)
+            return;
+        if (tid == 0)
+            lds_next = (int)((int64_t)j * T / N);
+    }
+    const int n16 = lane & 15;
+    const int kq = lane >> 4;
+    const int gl = F == 2 ? (n16 & 7) : n16;   // this lane's column (query head)
+    const int seg = lane & 15;                 // prologue: channels [8 seg, 8 seg + 8)
+    ParLds &pl = lds_par[wave];
+    while (true) {
+        // ---- the next segment: from tile column g to the end of its sequence or the share
+        __syncthreads();   // lds_next and lds_seg are written, the last segment is done
+        {
+            const int S = kargs().num_seqs;
+            const int T = lds_tiles[S];
+            const int N = min(NG, T);
+            const int g1 = (int)((int64_t)(j + 1) * T / N);
+            const int g = lds_next;
+            if (g >= g1)
+                break;
+            // the sequence holding column g: P[s] <= g < P[s + 1]
+            int s = 0, hi = S;
+            while (hi - s > 1) {
+                const int mid = (s + hi) >> 1;
+                if (lds_tiles[mid] <= g)
+                    s = mid;
+                else
+                    hi = mid;
+            }
+            const int seg_end = min(g1, lds_tiles[s + 1]);
+            __syncthreads();   // every thread has read lds_next
+            if (tid == 0) {
+                lds_seg[0] = s;
+                lds_seg[1] = g - lds_tiles[s];
+                lds_seg[2] = seg_end - lds_tiles[s];
+                lds_next = seg_end;
+            }
+            __syncthreads();
+        }
+        const int s = __builtin_amdgcn_readfirstlane(lds_seg[0]);
+        const int t0 = __builtin_amdgcn_readfirstlane(lds_seg[1]);
+        const int t1 = __builtin_amdgcn_readfirstlane(lds_seg[2]);
+        KArgs &k = kargs();
+        const int G = k.group;
+        const int L = min(k.seq_lens[s], k.max_seq_len);
+        // fused decode step: the segment holding position L - 1 writes that token's rows
+        // first; the prologue's barriers order those stores before every tile load of this
+        // workgroup, and no other workgroup reads that position
+        if (k.new_slots != nullptr && wave == 1 && lane < 8 && (L - 1) / kTile >= t0 &&
+            (L - 1) / kTile < t1)
+            write_new_rows<BK>(k, s, h, lane);
+        // the waves share the segment's tiles evenly
+        const int n_tiles = t1 - t0;
+        const int seg_tok0 = t0 * kTile, seg_tok1 = min(L, t1 * kTile);
+        const int t_begin = seg_tok0 + (wave * n_tiles / kDecodeWaves) * kTile;
+        const int t_end = min(seg_tok1, seg_tok0 + ((wave + 1) * n_tiles / kDecodeWaves) * kTile);
+        const int32_t *ptab = a.page_table + (int64_t)s * a.max_pages;
+        PageIds pid;
+        if (t_begin < t_end)
+            pid.fill(a, ptab, t_begin >> a.page_log2, lane);
+
+        // ---- a6: the query rows of (s, h): rotate, scale, round to one grid, cut into digits
+        float x[8];
+        float amax = 0.0f;
+        {
+            const int gq = wave * 4 + (lane >> 4);
+            if (gq < G) {
+                const int64_t qrow = (int64_t)s * k.num_q_heads + h * G + gq;
+                const u32x4 wq = *reinterpret_cast<const u32x4 *>(k.q + qrow * kHeadDim + 8 * seg);
+                const uint32_t d[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    x[2 * m] = __uint_as_float(d[m] << 16);
+                    x[2 * m + 1] = __uint_as_float(d[m] & 0xFFFF0000u);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    x[i] = 0.0f;
+            }
+            rotate_query_row<BK>(x, seg);
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] *= k.q_scale;
+                amax = fmaxf(amax, fabsf(x[i]));
+                sum += x[i];
+            }
+            sum = row16_sum(sum);
+            if (seg == 0 && gq < kMaxGroup)
+                lds_qsum[gq] = sum;
+        }
+        amax = col_max(row16_max(amax));
+        if (lane == 0)
+            lds_amax[wave] = amax;
+        {
+            constexpr int kWords = (int)(sizeof(QOperand<F>) / 16);
+            i32x4 *z = reinterpret_cast<i32x4 *>(&qop[0]);
+            for (int i = tid; i < kWords; i += 64 * kDecodeWaves)
+                z[i] = i32x4{0, 0, 0, 0};
+        }
+        __syncthreads();
+        amax = fmaxf(fmaxf(lds_amax[0], lds_amax[1]), fmaxf(lds_amax[2], lds_amax[3]));
+        int e = 0;
+        if (amax > 0.0f)
+            frexpf(amax, &e);
+        const float grid = ldexpf(1.0f, 20 - e);
+        {
+            const int gq = wave * 4 + (lane >> 4);
+            if (gq < G) {
+                uint32_t u[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    u[i] = __float_as_uint(__builtin_fmaf(x[i], grid, 0x1.8p23f)) +
+                           (0x808080u - 0x4B400000u);
+                const int ln = gq + 16 * (seg >> 2);
+#pragma unroll
+                for (int par = 0; par < 2; ++par) {
+#pragma unroll
+                    for (int dg = 0; dg < 3; ++dg) {
+                        const uint32_t k = 2 - dg;
+                        const uint32_t lo = __builtin_amdgcn_perm(u[par + 2], u[par], 0x0C0C0400u + k * 0x101u);
+                        const uint32_t hi = __builtin_amdgcn_perm(u[par + 6], u[par + 4], 0x0C0C0400u + k * 0x101u);
+                        const int32_t word = (int32_t)((lo | (hi << 16)) ^ 0x80808080u);
+                        if constexpr (F == 2) {
+                            reinterpret_cast<int32_t *>(&qop[0].v[par][dg][ln])[seg & 3] = word;
+                            reinterpret_cast<int32_t *>(&qop[0].v[2 + par][dg][ln + 8])[seg & 3] = word;
+                        } else {
+                            reinterpret_cast<int32_t *>(&qop[0].v[par][dg][ln])[seg & 3] = word;
+                        }
+                    }
+                }
+            }
+        }
+        WaveState st[1];
+        const int col_len[1] = {0};
+        const float kscale = lane < 32 ? ldexpf(1.0f, e - 20) : 1.0f;
+        st[0].m = kNoScore;
+        st[0].l = 0.0f;
+        st[0].z = 0.0f;
+        st[0].wsum = 0.0f;
+        st[0].E = 64;
+        st[0].slim = 0x1p-58f;
+        st[0].wpend = 0.0f;
+        st[0].nt = 0;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            st[0].acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        __syncthreads();   // qop and lds_qsum are complete
+        st[0].qsum = lds_qsum[gl];
+
+        // ---- a7..a9: the page walk
+        walk_tiles<F, false, CB, 1, true>(st, a, pid, ptab, h, t_begin, t_end, lane, kscale, qop, pl,
+                                          col_len, 0);
+
+        // ---- the waves' (and for F = 2 the two halves') states of this segment
+        WaveState &sb = st[0];
+        KArgs &ke = kargs();
+        const int eG = ke.group;
+        const int Hkv = ke.num_kv_heads;
+        const int es = __builtin_amdgcn_readfirstlane(lds_seg[0]);
+        const int e_t0 = __builtin_amdgcn_readfirstlane(lds_seg[1]);
+        const int e_t1 = __builtin_amdgcn_readfirstlane(lds_seg[2]);
+        const int ent = lds_tiles[es + 1] - lds_tiles[es];
+        sb.recentre();
+        sb.l = col_sum(sb.l);
+        sb.z = col_sum(sb.z);
+        sb.wsum = col_sum(sb.wsum);
+        float o[8][4];
+        {
+            const float u_even = ldexpf(16.0f, -sb.E), u_odd = ldexpf(64.0f, -sb.E);
+            const float zero = fmaf(8.0f, ldexpf(sb.wsum, -sb.E), sb.z);
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[c][r] = fmaf(sb.acc[c][r], (c & 1) ? u_odd : u_even, zero);
+        }
+        float m_w = sb.m, l_w = sb.l;
+        if constexpr (F == 2) {
+            const float m_o = dpp_row_ror8(sb.m);
+            const float M = fmaxf(sb.m, m_o);
+            const float fa = __builtin_amdgcn_exp2f(sb.m - M), fb = __builtin_amdgcn_exp2f(m_o - M);
+            l_w = sb.l * fa + dpp_row_ror8(sb.l) * fb;
+            m_w = M;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    o[c][r] = o[c][r] * fa + dpp_row_ror8(o[c][r]) * fb;
+        }
+        if (n16 < kSlots && gl < eG) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    lds_o[wave][n16][32 * kq + 8 * r + c] = o[c][r];
+            if (kq == 0) {
+                lds_m[wave][n16] = m_w;
+                lds_l[wave][n16] = l_w;
+            }
+        }
+        __syncthreads();
+        if (e_t0 == 0 && e_t1 == ent) {
+            // the pair's only segment: merge the waves, normalise, undo the V rotation, write
+            for (int gc = wave; gc < eG; gc += kDecodeWaves) {
+                float M = lds_m[0][gc];
+#pragma unroll
+                for (int wv = 1; wv < kDecodeWaves; ++wv)
+                    M = fmaxf(M, lds_m[wv][gc]);
+                float o0 = 0.0f, o1 = 0.0f, lsum = 0.0f;
+#pragma unroll
+                for (int wv = 0; wv < kDecodeWaves; ++wv) {
+                    const float f = __builtin_amdgcn_exp2f(lds_m[wv][gc] - M);
+                    o0 += f * lds_o[wv][gc][2 * lane];
+                    o1 += f * lds_o[wv][gc][2 * lane + 1];
+                    lsum += f * lds_l[wv][gc];
+                }
+                const float inv_l = 1.0f / lsum;
+                o0 *= inv_l;
+                o1 *= inv_l;
+                inverse_rotate_pair_rt(o0, o1, lane, ke.v_block);
+                const int64_t qrow = (int64_t)es * ke.num_q_heads + h * eG + gc;
+                *reinterpret_cast<float2 *>(ke.out + qrow * kHeadDim + 2 * lane) = make_float2(o0, o1);
+            }
+            continue;
+        }
+        // a partial of the pair: device-scope stores (past this XCD's L2), so the workgroup
+        // or the launch that merges reads them from any XCD
+        const int64_t slot = (int64_t)(j + es) * Hkv + h;
+        for (int i = tid; i < eG * kHeadDim; i += 64 * kDecodeWaves) {
+            const int gc = i >> 7, d = i & (kHeadDim - 1);
+            float M = lds_m[0][gc];
+#pragma unroll
+            for (int wv = 1; wv < kDecodeWaves; ++wv)
+                M = fmaxf(M, lds_m[wv][gc]);
+            float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+            for (int wv = 0; wv < kDecodeWaves; ++wv) {
+                const float f = __builtin_amdgcn_exp2f(lds_m[wv][gc] - M);
+                acc += f * lds_o[wv][gc][d];
+                lsum += f * lds_l[wv][gc];
+            }
+            const int64_t row = slot * eG + gc;
+            __hip_atomic_store(ke.part_o + row * kHeadDim + d, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == 0) {
+                __hip_atomic_store(ke.part_ml + 2 * row, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(ke.part_ml + 2 * row + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        if (ke.balanced_combine)
+            continue;   // a combine launch merges the partials
+        // Count this workgroup in once its partial stores have completed.  The ordering rests
+        // on the hardware: the stores above are agent-scope (sc1) stores, which complete at
+        // the device's coherence point, and s_waitcnt(0) waits until every one of this
+        // thread's stores has been acknowledged; the barrier then makes every thread's stores
+        // complete before thread 0 issues the counter update.  The workgroup that sees the
+        // count reach n reads the partials with agent-scope loads, which bypass its own
+        // XCD's L2 and fetch from that same point.  (A device-scope release fence would also
+        // order them, but on this chip it writes back and invalidates the whole L2 of the
+        // XCD, the other workgroups' tiles included.)
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        const int64_t pair = (int64_t)es * Hkv + h;
+        const int T = lds_tiles[ke.num_seqs];
+        const int N = min(NG, T);
+        const int j_lo = share_of(lds_tiles[es], T, N);
+        const int j_hi = share_of(lds_tiles[es + 1] - 1, T, N);
+        if (tid == 0)
+            lds_last = __hip_atomic_fetch_add(ke.counters + pair, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) == j_hi - j_lo;
+        __syncthreads();
+        if (lds_last) {
+            if (tid == 0)
+                __hip_atomic_store(ke.counters + pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int gc = wave; gc < eG; gc += kDecodeWaves) {
+                float o0, o1;
+                merge_slots(ke.part_o, ke.part_ml, eG, (int64_t)(j_lo + es) * Hkv + h, Hkv,
+                            j_hi - j_lo + 1, gc, lane, o0, o1);
+                inverse_rotate_pair_rt(o0, o1, lane, ke.v_block);
+                const int64_t qrow = (int64_t)es * ke.num_q_heads + h * eG + gc;
+                *reinterpret_cast<float2 *>(ke.out + qrow * kHeadDim + 2 * lane) = make_float2(o0, o1);
+            }
+        }
+    }
+}
+
+// ---- a10 for the balanced decode when pairs span many groups: one 1024-thread workgroup per
+// (sequence, query head) merges the pair's partials, 32 of them at a time (thread = partial
+// residue of 32, four channels), and undoes the V rotation.  Pairs of one segment were
+// written by the split launch and are skipped.
+template <int BV>
+__global__ __launch_bounds__(1024) void decode_balanced_combine_kernel(DecodeArgs a)
+{
+    const int s = blockIdx.x;
+    const int gq = blockIdx.y;            // query head
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int G = a.group;
+    const int Hkv = a.num_kv_heads;
+    const int h = gq / G, g = gq - h * G;
+    __shared__ int lds_tiles[kBalancedMaxSeqs + 1];
+    __shared__ int lds_wsum[16];
+    __shared__ float red[32];
+    __shared__ float part[32][kHeadDim];
+    tile_prefix<1024>(lds_tiles, lds_wsum, tid, tid & 63, wave);
+    const int T = lds_tiles[a.num_seqs];
+    const int nt = lds_tiles[s + 1] - lds_tiles[s];
+    if (nt == 0)
+        return;
+    const int NG = a.balanced_wgs / Hkv;
+    const int N = min(NG, T);
+    const int j_lo = share_of(lds_tiles[s], T, N);
+    const int j_hi = share_of(lds_tiles[s + 1] - 1, T, N);
+    const int n = j_hi - j_lo + 1;
+    if (n == 1)
+        return;
+    auto row = [&](int k) { return ((int64_t)(j_lo + k + s) * Hkv + h) * G + g; };
+    float M = -INFINITY;
+    for (int k = tid; k < n; k += 1024)
+        M = fmaxf(M, a.part_ml[2 * row(k)]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        M = fmaxf(M, wave_xor(M, o));
+    if ((tid & 63) == 0)
+        red[wave] = M;
+    __syncthreads();
+    M = red[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w)
+        M = fmaxf(M, red[w]);
+    float l = 0.0f;
+    for (int k = tid; k < n; k += 1024)
+        l += __builtin_amdgcn_exp2f(a.part_ml[2 * row(k)] - M) * a.part_ml[2 * row(k) + 1];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        l += wave_xor(l, o);
+    if ((tid & 63) == 0)
+        red[16 + wave] = l;
+    const int sub = tid >> 5, dq = tid & 31;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int k = sub; k < n; k += 32) {
+        const float wk = __builtin_amdgcn_exp2f(a.part_ml[2 * row(k)] - M);
+        acc += wk * *reinterpret_cast<const f32x4 *>(a.part_o + row(k) * kHeadDim + 4 * dq);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        part[sub][4 * dq + c] = acc[c];
+    __syncthreads();
+    if (tid >= 64)
+        return;
+    l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w)
+        l += red[16 + w];
+    const float inv_l = 1.0f / l;
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+        o0 += part[k][2 * tid];
+        o1 += part[k][2 * tid + 1];
+    }
+    o0 *= inv_l;
+    o1 *= inv_l;
+    inverse_rotate_pair<BV>(o0, o1, tid);
+    *reinterpret_cast<float2 *>(a.out + ((int64_t)s * a.num_q_heads + gq) * kHeadDim + 2 * tid) =
+        make_float2(o0, o1);
+}
+
 // Tokens attended by output row r of the combine: the sequence length (decode) or the
 // causal length of query row r (extend: the sequence holding r by binary search over
 // qo_start, then its position + 1).
@@ -1272,7 +1874,9 @@ __device__ __forceinline__ int row_length(const DecodeArgs &a, int r)
             hi = mid;
     }
     const int n = a.qo_start[lo + 1] - a.qo_start[lo];
-    return min(a.seq_lens[lo], a.max_seq_len) - n + (r - a.qo_start[lo]) + 1;
+    // at most max_seq_len even for a qo_start that breaks its preconditions, so a row never
+    // counts more splits than the workspace holds
+    return min(min(a.seq_lens[lo], a.max_seq_len) - n + (r - a.qo_start[lo]) + 1, a.max_seq_len);
 }
 
 // ---- a10: combine the splits of one (sequence, query head), undo the V rotation ---------
@@ -1400,12 +2004,12 @@ void launch_f1_widths(const DecodeArgs &a, const dim3 &grid, hipStream_t s)
     }
 }
 
-// The decode's split grid fits on the device at once (four workgroups per CU; two for the
-// 16-column kernel).
+// The decode's split grid fits on the device at once (kSplitWavesF2 workgroups per CU; two
+// for the 16-column kernel).
 bool one_round(const DecodeArgs &a)
 {
     const int64_t wgs = (int64_t)a.max_splits * a.num_kv_heads * a.num_seqs;
-    return wgs <= (int64_t)device_cus() * (a.group > 8 ? 2 : 4);
+    return wgs <= (int64_t)device_cus() * (a.group > 8 ? 2 : kSplitWavesF2);
 }
 
 template <int BK>
@@ -1443,6 +2047,29 @@ hipError_t launch_split(const DecodeArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int BK, int F>
+void launch_balanced_widths(const DecodeArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)a.balanced_wgs), block(64 * kDecodeWaves);
+    const int cb = (a.k_bits == 2 ? 1 : 0) | (a.v_bits == 2 ? 2 : 0);
+    switch (cb) {
+    case 1: hipLaunchKernelGGL((decode_balanced_kernel<BK, F, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_balanced_kernel<BK, F, 2>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_balanced_kernel<BK, F, 3>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_balanced_kernel<BK, F, 0>), grid, block, 0, s, a); break;
+    }
+}
+
+template <int BK>
+hipError_t launch_balanced(const DecodeArgs &a, hipStream_t s)
+{
+    if (a.group > 8)
+        launch_balanced_widths<BK, 1>(a, s);
+    else
+        launch_balanced_widths<BK, 2>(a, s);
+    return hipGetLastError();
+}
+
 template <int BV>
 hipError_t launch_combine(const DecodeArgs &a, hipStream_t s)
 {
@@ -1458,11 +2085,39 @@ hipError_t launch_combine(const DecodeArgs &a, hipStream_t s)
 
 }  // namespace
 
+int decode_resident_wgs(int group)
+{
+    return device_cus() * (group > 8 ? 2 : kBalancedWavesF2);
+}
+
 int launch_decode(int k_block, int v_block, const DecodeArgs &args, void *stream)
 {
     if (args.num_seqs == 0 || args.num_rows == 0)
         return 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (args.balanced_wgs > 0) {
+        hipError_t e;
+        switch (k_block) {
+        case 0: e = launch_balanced<0>(args, s); break;
+        case 16: e = launch_balanced<16>(args, s); break;
+        case 32: e = launch_balanced<32>(args, s); break;
+        case 64: e = launch_balanced<64>(args, s); break;
+        case 128: e = launch_balanced<128>(args, s); break;
+        default: return hipErrorInvalidValue;
+        }
+        if (e != hipSuccess || !args.balanced_combine)
+            return e;
+        const dim3 grid((unsigned)args.num_seqs, (unsigned)args.num_q_heads);
+        switch (v_block) {
+        case 0: hipLaunchKernelGGL(decode_balanced_combine_kernel<0>, grid, dim3(1024), 0, s, args); break;
+        case 16: hipLaunchKernelGGL(decode_balanced_combine_kernel<16>, grid, dim3(1024), 0, s, args); break;
+        case 32: hipLaunchKernelGGL(decode_balanced_combine_kernel<32>, grid, dim3(1024), 0, s, args); break;
+        case 64: hipLaunchKernelGGL(decode_balanced_combine_kernel<64>, grid, dim3(1024), 0, s, args); break;
+        case 128: hipLaunchKernelGGL(decode_balanced_combine_kernel<128>, grid, dim3(1024), 0, s, args); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     // The in-kernel combine pays where launch latency dominates: a grid resident in one
     // round, of at most kInKernelCombineSplits splits per row (the Qwen3-4B-like decode
     // 19.4 -> 18.4 us, the small-batch fused step 21.3 -> 17.6 us).  Otherwise the combine

@@ -24,6 +24,18 @@ constexpr int kExtendBlocks = 2;    // extend: 16-column blocks per wave (query 
 constexpr int kSplitCounters = 16384;
 constexpr size_t kCounterBytes = size_t(kSplitCounters) * 4;
 constexpr int kInKernelCombineSplits = 16;   // most splits per row merged inside the split launch
+// the balanced decode keeps the tiles per sequence (prefix sums) in LDS: at most this many
+// sequences
+constexpr int kBalancedMaxSeqs = 1024;
+// most workgroups of the balanced decode (its workspace is sized for this many)
+constexpr int kBalancedMaxWgs = 2048;
+// waves per SIMD (workgroups per CU) of the balanced decode with up to eight query heads per
+// KV head: two, so that its segment loop fits the register file without spilling (~180
+// VGPRs; the split kernel measured the same at two, three and four)
+constexpr int kBalancedWavesF2 = 2;
+// waves per SIMD of the split decode with up to eight query heads per KV head (its tile walk,
+// the page-id window and the epilogue take ~140 VGPRs)
+constexpr int kSplitWavesF2 = 3;
 
 struct WriteArgs {
     const uint16_t *k;          // bf16 bits
@@ -60,6 +72,8 @@ struct CopyArgs {
 struct DecodePlan {
     int32_t split_tokens;       // tokens per workgroup, multiple of kTile * kDecodeWaves
     int32_t max_splits;         // ceil(max_seq_len / split_tokens), >= 1
+    int32_t balanced_wgs = 0;   // > 0: the balanced decode with this many workgroups (at
+                                // most kBalancedMaxWgs; the split plan is then unused)
 };
 
 struct DecodeArgs {
@@ -89,6 +103,14 @@ struct DecodeArgs {
     int32_t max_splits;
     // decode grid order: 0 = (split, KV head, sequence), 1 = (sequence, KV head, split)
     int32_t seq_major = 0;
+    // > 0: the balanced decode, one resident round of this many workgroups (NG groups of
+    // Hkv, group j's share of the (sequence, tile) columns read by one workgroup per KV
+    // head); its partials are indexed by slot = (j + sequence) * Hkv + KV head,
+    // [slot][G][128] and [slot][G][2]
+    int32_t balanced_wgs = 0;
+    // balanced decode: 1 = a combine launch merges the pairs of several shares (pairs span
+    // many groups), 0 = the last workgroup of each pair merges it
+    int32_t balanced_combine = 0;
     float q_scale;              // sm_scale * log2(e)
     // extend (chunked prefill) only; qo_start == nullptr for the decode.  The output
     // rows are then query rows: q, out [total_q][Hq][128], part_* [total_q][Hq][splits]
@@ -121,6 +143,9 @@ int launch_bf16_paged_write(const CopyArgs &a, void *stream);
 int launch_device_copy(void *dst, const void *src, size_t bytes, void *stream);
 // decode, or extend when a.qo_start is set
 int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream);
+// workgroups of one resident round of the balanced decode (kBalancedWavesF2 per CU; two for
+// more than eight query heads per KV head)
+int decode_resident_wgs(int group);
 const char *hip_error_string(int err);
 // compute units of the current device (read once per process; 256 if the query fails)
 int device_cus();

@@ -116,15 +116,27 @@ def test_decode_validation(K):
     small = size.value
     ws(_desc(K), split=128)
     assert size.value > small
-    # the automatic split keeps at most 64 splits (one wave combines them): a 1M-token
-    # sequence takes 16,384-token splits; 64 KiB of split counters, then partials of
-    # 128 + 2 floats per (row, head, split)
+    # a 1M-token sequence (enough work for several rounds of split workgroups) takes the
+    # balanced decode: 64 KiB of split counters, then partials of 128 + 2 floats per query
+    # head of a KV head and slot, with 2048 + S * Hkv slots (a workgroup's share starts and
+    # ends at most one partial per pair)
     counters = 16384 * 4
     assert ws(_desc(K), S=1, maxlen=1 << 20) == K.KVRQ_OK
-    assert size.value == counters + 1 * 64 * 64 * (128 + 2) * 4
+    assert size.value == counters + (2048 + 1 * 8) * 8 * (128 + 2) * 4
     # a forced split size is kept as given
     assert ws(_desc(K), S=1, maxlen=1 << 20, split=4096) == K.KVRQ_OK
     assert size.value == counters + 1 * 64 * 256 * (128 + 2) * 4
+    # the balanced grid on request, for any shape that fits it (at most 1024 sequences);
+    # below 2^22 tokens of work the automatic plan keeps split workgroups
+    assert ws(_desc(K), S=4, maxlen=1000, split=K.KVRQ_SPLIT_BALANCED) == K.KVRQ_OK
+    assert size.value == counters + (2048 + 4 * 8) * 8 * (128 + 2) * 4
+    assert ws(_desc(K), S=1025, maxlen=1000, split=K.KVRQ_SPLIT_BALANCED) == K.KVRQ_EUNSUPPORTED
+    assert ws(_desc(K), S=1025, maxlen=1000) == K.KVRQ_OK
+    assert ws(_desc(K), split=-2) == K.KVRQ_EINVAL
+    # the extend has no balanced grid
+    assert L.kv_int4_paged_extend_workspace(ctypes.byref(_desc(K)), 1, 64, 16, 16, 64,
+                                            K.KVRQ_SPLIT_BALANCED, ctypes.byref(size)) == \
+        K.KVRQ_EUNSUPPORTED
 
     def dec(desc=None, q=0x1000, S=2, Hq=64, tab=0x2000, maxp=400, lens=0x3000, maxlen=5000,
             scale=0.0, split=0, out=0x4000, wsp=0x5000, wsb=1 << 30):

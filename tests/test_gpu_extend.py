@@ -150,3 +150,33 @@ def test_one_workspace_for_decode_and_extend(K):
         torch.cuda.synchronize()
         assert int(ws[:16384 * 4].count_nonzero()) == 0, f"counters left set after the {step}"
         decode_compare(out.cpu().numpy(), ref, f"shared workspace: {step}")
+
+
+@pytest.mark.parametrize("split", [0, 128])
+def test_bad_qo_start_stays_inside_its_buffers(K, split):
+    """qo_start is device data the host cannot check.  Entries beyond total_q, a decreasing
+    pair and a negative start give unspecified rows but no access outside q, out or the
+    workspace: both buffers sit inside guard bands that must come back untouched."""
+    import torch
+    lens, news = [300, 200, 150, 90], [20, 20, 20, 20]
+    Hkv, G = 2, 4
+    Hq = Hkv * G
+    cache, orc, q, qo, tab, L = _build(K, lens, news, Hkv, Hq, 16, 64, 0, seed=77)
+    total_q = int(qo[-1])
+    guard = 4096
+    for bad in ([0, 50, 30, 500, total_q], [-8, 10, 70, 75, total_q], [0, 79, 79, 79, 80]):
+        bad = np.array(bad, np.int32)
+        n_out = total_q * Hq * D
+        big = torch.full((n_out + 2 * guard,), 12345.0, dtype=torch.float32, device="cuda")
+        out = big[guard:guard + n_out].view(total_q, Hq, D)
+        n_ws = K.kv_int4_paged_extend_workspace(cache, len(lens), Hq, total_q, 40, int(L.max()), split)
+        ws_big = torch.full((max(n_ws, 16) + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+        ws = ws_big[guard:guard + max(n_ws, 16)]
+        ws.zero_()
+        K.kv_int4_paged_extend(cache, bf16_dev(q), to_dev(bad), to_dev(tab), to_dev(L), int(L.max()), 40,
+                               out=out, split_tokens=split, workspace=ws)
+        torch.cuda.synchronize()
+        b = big.cpu().numpy()
+        assert np.all(b[:guard] == 12345.0) and np.all(b[guard + n_out:] == 12345.0), bad
+        w = ws_big.cpu().numpy()
+        assert np.all(w[:guard] == 0x5A) and np.all(w[guard + max(n_ws, 16):] == 0x5A), bad
