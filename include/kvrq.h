@@ -252,6 +252,26 @@ KVRQ_API kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_c
                                  int32_t split_tokens, float *out, void *workspace,
                                  size_t workspace_bytes, void *stream);
 
+/* kv_int4_paged_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The split counters and partials live in the library's own static device
+ * array of 32 MiB per GPU (kept until the process ends); the call allocates and frees
+ * nothing.  A decode whose workspace (kv_int4_paged_decode_workspace with the same
+ * arguments) exceeds 32 MiB is rejected with KVRQ_EWORKSPACE before any HIP call; the
+ * Qwen3-32B-like shape (256 sequences, 64 query and 8 KV heads) needs ~17 MiB.  The first
+ * call on a device looks the array up and clears its counters with a small kernel on
+ * `stream`; every call leaves them zero.  All calls on one GPU share the array: calls that
+ * may overlap in time on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  Arguments, results and launches are those of
+ * kv_int4_paged_decode. */
+KVRQ_API kvrq_status kv_int4_paged_decode_noalloc(const kvrq_cache_desc *d,
+                                                  const kvrq_cache_buffers *b, const void *q,
+                                                  int32_t num_seqs, int32_t num_q_heads,
+                                                  const int32_t *page_table,
+                                                  int32_t max_pages_per_seq, const int32_t *seq_lens,
+                                                  int32_t max_seq_len, float sm_scale,
+                                                  int32_t split_tokens, float *out, void *stream);
+
 /* Fused decode step: write each sequence's new token and decode over it, in
  * one pass of the decode's split kernel (plus its combine).  For the
  * small-batch, latency-bound regime the pages serve next to the

@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         "kv_int4_paged_decode_workspace": (st, [P, i32, i32, i32, i32, P]),
         "kv_int4_paged_decode": (st, [P, P, P, i32, i32, P, i32, P, i32, ctypes.c_float, i32, P, P,
                                       sz, P]),
+        "kv_int4_paged_decode_noalloc": (st, [P, P, P, i32, i32, P, i32, P, i32, ctypes.c_float,
+                                              i32, P, P]),
         "kv_int4_paged_decode_step": (st, [P, P, P, P, i64, i64, P, P, i32, i32, P, i32, P, i32,
                                            ctypes.c_float, i32, P, P, sz, P]),
         "kv_int4_paged_extend_workspace": (st, [P, i32, i32, i32, i32, i32, i32, P]),
@@ -208,6 +210,27 @@ def kv_int4_paged_decode(cache: PagedInt4Cache, q, page_table, seq_lens, max_seq
         ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(q), S, Hq, _ptr(page_table),
         int(page_table.shape[1]), _ptr(seq_lens), int(max_seq_len), float(sm_scale), int(split_tokens),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def kv_int4_paged_decode_noalloc(cache: PagedInt4Cache, q, page_table, seq_lens, max_seq_len: int,
+                                 out, sm_scale: float = 0.0, split_tokens: int = 0, stream=None):
+    """kv_int4_paged_decode with the library's static per-GPU scratch instead of a workspace:
+    writes fp32 ``out`` [S][Hq][128] (caller-allocated) and allocates nothing."""
+    import torch
+    S, Hq, D = q.shape
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or D != HEAD_DIM:
+        raise ValueError("q must be contiguous bf16 [S][Hq][128]")
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.shape[0] != S:
+        raise ValueError("page_table must be contiguous int32 [S][max_pages]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (S,):
+        raise ValueError("seq_lens must be int32 [S]")
+    if out.dtype != torch.float32 or tuple(out.shape) != (S, Hq, D) or not out.is_contiguous():
+        raise ValueError("out must be contiguous fp32 [S][Hq][128]")
+    _check(lib().kv_int4_paged_decode_noalloc(
+        ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(q), S, Hq, _ptr(page_table),
+        int(page_table.shape[1]), _ptr(seq_lens), int(max_seq_len), float(sm_scale),
+        int(split_tokens), _ptr(out), _stream(stream)))
     return out
 
 

@@ -30,6 +30,7 @@ HIP_COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fvisibil
 SOURCES = [
     ("kvrq_write.hip", ["-ffp-contract=off"]),
     ("kvrq_decode.hip", []),
+    ("kvrq_noalloc.hip", []),
 ]
 
 

@@ -538,7 +538,7 @@ kvrq_status decode_impl(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, c
                         int32_t max_pages_per_seq, const int32_t *seq_lens, int32_t max_seq_len,
                         float sm_scale, int32_t split_tokens, float *out, void *workspace,
                         size_t workspace_bytes, void *stream, const StepRows *step,
-                        const char *what)
+                        const char *what, bool static_scratch = false)
 {
     kvrq_status st = check_decode_shape(d, num_seqs, num_q_heads, max_seq_len, split_tokens);
     if (st)
@@ -565,6 +565,24 @@ kvrq_status decode_impl(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, c
         return fail(KVRQ_EINVAL, "sm_scale must be finite");
     const kvrq::DecodePlan plan = plan_decode(num_seqs, d->num_kv_heads, max_seq_len, split_tokens);
     const size_t need = decode_workspace_bytes(num_seqs, num_q_heads, plan, d->num_kv_heads);
+    if (static_scratch) {
+        // the library's own per-device scratch: the last check before the first HIP call
+        if (need > kvrq::kNoallocScratchBytes)
+            return fail(KVRQ_EWORKSPACE, "%s: this decode needs %zu bytes of scratch, the static "
+                        "scratch holds %zu (fewer sequences, query heads or splits, or "
+                        "kv_int4_paged_decode with a workspace)", what, need,
+                        kvrq::kNoallocScratchBytes);
+        if (plan.balanced_wgs == 0 && plan.max_splits > 65535 * 64)
+            return fail(KVRQ_EUNSUPPORTED, "too many splits");
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (need > 0) {
+            st = hip_status(kvrq::noalloc_scratch(&workspace, stream), what);
+            if (st)
+                return st;
+            workspace_bytes = kvrq::kNoallocScratchBytes;
+        }
+    }
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(KVRQ_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                     workspace ? workspace_bytes : size_t(0));
@@ -651,6 +669,19 @@ kvrq_status kv_int4_paged_decode(const kvrq_cache_desc *d, const kvrq_cache_buff
     return decode_impl(d, b, q, num_seqs, num_q_heads, page_table, max_pages_per_seq, seq_lens,
                        max_seq_len, sm_scale, split_tokens, out, workspace, workspace_bytes, stream,
                        nullptr, "kv_int4_paged_decode");
+}
+
+KVRQ_API kvrq_status kv_int4_paged_decode_noalloc(const kvrq_cache_desc *d,
+                                                  const kvrq_cache_buffers *b, const void *q,
+                                                  int32_t num_seqs, int32_t num_q_heads,
+                                                  const int32_t *page_table,
+                                                  int32_t max_pages_per_seq, const int32_t *seq_lens,
+                                                  int32_t max_seq_len, float sm_scale,
+                                                  int32_t split_tokens, float *out, void *stream)
+{
+    return decode_impl(d, b, q, num_seqs, num_q_heads, page_table, max_pages_per_seq, seq_lens,
+                       max_seq_len, sm_scale, split_tokens, out, nullptr, 0, stream, nullptr,
+                       "kv_int4_paged_decode_noalloc", true);
 }
 
 KVRQ_API kvrq_status kv_int4_paged_decode_step(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,

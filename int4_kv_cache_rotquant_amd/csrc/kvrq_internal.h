@@ -137,6 +137,9 @@ struct DecodeArgs {
     int32_t v_bits = 4;
 };
 
+// bytes of the static decode scratch behind kv_int4_paged_decode_noalloc (per device)
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+
 // Returns a hipError_t value (0 = success).
 int launch_rotquant_write(int k_block, int v_block, const WriteArgs &a, void *stream);
 int launch_bf16_paged_write(const CopyArgs &a, void *stream);
@@ -147,6 +150,9 @@ int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream);
 // more than eight query heads per KV head)
 int decode_resident_wgs(int group);
 const char *hip_error_string(int err);
+// device address of the static decode scratch on the current device (looked up, and its
+// counters cleared on `stream`, on the first call for that device)
+int noalloc_scratch(void **ptr, void *stream);
 // compute units of the current device (read once per process; 256 if the query fails)
 int device_cus();
 
