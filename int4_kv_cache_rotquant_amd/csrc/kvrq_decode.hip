@@ -189,11 +189,12 @@ constexpr uint32_t kMant47 = 0x00F000F0u;   // mantissa bits 4..7 of both halves
 // Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
 
-// Cache policy of the tile loads: the default.  A plain streaming read runs faster with
-// non-temporal loads on MI355X (7.0 against 6.3 TB/s), but the decode's page walk measured
-// slower with them (the Qwen3-32B-like decode 641 -> 657 us, the 1M-token one 223 -> 242 us),
-// and the extend, which re-reads a sequence's tiles from the L2, much slower.
-constexpr int kTileLoadAux = 0;
+// Cache policy of the decode's code loads: non-temporal ("nt"): the cache is read once per
+// decode, and a streaming read runs at 7.0 TB/s with nt loads on MI355X against 6.3 with the
+// default policy.  With two tiles really in flight per wave (walk_tiles) the Qwen3-32B-like
+// decode went 610 -> 569 us.  (The extend keeps default-policy loads: its row blocks re-read
+// a sequence's tiles from the L2.)
+constexpr int kTileLoadAux = 2;
 
 // K codes become int8 MFMA operands: the even and the odd nibbles of a dword, masked in
 // place, are four bytes each.  Scores are integer dot products of codes with the query

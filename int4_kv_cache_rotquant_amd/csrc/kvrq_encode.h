@@ -85,11 +85,25 @@ __device__ __forceinline__ void rotate_row(float (&x)[32], int ql)
     }
 }
 
+// Stores of the encoded rows: non-temporal (NT) for the write kernel, whose output is not
+// read back by it (measured on MI355X: the 32k-token chunk write 37.7 -> 35.6 us, and the
+// 1M-token decode that follows 64 such writes 234 -> 205 us, since the fill no longer leaves
+// the Infinity Cache full of dirty lines); plain for the fused decode step, whose workgroup
+// reads its rows back.
+template <bool NT, typename T>
+__device__ __forceinline__ void store_row(T *p, const T &v)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
 // Rotate, quantise and store one row held in x; called by all four lanes of the quad.
 // 4 bits: 15 levels, two codes per byte, 64-byte rows; 2 bits: 3 levels, four codes per
 // byte (channel d at bit 2 (d % 4) of byte d / 4), 32-byte rows.  BITS fixes the width at
-// compile time (4 or 2); BITS = 0 takes it from `bits` at run time.
-template <int B, int BITS = 4>
+// compile time (4 or 2); BITS = 0 takes it from `bits` at run time.  NT: non-temporal stores.
+template <int B, int BITS = 4, bool NT = false>
 __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t *__restrict__ codes,
                                            uint32_t *__restrict__ params, int64_t num_slots,
                                            int num_kv_heads, int page_log2, int h, int ql,
@@ -152,9 +166,9 @@ __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t
         }
         if (store) {
             u32x2 *dst = reinterpret_cast<u32x2 *>(codes + cell * (kRowCodeBytes / 2)) + ql;
-            *dst = u32x2{out[0], out[1]};
+            store_row<NT>(dst, u32x2{out[0], out[1]});
             if (ql == 0)
-                params[cell] = s_bits | (z_bits << 16);
+                store_row<NT>(params + cell, s_bits | (z_bits << 16));
         }
         return;
     }
@@ -185,9 +199,9 @@ __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t
     }
     if (store) {
         u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + ql;
-        *dst = u32x4{out[0], out[1], out[2], out[3]};
+        store_row<NT>(dst, u32x4{out[0], out[1], out[2], out[3]});
         if (ql == 0)
-            params[cell] = s_bits | (z_bits << 16);
+            store_row<NT>(params + cell, s_bits | (z_bits << 16));
     }
 }
 

@@ -97,7 +97,7 @@ void rotquant_write_kernel(WriteArgs a)
             bf16x8_to_f32(RK.raw[j], x + 8 * j);
         int32_t slot = RK.valid ? RK.slot : -1;
         issue(RK, a.k, a.k_stride, pf);
-        encode_row<BK, KBITS>(x, slot, a.k_codes, a.k_params, a.num_slots, a.num_kv_heads,
+        encode_row<BK, KBITS, true>(x, slot, a.k_codes, a.k_params, a.num_slots, a.num_kv_heads,
                               a.page_log2, h, ql);
 
 #pragma unroll
@@ -105,7 +105,7 @@ void rotquant_write_kernel(WriteArgs a)
             bf16x8_to_f32(RV.raw[j], x + 8 * j);
         slot = RV.valid ? RV.slot : -1;
         issue(RV, a.v, a.v_stride, pf);
-        encode_row<BV, VBITS>(x, slot, a.v_codes, a.v_params, a.num_slots, a.num_kv_heads,
+        encode_row<BV, VBITS, true>(x, slot, a.v_codes, a.v_params, a.num_slots, a.num_kv_heads,
                               a.page_log2, h, ql);
         if (!more)
             break;
