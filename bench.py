@@ -718,6 +718,22 @@ def main():
         copy_ms.append(e0.elapsed_time(e1))
     copy_gbps = 2 * copy_bytes / (float(np.median(copy_ms)) * 1e-3) / 1e9
     del src, dst
+    # the measured read ceiling: a 2 GiB non-temporal streaming read (kvrq_device_read, eight
+    # waves per CU), median of five; the decode is a read-only kernel
+    read_bytes = 2 << 30
+    rsrc = torch.ones(read_bytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvrq_device_read(rsrc, sink)
+    read_ms = []
+    for _ in range(5):
+        e0, e1 = HipEvent(torch), HipEvent(torch)
+        e0.record()
+        K.kvrq_device_read(rsrc, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        read_ms.append(e0.elapsed_time(e1))
+    read_gbps = read_bytes / (float(np.median(read_ms)) * 1e-3) / 1e9
+    del rsrc, sink
 
     names = list(s.kernels)
     per_kernel = {}
@@ -754,7 +770,8 @@ def main():
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": None if traffic is None else round(traffic), "traffic_note": traffic_note,
-                    "frac_of_copy_probe": round(achieved / copy_gbps, 4)}
+                    "frac_of_copy_probe": round(achieved / copy_gbps, 4),
+                    "frac_of_read_probe": round(achieved / read_gbps, 4)}
 
     ms_per_step = elapsed / args.steps * 1e3
     value = s.tokens_per_step * args.steps / elapsed
@@ -787,6 +804,7 @@ def main():
         "hbm_gbps_step": round(sum(per_kernel[n]["algorithmic_bytes"] * per_kernel[n]["launches_per_step"]
                                    for n in names) / (ms_per_step * 1e-3) / 1e9, 1),
         "copy_probe_gbps": round(copy_gbps, 1),
+        "read_probe_gbps": round(read_gbps, 1),
         "kernel_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -365,6 +365,12 @@ KVRQ_API kvrq_status kvrq_bf16_paged_write(const kvrq_cache_desc *d, void *k_cac
  * achievable HBM bandwidth and to calibrate byte counters. */
 KVRQ_API kvrq_status kvrq_device_copy(void *dst, const void *src, size_t bytes, void *stream);
 
+/* Streaming read of `bytes` bytes (multiple of 16, src 16-byte aligned): non-temporal
+ * loads, eight waves per CU, nothing written but possibly one word at `sink` (a device
+ * uint32; in practice never).  The ceiling a read-only kernel such as the decode can reach,
+ * measured the same way on the same device. */
+KVRQ_API kvrq_status kvrq_device_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

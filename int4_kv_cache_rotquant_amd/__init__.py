@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     kvrq_bf16_paged_write,
     kvrq_cache_sizes,
     kvrq_device_copy,
+    kvrq_device_read,
     last_error,
     lib,
     status_str,

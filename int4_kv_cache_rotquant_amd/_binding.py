@@ -82,6 +82,7 @@ def lib() -> ctypes.CDLL:
                                       i32, P, P, sz, P]),
         "kvrq_bf16_paged_write": (st, [P, P, P, P, P, i64, i64, i64, P, P]),
         "kvrq_device_copy": (st, [P, P, sz, P]),
+        "kvrq_device_read": (st, [P, sz, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -318,6 +319,11 @@ def kvrq_bf16_paged_write(desc: CacheDesc, k_cache, v_cache, k, v, slot_mapping,
 def kvrq_device_copy(dst, src, nbytes: Optional[int] = None, stream=None) -> None:
     n = nbytes if nbytes is not None else src.numel() * src.element_size()
     _check(lib().kvrq_device_copy(_ptr(dst), _ptr(src), n, _stream(stream)))
+
+
+def kvrq_device_read(src, sink, nbytes: Optional[int] = None, stream=None) -> None:
+    n = nbytes if nbytes is not None else src.numel() * src.element_size()
+    _check(lib().kvrq_device_read(_ptr(src), n, _ptr(sink), _stream(stream)))
 
 
 # --------------------------------------------------------------------- host page pool

@@ -829,6 +829,17 @@ kvrq_status kvrq_bf16_paged_write(const kvrq_cache_desc *d, void *k_cache, void 
     return hip_status(kvrq::launch_bf16_paged_write(a, stream), "kvrq_bf16_paged_write");
 }
 
+kvrq_status kvrq_device_read(const void *src, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (bytes == 0)
+        return KVRQ_OK;
+    if (!src || !sink)
+        return fail(KVRQ_EINVAL, "src and sink must be non-NULL");
+    if (bytes % 16 || !aligned(src, 16) || !aligned(sink, 4))
+        return fail(KVRQ_EINVAL, "bytes must be a multiple of 16, src 16-byte and sink 4-byte aligned");
+    return hip_status(kvrq::launch_device_read(src, bytes, sink, stream), "kvrq_device_read");
+}
+
 kvrq_status kvrq_device_copy(void *dst, const void *src, size_t bytes, void *stream)
 {
     if (bytes == 0)

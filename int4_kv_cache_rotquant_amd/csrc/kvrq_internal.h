@@ -144,6 +144,7 @@ constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
 int launch_rotquant_write(int k_block, int v_block, const WriteArgs &a, void *stream);
 int launch_bf16_paged_write(const CopyArgs &a, void *stream);
 int launch_device_copy(void *dst, const void *src, size_t bytes, void *stream);
+int launch_device_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 // decode, or extend when a.qo_start is set
 int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream);
 // workgroups of one resident round of the balanced decode (kBalancedWavesF2 per CU; two for

@@ -25,6 +25,8 @@
 // disabled for this file (-ffp-contract=off) so no multiply-add is fused.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kvrq_encode.h"
 #include "kvrq_internal.h"
 
@@ -148,6 +150,35 @@ __global__ __launch_bounds__(256) void device_copy_kernel(u32x4 *__restrict__ ds
         dst[i] = src[i];
 }
 
+// Streaming read of n 16-byte elements: grid-stride, four non-temporal loads in flight per
+// lane, every load instruction of the grid covering one contiguous span; the words are
+// folded into one value per lane that is stored only if it equals `magic` (never, for the
+// data it is given), so the loads cannot be dropped and nothing is written.
+__global__ __launch_bounds__(256) void device_read_kernel(const u32x4 *__restrict__ src, int64_t n,
+                                                          uint32_t *sink, uint32_t magic)
+{
+    constexpr int U = 4;
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    int64_t i = 0;
+    for (; (i + U) * nth <= n; i += U) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = __builtin_nontemporal_load(src + (i + u) * nth + tid);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (int64_t e = i * nth + tid; e < n; e += nth) {
+        const u32x4 v = __builtin_nontemporal_load(src + e);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == magic)
+        *sink = acc;
+}
+
 // Persistent grid: enough workgroups for a few resident waves per SIMD, each wave
 // then walks several tiles so its next loads overlap its current arithmetic.
 unsigned write_grid(const WriteArgs &a)
@@ -241,6 +272,20 @@ int launch_device_copy(void *dst, const void *src, size_t bytes, void *stream)
     hipLaunchKernelGGL(device_copy_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<u32x4 *>(dst),
                        static_cast<const u32x4 *>(src), n);
+    return hipGetLastError();
+}
+
+int launch_device_read(const void *src, size_t bytes, uint32_t *sink, void *stream)
+{
+    const int64_t n = (int64_t)(bytes / 16);
+    if (n == 0)
+        return 0;
+    // two 256-lane workgroups per CU (eight waves): the fastest streaming read measured
+    // (7.0 TB/s on 3 GiB, against 6.3 with four and 5.7 with sixteen waves per CU)
+    const int64_t blocks = std::min<int64_t>((int64_t)device_cus() * 2, (n + 255) / 256);
+    hipLaunchKernelGGL(device_read_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src), n, sink,
+                       0x9E3779B9u);
     return hipGetLastError();
 }
 

@@ -210,6 +210,34 @@ def test_high_concurrency_sampled(K):
     torch.cuda.synchronize()
 
 
+def test_high_concurrency_full_step(K):
+    """One whole Qwen3-32B-like decode step: 256 sequences of log-normal lengths (median
+    8192, clip [512, 32768]) plus the step's new token, Hq=64, Hkv=8, page 16 scattered over
+    the ~3 GB pool, K block 128, the automatic (balanced) plan; every sequence and query head
+    checked against the oracle run on the cache bytes the GPU wrote (copied back)."""
+    import torch
+    from gpu_harness import gpu_cache_arrays
+    w = W.qwen3_32b_like_decode()
+    lens = (w.seq_lens + 1).astype(np.int32)
+    S, Hkv, Hq, P = w.num_seqs, 8, 64, 16
+    cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, 128, 0, fill=0)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed + 17)
+    for s in range(S):
+        slots = w.paging.slots(s, 0, int(lens[s]))
+        K.kv_rotquant_write(cache, W.make_rows_torch(gen, int(lens[s]), Hkv, w.k_out, "cuda"),
+                            W.make_rows_torch(gen, int(lens[s]), Hkv, None, "cuda"), to_dev(slots))
+    q = W.f32_to_bf16_bits(w.rng(4).standard_normal((S, Hq, D)).astype(np.float32))
+    tab = w.paging.page_table()
+    log(f"full high-concurrency step: {int(lens.sum())} tokens")
+    out = _run(K, cache, q, tab, lens)
+    arrays = gpu_cache_arrays(cache)
+    del cache
+    torch.cuda.empty_cache()
+    ref = oracle.decode(q, arrays, tab, lens, Hkv, P, 128, 0)
+    decode_compare(out, ref, "hc_full_step")
+
+
 def test_long_context_one_kv_head(K):
     """One 1,048,576-token sequence, Hq=64, Hkv=8, page 64 scattered, K and V rotated with
     block 128, filled by 64 writes of 16384 tokens; KV head 0's eight query heads are
