@@ -544,8 +544,8 @@ def cpu_baseline_steps(args, w, kb, rng, cores, threads):
     each timed rep writes one new token per sampled sequence and decodes the sampled sequences
     over it, as a GPU step does for all of them."""
     import oracle
-    lens = w.seq_lens[:4].astype(np.int64)
-    steps = int(w.notes["steps"])
+    lens = w.seq_lens[:8].astype(np.int64)
+    steps = 4 * int(w.notes["steps"])    # cap on timed reps; the time target normally ends it
     paging = W.assign_pages(rng, [int(L) + steps for L in lens], w.page_size)
     cache = oracle.Cache(paging.num_pages, w.num_kv_heads, w.page_size, k_bits=args.k_bits,
                          v_bits=args.v_bits)
@@ -642,9 +642,10 @@ def parse_counter_dirs(fetch_dir, write_dir, out_json, profiled_args=""):
     print(json.dumps(out, indent=1, sort_keys=True))
 
 
-def traffic_from_counters(path, kernel_symbol, copy_bytes):
-    """HBM bytes per launch of ``kernel_symbol`` from a counters summary, scaled by the plain
-    copy kernel's counter-to-byte factor; None if absent or taken on other kernel sources."""
+def traffic_from_counters(path, kernel_symbols, copy_bytes):
+    """HBM bytes per launch of the first of ``kernel_symbols`` that the counters summary holds,
+    scaled by the plain copy kernel's counter-to-byte factor; None if absent or taken on other
+    kernel sources."""
     if not path or not os.path.exists(path):
         return None, None
     with open(path) as f:
@@ -658,7 +659,11 @@ def traffic_from_counters(path, kernel_symbol, copy_bytes):
                 return v["mean"]
         return None
 
-    f_k, w_k = pick(c["fetch_kib"], kernel_symbol), pick(c["write_kib"], kernel_symbol)
+    f_k = w_k = None
+    for sym in kernel_symbols:
+        f_k, w_k = pick(c["fetch_kib"], sym), pick(c["write_kib"], sym)
+        if f_k is not None:
+            break
     f_c, w_c = pick(c["fetch_kib"], "device_copy_kernel"), pick(c["write_kib"], "device_copy_kernel")
     if None in (f_k, w_k, f_c, w_c):
         return None, "incomplete"
@@ -676,7 +681,7 @@ def main():
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the rotated INT4 KV-cache path shards by KV head or by "
-              "sequence with no exchange, and this build runs on a single MI355X only "
+              "sequence with no exchange, and it is measured on a single MI355X only "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         return 2
 
@@ -752,10 +757,13 @@ def main():
         per_kernel[name]["algorithmic_tflops"] = round(f / (per_kernel[name]["mean_us"] * 1e-6) / 1e12, 1)
     dominant = max(names, key=lambda n: per_kernel[n]["mean_us"] * per_kernel[n]["launches_per_step"])
     dk = per_kernel[dominant]
-    symbol = {"kv_rotquant_write": "rotquant_write_kernel", "kv_int4_paged_decode": "decode_split_kernel",
-              "kv_int4_paged_decode_step": "decode_split_kernel",
-              "kv_int4_paged_extend": "decode_split_kernel",
-              "kvrq_bf16_paged_write": "bf16_paged_write_kernel"}[dominant]
+    # the decode runs either the balanced persistent kernel or the split kernel, whichever
+    # the plan chose for the workload; the counters hold the one that ran
+    decode_kernels = ("decode_balanced_kernel", "decode_split_kernel")
+    symbol = {"kv_rotquant_write": ("rotquant_write_kernel",), "kv_int4_paged_decode": decode_kernels,
+              "kv_int4_paged_decode_step": decode_kernels,
+              "kv_int4_paged_extend": ("decode_split_kernel",),
+              "kvrq_bf16_paged_write": ("bf16_paged_write_kernel",)}[dominant]
     traffic, traffic_note = traffic_from_counters(args.counters, symbol, copy_bytes)
     if dominant in flops:
         # dense attention: QK^T on int8 MFMA (5.0 POP/s), PV on f16 MFMA (2.5 PFLOP/s), half
