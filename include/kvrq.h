@@ -185,7 +185,10 @@ KVRQ_API int32_t kvrq_pool_free_pages(const kvrq_pool *p);
  * For every written row (token t, head h, tensor X) with block b:
  *   y = H_b x in fp32 (butterflies of width 1, 2, ..., b/2, then * fp32(1/sqrt b)),
  *   scale = fp16((max y - min y) / 15), zero = fp16(min y),
- *   code_d = clamp(round_half_even((y_d - zero) / scale), 0, 15)  (0 if scale == 0).
+ *   code_d = clamp(round_half_even((y_d - zero) * fp32(1 / scale)), 0, 15)  (0 if
+ *   scale == 0), with scale and zero the stored fp16 values widened to fp32 and the
+ *   reciprocal rounded to fp32 (not a true division: the two can differ by one code at a
+ *   rounding boundary).
  * One launch on `stream`; rows are independent (no atomics). */
 KVRQ_API kvrq_status kv_rotquant_write(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
                               const void *k, const void *v, int64_t num_tokens,

@@ -19,8 +19,9 @@ constexpr int kWriteWgsPerCu = kWriteWavesPerSimd;
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave
 constexpr int kDecodeWaves = 4;     // waves per decode workgroup, each on its own token range
 constexpr int kExtendBlocks = 2;    // extend: 16-column blocks per wave (query rows x heads)
-// split workspaces start with this many int32 split counters (used by the decode when
-// sequences x KV heads fits them and a row has at most 64 splits); the partials follow
+// split workspaces start with this many int32 split counters (used by the split decode when
+// sequences x KV heads fits them, its grid is resident at once and a row has at most
+// kInKernelCombineSplits splits, and by the balanced decode); the partials follow
 constexpr int kSplitCounters = 16384;
 constexpr size_t kCounterBytes = size_t(kSplitCounters) * 4;
 constexpr int kInKernelCombineSplits = 16;   // most splits per row merged inside the split launch

@@ -293,7 +293,7 @@ def test_single_split_writes_the_output(K, G, vb):
 
 @pytest.mark.parametrize("G", [4, 16])
 def test_in_kernel_combine_reuses_its_workspace(K, G):
-    """Up to 64 splits are merged inside the split launch: the last split of each (sequence,
+    """Up to 16 splits are merged inside the split launch: the last split of each (sequence,
     KV head) to finish, elected by a counter at the head of the workspace, combines the
     partials; a row of one split writes itself and an empty row gets zeros.  Three calls
     share one zero-filled workspace, each with fresh queries: every output matches the
