@@ -102,7 +102,8 @@ __device__ __forceinline__ void store_row(T *p, const T &v)
 // Rotate, quantise and store one row held in x; called by all four lanes of the quad.
 // 4 bits: 15 levels, two codes per byte, 64-byte rows; 2 bits: 3 levels, four codes per
 // byte (channel d at bit 2 (d % 4) of byte d / 4), 32-byte rows.  BITS fixes the width at
-// compile time (4 or 2); BITS = 0 takes it from `bits` at run time.  NT: non-temporal stores.
+// compile time (4 or 2); BITS = 0 takes it from `bits` at run time.  NT: non-temporal code
+// stores (the parameter words are always stored plainly).
 template <int B, int BITS = 4, bool NT = false>
 __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t *__restrict__ codes,
                                            uint32_t *__restrict__ params, int64_t num_slots,
@@ -168,7 +169,7 @@ __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t
             u32x2 *dst = reinterpret_cast<u32x2 *>(codes + cell * (kRowCodeBytes / 2)) + ql;
             store_row<NT>(dst, u32x2{out[0], out[1]});
             if (ql == 0)
-                store_row<NT>(params + cell, s_bits | (z_bits << 16));
+                store_row<false>(params + cell, s_bits | (z_bits << 16));
         }
         return;
     }
@@ -200,8 +201,11 @@ __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t
     if (store) {
         u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + ql;
         store_row<NT>(dst, u32x4{out[0], out[1], out[2], out[3]});
+        // the parameters always as plain stores: a tile's 16 words fill half a 128-byte line
+        // whose other half a neighbouring wave writes, and the L2 merges the two halves
+        // before the line goes to memory (the Qwen3-4B-like write, page 16: -4%)
         if (ql == 0)
-            store_row<NT>(params + cell, s_bits | (z_bits << 16));
+            store_row<false>(params + cell, s_bits | (z_bits << 16));
     }
 }
 

@@ -12,9 +12,12 @@ constexpr int kHeadDim = 128;       // channels per head
 constexpr int kRowCodeBytes = 64;   // packed INT4 bytes per (token, head) row (2-bit: 32)
 constexpr int kTile = 32;           // decode tokens per inner step
 constexpr int kWriteTile = 16;      // write tokens per wave step (four lanes per row)
-constexpr int kWriteWavesPerSimd = 5;  // occupancy target (the kernel fits six)
+// write waves per SIMD: two, each walking twice as many tiles as at five (measured on
+// MI355X: the 32k-token chunk 35.9 -> 34.7 us, the Qwen3-4B-like write 45.3 -> 42.7 us with
+// the temporal parameter stores; one wave per SIMD leaves the rotation exposed)
+constexpr int kWriteWavesPerSimd = 2;
 // persistent write grid: 256-lane workgroups per CU, one wave per SIMD each, so all of them
-// are resident at once (a sixth, waiting for a slot, measured 8% slower on 16k-token chunks)
+// are resident at once (one more, waiting for a slot, measured 8% slower on 16k-token chunks)
 constexpr int kWriteWgsPerCu = kWriteWavesPerSimd;
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave
 constexpr int kDecodeWaves = 4;     // waves per decode workgroup, each on its own token range

@@ -16,7 +16,7 @@
 // consecutive slots of a page.  Waves are persistent: each walks the tile pairs
 // with a stride of the grid's wave count and keeps the next tile's loads in
 // flight while it encodes the current one.  The small per-lane footprint keeps
-// five waves per SIMD resident, enough to cover memory latency with arithmetic.
+// two waves per SIMD resident; each keeps a tile pair in flight while it encodes the last.
 //
 // Bit-exactness: every step runs in IEEE binary32 in a fixed order --
 // butterfly widths 1, 2, 4, ... with (u+w, u-w), then * fp32(1/sqrt b); exact
