@@ -79,6 +79,26 @@ def test_degenerate_and_extreme_rows(K):
         run_write_case(K, k, v, slots, 3, Hkv, P, kb, vb, f"degenerate_{kb}_{vb}")
 
 
+def test_round_half_even_ties(K):
+    """Plain rows whose codes all fall exactly on a half: (y - zero) * (1 / scale) is
+    k + 0.5 for every non-extreme channel (scales 1, 2 and 0.5 are exact in fp16), so each
+    code is decided by the round-half-to-even rule alone (0.5 -> 0, 1.5 -> 2, 2.5 -> 2)."""
+    T, Hkv, P = 4, 1, 4
+    x = np.zeros((T, Hkv, D), np.float32)
+    half = np.arange(D) % 15 + 0.5                 # 0.5, 1.5, ..., 14.5
+    x[0, 0] = half
+    x[0, 0, :2] = [0.0, 15.0]                      # scale 1, zero 0
+    x[1, 0] = half - 8.0
+    x[1, 0, :2] = [-8.0, 7.0]                      # scale 1, zero -8
+    x[2, 0] = 2.0 * half
+    x[2, 0, :2] = [0.0, 30.0]                      # scale 2
+    x[3, 0] = 0.5 * half
+    x[3, 0, :2] = [0.0, 7.5]                       # scale 0.5
+    k = W.f32_to_bf16_bits(x)
+    v = W.f32_to_bf16_bits(x[::-1].copy())
+    run_write_case(K, k, v, np.arange(T, dtype=np.int32), 1, Hkv, P, 0, 0, "ties")
+
+
 def test_strided_input_and_page_sizes(K):
     rng = np.random.default_rng(6)
     T, Hkv = 50, 2
