@@ -94,6 +94,9 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="oracle threads (0: every core of the process's affinity)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the size-matched streaming-read and copy ceilings and print "
+                         "them as one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="(accepted for older scripts: the 1 GiB copy probe always runs)")
     ap.add_argument("--counters", default=None,
@@ -673,6 +676,43 @@ def traffic_from_counters(path, kernel_symbols, copy_bytes):
         {"fetch_factor": fetch_factor, "write_factor": write_factor}
 
 
+# ------------------------------------------------------------------ ceilings
+def measure_ceilings(torch, K, reps=20):
+    """Streaming-read (kvrq_device_read) and plain-copy (kvrq_device_copy) rates at the sizes
+    the kernels move per launch: a short kernel pays its ramp-up and drain, so a 134 MB read
+    is the fair ceiling of a write that reads 134 MB, not a 2 GiB one.  Between runs a 1 GiB
+    read evicts the 256 MB Infinity Cache without leaving dirty lines (a fill would, and their
+    write-back would slow the next run).  A copy below ~256 MB is flattered: its writes stay
+    in the Infinity Cache and reach HBM only after the kernel ends."""
+    big = torch.ones((2 << 30) // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty((1 << 30) // 4, dtype=torch.int32, device="cuda")
+    flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            K.kvrq_device_read(flush, sink)
+            e0, e1 = HipEvent(torch), HipEvent(torch)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)) * 1e-3
+
+    out = {"read": {}, "copy": {}, "reps": reps, "statistic": "median"}
+    for mb in (42.5, 85, 134, 170, 268, 1024, 2048):
+        n = int(mb * 1e6) // 4096 * 4096
+        t = timed(lambda: K.kvrq_device_read(big, sink, nbytes=n))
+        out["read"][f"{mb:g}MB"] = {"us": round(t * 1e6, 2), "gbps": round(n / t / 1e9, 1)}
+    for mb in (42.5, 85, 134, 512):
+        n = int(mb * 1e6) // 4096 * 4096
+        t = timed(lambda: K.kvrq_device_copy(dst, big, nbytes=n))
+        out["copy"][f"{mb:g}MB"] = {"us": round(t * 1e6, 2), "gbps_rw": round(2 * n / t / 1e9, 1)}
+    return out
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse_args()
@@ -690,6 +730,9 @@ def main():
     K.lib()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.ceilings:
+        print(json.dumps(measure_ceilings(torch, K)))
+        return 0
     s = Setup(args, K, torch)
     torch.cuda.synchronize()
 
