@@ -719,11 +719,29 @@ __device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile<CB>
 // last tile re-reads it, an L2 hit): a path into the loop head with one tile in flight would
 // make the compiler wait for both tiles everywhere.  The page-id window moves along with the
 // prefetches, so the pipeline runs through the whole range without draining.
+// The first two tiles of a walk: A at t_begin, B one tile on (or the last tile again).
+template <int CB, bool BUF>
+__device__ __forceinline__ void walk_first_tiles(Tile<CB> &A, Tile<CB> &B, const DecodeArgs &a,
+                                                 PageIds &pid, const int32_t *ptab, int h,
+                                                 int t_begin, int t_end, int lane)
+{
+    const int n = (t_end - t_begin + kTile - 1) / kTile;
+    LaneAddr la;
+    la.init<CB>(lane);
+    const int last = t_begin + (n - 1) * kTile;
+    load_tile<CB, BUF>(A, a, pid, h, t_begin, t_end, la);
+    const int tb = min(t_begin + kTile, last);
+    pid.reach(a, ptab, (min(tb + kTile, t_end) - 1) >> a.page_log2, lane);
+    load_tile<CB, BUF>(B, a, pid, h, tb, t_end, la);
+}
+
+// PRE: the caller has issued the first two tiles into A and B (walk_first_tiles) already.
 template <int F, bool EXT, int CB, int NB, bool BUF>
 __device__ __forceinline__ void walk_tiles(WaveState (&st)[NB], const DecodeArgs &a, PageIds &pid,
                                            const int32_t *ptab, int h, int t_begin, int t_end,
                                            int lane, float kscale, const QOperand<F> *qop,
-                                           ParLds &pl, const int (&col_len)[NB], int mask_from)
+                                           ParLds &pl, const int (&col_len)[NB], int mask_from,
+                                           Tile<CB> &A, Tile<CB> &B, bool pre = false)
 {
     const int n = (t_end - t_begin + kTile - 1) / kTile;
     if (n <= 0)
@@ -733,13 +751,8 @@ __device__ __forceinline__ void walk_tiles(WaveState (&st)[NB], const DecodeArgs
     const int last = t_begin + (n - 1) * kTile;   // start of the last tile
     // the largest page index a tile starting at t reads
     auto top_page = [&](int t) { return (min(t + kTile, t_end) - 1) >> a.page_log2; };
-    Tile<CB> A, B;
-    load_tile<CB, BUF>(A, a, pid, h, t_begin, t_end, la);
-    {
-        const int tb = min(t_begin + kTile, last);
-        pid.reach(a, ptab, top_page(tb), lane);
-        load_tile<CB, BUF>(B, a, pid, h, tb, t_end, la);
-    }
+    if (!pre)
+        walk_first_tiles<CB, BUF>(A, B, a, pid, ptab, h, t_begin, t_end, lane);
     int i = 0;
     for (; i + 2 < n; i += 2) {
         const int ta = t_begin + i * kTile;
@@ -1029,32 +1042,18 @@ void decode_split_kernel(DecodeArgs a)
                 x[b][i] = 0.0f;
         }
     }
-    // With the query rows on their way, touch the wave's first two tiles: one dword of every
-    // 128-byte line of their K and V code blocks (lanes 0..31 K, 32..63 V), so the lines
-    // travel to the L2 while the prologue runs and the tile loads after it find them there.
-    // The value is only waited for after the prologue.  (Decode only: the extend's long
-    // workgroups gain nothing from it.  Not in the workgroup of a fused step that writes the
-    // new token's rows: its reads must all follow those stores.)
-    uint32_t touch = 0;
+    // With the query rows on their way, issue the wave's first two tiles, so that their
+    // loads overlap the query prologue and the walk starts on data already in registers
+    // (a load round trip at kernel start, ~3 us on the Qwen3-4B-like decode, is paid once).
+    // Loads return in order, so the prologue's wait for the query rows does not wait for
+    // the tiles.  (Decode only: the extend's long workgroups gain nothing from it.  Not in
+    // the workgroup of a fused step that writes the new token's rows: its reads must all
+    // follow those stores, which the prologue's barriers order.)
+    Tile<CB> TA, TB;
     const bool writer = a.new_slots != nullptr && split == (L - 1) / a.split_tokens;
-    if (!EXT && !writer && t_begin < t_end) {
-        using CW = CodeWidths<CB>;
-        const int P = 1 << a.page_log2;
-        int pg[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            pg[j] = pid.page(min(t_begin + 16 * j, t_end - 1) >> a.page_log2);
-        const int j = (lane >> 3) & 3;   // half tile: tile j / 2, half j % 2
-        const int tok = min(t_begin + 16 * j, t_end - 1) & ~15;
-        const int page = j == 0 ? pg[0] : j == 1 ? pg[1] : j == 2 ? pg[2] : pg[3];
-        const bool is_k = lane < 32;
-        const int row = is_k ? CW::k_row : CW::v_row;
-        const int lines = 16 * row / 128;   // 128-byte lines of a 16-token block: 8 or 4
-        const uint8_t *blk = (is_k ? a.k_codes : a.v_codes) +
-                             ((uint64_t)((uint32_t)page * (uint32_t)a.num_kv_heads + (uint32_t)h) * P +
-                              (uint32_t)(tok & (P - 1))) * row;
-        touch = *reinterpret_cast<const uint32_t *>(blk + 128 * ((lane & 7) % lines));
-    }
+    const bool pre = !EXT && !writer && t_begin < t_end;
+    if (pre)
+        walk_first_tiles<CB, !EXT>(TA, TB, a, pid, ptab, h, t_begin, t_end, lane);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int g = b * 16 + wave * 4 + (lane >> 4);
@@ -1154,11 +1153,10 @@ void decode_split_kernel(DecodeArgs a)
             st[b].acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     __syncthreads();   // qop is complete
-    asm volatile("" ::"v"(touch));   // the touch loads have landed by now
 
     // ---- a7..a9: the page walk
     walk_tiles<F, EXT, CB, NB, !EXT>(st, a, pid, ptab, h, t_begin, t_end, lane, kscale, qop,
-                                     lds_par[wave], col_len, mask_from);
+                                     lds_par[wave], col_len, mask_from, TA, TB, pre);
 
     // ---- the waves' (and, for F = 2, the two halves') partial states of this split, one
     // block of 16 columns at a time through the same LDS.  The output rows are written here
@@ -1641,8 +1639,9 @@ void decode_balanced_kernel(DecodeArgs a)
         st[0].qsum = lds_qsum[gl];
 
         // ---- a7..a9: the page walk
+        Tile<CB> TA, TB;
         walk_tiles<F, false, CB, 1, true>(st, a, pid, ptab, h, t_begin, t_end, lane, kscale, qop, pl,
-                                          col_len, 0);
+                                          col_len, 0, TA, TB);
 
         // ---- the waves' (and for F = 2 the two halves') states of this segment
         WaveState &sb = st[0];
