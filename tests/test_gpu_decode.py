@@ -3,9 +3,10 @@
 same seeded inputs (the write is bit-exact, checked in test_gpu_write.py).
 
 Covers the tiny case (G=1), the Qwen3-4B-like layer (G=4, 16 ragged sequences, page 16
-scattered), the high-concurrency shape (G=8, 256 log-normal sequences, sampled
-sequences checked), the 1M-token long context (G=8, K and V rotated, one KV head
-checked), split-count sweeps, page-table permutation invariance, GQA group sizes
+scattered), the high-concurrency workload (G=8, 256 log-normal sequences, 100 steps of
+write + decode: steps 1, 50 and 100 checked in full and every step write byte for byte),
+the 1M-token long context (G=8, K and V rotated: the whole fill byte for byte and all 64
+query heads), split-count sweeps, page-table permutation invariance, GQA group sizes
 1..16, page sizes 16..128, every block pair, lengths 0, 1, 15..33 and tail tiles,
 caches of degenerate rows (zero and tiny scales, spiked keys) in decode and extend, the
 in-kernel combine over calls that share one workspace, and the combine launch it falls
@@ -210,67 +211,97 @@ def test_high_concurrency_sampled(K):
     torch.cuda.synchronize()
 
 
-def test_high_concurrency_full_step(K):
-    """One whole Qwen3-32B-like decode step: 256 sequences of log-normal lengths (median
-    8192, clip [512, 32768]) plus the step's new token, Hq=64, Hkv=8, page 16 scattered over
-    the ~3 GB pool, K block 128, the automatic (balanced) plan; every sequence and query head
-    checked against the oracle run on the cache bytes the GPU wrote (copied back)."""
+def test_high_concurrency_100_steps(K):
+    """The Qwen3-32B-like workload over its 100 decode steps: 256 sequences of log-normal
+    lengths (median 8192, clip [512, 32768]) filled on the device, Hq=64, Hkv=8, page 16
+    scattered over the ~3 GB pool, K block 128, the automatic (balanced) plan.  Each step
+    writes one new token per sequence (kv_rotquant_write) and decodes every sequence over
+    it.  Steps 1, 50 and 100 are checked in full against the oracle (every sequence and
+    query head, on the cache bytes the GPU wrote); after the last step the pool must equal
+    the pool after the fill with the oracle's write of all 25,600 step rows applied, byte
+    for byte (so every step write is exact and nothing else in the pool moved)."""
     import torch
-    from gpu_harness import gpu_cache_arrays
+    from gpu_harness import assert_write_ok, compare_write, gpu_cache_arrays
     w = W.qwen3_32b_like_decode()
-    lens = (w.seq_lens + 1).astype(np.int32)
     S, Hkv, Hq, P = w.num_seqs, 8, 64, 16
+    steps = int(w.notes["steps"])
     cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, 128, 0, fill=0)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(w.seed + 17)
     for s in range(S):
-        slots = w.paging.slots(s, 0, int(lens[s]))
-        K.kv_rotquant_write(cache, W.make_rows_torch(gen, int(lens[s]), Hkv, w.k_out, "cuda"),
-                            W.make_rows_torch(gen, int(lens[s]), Hkv, None, "cuda"), to_dev(slots))
+        L = int(w.seq_lens[s])
+        K.kv_rotquant_write(cache, W.make_rows_torch(gen, L, Hkv, w.k_out, "cuda"),
+                            W.make_rows_torch(gen, L, Hkv, None, "cuda"),
+                            to_dev(w.paging.slots(s, 0, L)))
+    base = gpu_cache_arrays(cache)
     q = W.f32_to_bf16_bits(w.rng(4).standard_normal((S, Hq, D)).astype(np.float32))
     tab = w.paging.page_table()
-    log(f"full high-concurrency step: {int(lens.sum())} tokens")
-    out = _run(K, cache, q, tab, lens)
-    arrays = gpu_cache_arrays(cache)
+    ks, vs, sl = [], [], []
+    for i in range(steps):
+        slots = np.array([w.paging.slots(s, int(w.seq_lens[s]) + i, 1)[0] for s in range(S)],
+                         np.int32)
+        k = W.make_rows_torch(gen, S, Hkv, w.k_out, "cuda")
+        v = W.make_rows_torch(gen, S, Hkv, None, "cuda")
+        K.kv_rotquant_write(cache, k, v, to_dev(slots))
+        ks.append(k.view(torch.int16).cpu().numpy().view(np.uint16))
+        vs.append(v.view(torch.int16).cpu().numpy().view(np.uint16))
+        sl.append(slots)
+        lens = (w.seq_lens + i + 1).astype(np.int32)
+        out = _run(K, cache, q, tab, lens)
+        if i + 1 in (1, 50, steps):
+            log(f"step {i + 1}: {int(lens.sum())} tokens")
+            ref = oracle.decode(q, gpu_cache_arrays(cache), tab, lens, Hkv, P, 128, 0)
+            decode_compare(out, ref, f"hc_step_{i + 1}")
+    final = gpu_cache_arrays(cache)
     del cache
     torch.cuda.empty_cache()
-    ref = oracle.decode(q, arrays, tab, lens, Hkv, P, 128, 0)
-    decode_compare(out, ref, "hc_full_step")
+    orc = oracle.Cache(w.paging.num_pages, Hkv, P, fill=0)
+    orc.k_codes[...], orc.v_codes[...], orc.k_params[...], orc.v_params[...] = base
+    del base
+    k_all, v_all, s_all = np.concatenate(ks), np.concatenate(vs), np.concatenate(sl)
+    oracle.write(orc, k_all, v_all, s_all, 128, 0)
+    assert_write_ok(compare_write(final, orc, {"k": k_all, "v": v_all}, s_all, (128, 0)),
+                    "hc_100_step_writes")
 
 
-def test_long_context_one_kv_head(K):
+def test_long_context_full(K):
     """One 1,048,576-token sequence, Hq=64, Hkv=8, page 64 scattered, K and V rotated with
-    block 128, filled by 64 writes of 16384 tokens; KV head 0's eight query heads are
-    checked against the oracle."""
+    block 128 and both with outlier channels: the fill by 64 writes of 16384 tokens is
+    checked byte for byte against the oracle's write of the same rows (all 16.8M rows), and
+    the decode of all 64 query heads against the oracle."""
     import torch
+    from gpu_harness import assert_write_ok, compare_write, gpu_cache_arrays
     w = W.long_context()
     C, L, Hkv, Hq, P = w.notes["chunk"], 1 << 20, 8, 64, 64
     cache = K.PagedInt4Cache(w.paging.num_pages, Hkv, P, 128, 128, fill=0)
-    k0 = np.empty((L, 1, D), np.uint16)
-    v0 = np.empty((L, 1, D), np.uint16)
+    kh = np.empty((L, Hkv, D), np.uint16)
+    vh = np.empty((L, Hkv, D), np.uint16)
+    slots = w.paging.slots(0, 0, L)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(w.seed)
-    one = W.OutlierSpec
     for c in range(L // C):
-        # KV head 0 from the seeded host generator (it is checked), heads 1..7 on the device
-        rng = w.rng(100 + c)
-        k0[c * C:(c + 1) * C] = W.make_rows(rng, C, 1, one(w.k_out.mult[:1]))
-        v0[c * C:(c + 1) * C] = W.make_rows(rng, C, 1, one(w.v_out.mult[:1]))
-        krest = W.make_rows_torch(gen, C, Hkv - 1, one(w.k_out.mult[1:]), "cuda")
-        vrest = W.make_rows_torch(gen, C, Hkv - 1, one(w.v_out.mult[1:]), "cuda")
-        k = torch.cat([bf16_dev(k0[c * C:(c + 1) * C]), krest], dim=1)
-        v = torch.cat([bf16_dev(v0[c * C:(c + 1) * C]), vrest], dim=1)
-        K.kv_rotquant_write(cache, k, v, to_dev(w.paging.slots(0, c * C, C)))
+        k = W.make_rows_torch(gen, C, Hkv, w.k_out, "cuda")
+        v = W.make_rows_torch(gen, C, Hkv, w.v_out, "cuda")
+        K.kv_rotquant_write(cache, k, v, to_dev(slots[c * C:(c + 1) * C]))
+        kh[c * C:(c + 1) * C] = k.view(torch.int16).cpu().numpy().view(np.uint16)
+        vh[c * C:(c + 1) * C] = v.view(torch.int16).cpu().numpy().view(np.uint16)
     q = W.f32_to_bf16_bits(w.rng(3).standard_normal((1, Hq, D)).astype(np.float32))
     tab = w.paging.page_table()
     lens = np.array([L], np.int32)
     out = _run(K, cache, q, tab, lens)
-    log("long context: oracle write of KV head 0")
-    orc = oracle.Cache(w.paging.num_pages, 1, P, fill=0)
-    oracle.write(orc, k0, v0, w.paging.slots(0, 0, L), 128, 128)
-    ref = _ref(orc, q[:, :8].copy(), tab, lens, 1, P, 128, 128)
-    decode_compare(out[:, :8], ref, "long_context_h0")
-    torch.cuda.synchronize()
+    gpu = gpu_cache_arrays(cache)
+    del cache
+    torch.cuda.empty_cache()
+    log("long context: oracle write of all 8 KV heads")
+    orc = oracle.Cache(w.paging.num_pages, Hkv, P, fill=0)
+    oracle.write(orc, kh, vh, slots, 128, 128)
+    assert_write_ok(compare_write(gpu, orc, {"k": kh, "v": vh}, slots, (128, 128)),
+                    "long_context_fill")
+    del kh, vh
+    log("long context: oracle decode of 64 query heads")
+    ref = oracle.decode(q, (orc.k_codes, orc.v_codes, orc.k_params, orc.v_params), tab, lens,
+                        Hkv, P, 128, 128)
+    decode_compare(out, ref, "long_context_full")
 
 
 @pytest.mark.parametrize("G,vb", [(4, 128), (16, 0), (8, 32)])
