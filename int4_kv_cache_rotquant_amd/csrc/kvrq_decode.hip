@@ -712,13 +712,6 @@ __device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile<CB>
     }
 }
 
-// ---- a7..a9: one wave's page walk over the tokens [t_begin, t_end), two register tiles in
-// flight: each is refilled with the tile two ahead right after it is consumed, so the same
-// loads are outstanding at every tile and the wait before a tile covers that tile's loads
-// only.  The loop has one exit and issues both prefetches in every pass (a prefetch past the
-// last tile re-reads it, an L2 hit): a path into the loop head with one tile in flight would
-// make the compiler wait for both tiles everywhere.  The page-id window moves along with the
-// prefetches, so the pipeline runs through the whole range without draining.
 // The first two tiles of a walk: A at t_begin, B one tile on (or the last tile again).
 template <int CB, bool BUF>
 __device__ __forceinline__ void walk_first_tiles(Tile<CB> &A, Tile<CB> &B, const DecodeArgs &a,
@@ -735,7 +728,15 @@ __device__ __forceinline__ void walk_first_tiles(Tile<CB> &A, Tile<CB> &B, const
     load_tile<CB, BUF>(B, a, pid, h, tb, t_end, la);
 }
 
-// PRE: the caller has issued the first two tiles into A and B (walk_first_tiles) already.
+// ---- a7..a9: one wave's page walk over the tokens [t_begin, t_end), two register tiles in
+// flight: each is refilled with the tile two ahead right after it is consumed, so the same
+// loads are outstanding at every tile and the wait before a tile covers that tile's loads
+// only.  The loop has one exit and issues both prefetches in every pass (a prefetch past the
+// last tile re-reads it, an L2 hit): a path into the loop head with one tile in flight would
+// make the compiler wait for both tiles everywhere.  The page-id window moves along with the
+// prefetches, so the pipeline runs through the whole range without draining.
+// pre: the caller has issued the first two tiles into A and B (walk_first_tiles) already;
+// otherwise the walk issues them itself.
 template <int F, bool EXT, int CB, int NB, bool BUF>
 __device__ __forceinline__ void walk_tiles(WaveState (&st)[NB], const DecodeArgs &a, PageIds &pid,
                                            const int32_t *ptab, int h, int t_begin, int t_end,
