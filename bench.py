@@ -94,6 +94,9 @@ def parse_args(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="oracle threads (0: every core of the process's affinity)")
+    ap.add_argument("--bdr-vs-plain", action="store_true",
+                    help="also time the 32k prefill-chunk write with BDR-128 and plain INT4 "
+                         "(always on for the default workload)")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the size-matched streaming-read and copy ceilings and print "
                          "them as one JSON line")
@@ -713,6 +716,35 @@ def measure_ceilings(torch, K, reps=20):
     return out
 
 
+# ------------------------------------------------------------------ BDR against plain INT4
+def measure_bdr_vs_plain(args, torch, K, steps=1000, warmup=1000):
+    """The prefill-chunk workload's write (32768 tokens, 8 KV heads, page 64, permuted pages,
+    four rotating input sets, back-to-back launches as in `--workload prefill_chunk`) with the
+    BDR-128 rotation on K and as plain INT4 (no rotation): the pages' claim is a rotated
+    write as fast as the plain one.  Mean HIP-event time per launch over the timed steps of
+    each, after as many warm-up steps."""
+    out = {"workload": "prefill_chunk", "steps": steps, "warmup": warmup, "statistic": "mean"}
+    for variant in ("bdr", "plain"):
+        va = argparse.Namespace(**dict(vars(args), workload="prefill_chunk", variant=variant,
+                                       k_block=None, k_bits=4, v_bits=4))
+        su = Setup(va, K, torch)
+        evs = [[HipEvent(torch), HipEvent(torch)] for _ in range(steps)]
+        warm = [HipEvent(torch), HipEvent(torch)]
+        for i in range(warmup):
+            su.step(i, warm)
+        for i in range(steps):
+            su.step(i, evs[i])
+        torch.cuda.synchronize()
+        us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+        nbytes = su.kernels["kv_rotquant_write"]
+        out[f"{variant}_k_block"] = su.kb
+        out[f"{variant}_us"] = round(us, 2)
+        out[f"{variant}_hbm_frac"] = round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        del su
+    out["overhead"] = round(out["bdr_us"] / out["plain_us"] - 1.0, 4)
+    return out
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse_args()
@@ -858,6 +890,9 @@ def main():
         "read_probe_gbps": round(read_gbps, 1),
         "kernel_hash": kernel_source_hash(),
     }
+    if args.workload == "qwen3_32b_like_decode" or args.bdr_vs_plain:
+        # the write-side claim, next to the headline decode step
+        result["bdr_vs_plain"] = measure_bdr_vs_plain(args, torch, K)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args)
     print(json.dumps(result))
