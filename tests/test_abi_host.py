@@ -215,6 +215,12 @@ def test_helper_validation(K):
     assert L.kvrq_device_copy(0x1000, 0x2000, 0, None) == K.KVRQ_OK
     assert L.kvrq_device_copy(0x1000, 0x2000, 24, None) == K.KVRQ_EINVAL
     assert L.kvrq_device_copy(0, 0x2000, 32, None) == K.KVRQ_EINVAL
+    assert L.kvrq_device_read(0x1000, 0, 0x2000, None) == K.KVRQ_OK
+    assert L.kvrq_device_read(0x1000, 24, 0x2000, None) == K.KVRQ_EINVAL
+    assert L.kvrq_device_read(0x1008, 32, 0x2000, None) == K.KVRQ_EINVAL
+    assert L.kvrq_device_read(0x1000, 32, 0x2002, None) == K.KVRQ_EINVAL
+    assert L.kvrq_device_read(0, 32, 0x2000, None) == K.KVRQ_EINVAL
+    assert L.kvrq_device_read(0x1000, 32, 0, None) == K.KVRQ_EINVAL
     d = _desc(K)
     assert L.kvrq_bf16_paged_write(ctypes.byref(d), 0, 0x1000, 0x2000, 0x3000, 4, 1024, 1024,
                                    0x4000, None) == K.KVRQ_EINVAL
