@@ -78,7 +78,7 @@ typedef int32_t kvrq_status;
 enum {
     KVRQ_OK = 0,
     KVRQ_EINVAL = 1,        /* null pointer, negative size, bad alignment, bad shape */
-    KVRQ_EUNSUPPORTED = 2,  /* valid request outside what this build implements */
+    KVRQ_EUNSUPPORTED = 2,  /* valid request outside what the library implements */
     KVRQ_ENOPAGES = 3,      /* the page pool cannot satisfy a request */
     KVRQ_EHIP = 4,          /* a HIP launch or runtime error */
     KVRQ_EWORKSPACE = 5     /* workspace too small */
