@@ -99,16 +99,26 @@ __device__ __forceinline__ void store_row(T *p, const T &v)
         *p = v;
 }
 
+// One staged tile of 16 rows (the write kernel's LDS staging): each lane's code piece (16
+// bytes; 8 at 2 bits), and per row the parameter word and the destination cell
+// (0xFFFFFFFF: nothing to store).
+struct StageSlot {
+    u32x4 piece[64];
+    uint32_t par[16];
+    uint32_t cell[16];
+};
+
 // Rotate, quantise and store one row held in x; called by all four lanes of the quad.
 // 4 bits: 15 levels, two codes per byte, 64-byte rows; 2 bits: 3 levels, four codes per
 // byte (channel d at bit 2 (d % 4) of byte d / 4), 32-byte rows.  BITS fixes the width at
 // compile time (4 or 2); BITS = 0 takes it from `bits` at run time.  NT: non-temporal code
-// stores (the parameter words are always stored plainly).
+// stores (the parameter words are always stored plainly).  With `stage`, nothing is stored:
+// the encoded tile goes to that LDS slot, and the caller stores it later.
 template <int B, int BITS = 4, bool NT = false>
 __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t *__restrict__ codes,
                                            uint32_t *__restrict__ params, int64_t num_slots,
                                            int num_kv_heads, int page_log2, int h, int ql,
-                                           int bits = 4)
+                                           int bits = 4, StageSlot *stage = nullptr)
 {
 #pragma clang fp contract(off)
     static_assert(BITS == 4 || BITS == 2 || BITS == 0, "code widths: 4, 2, or run time");
@@ -176,6 +186,15 @@ __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t
                 out[k] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
             }
         }
+        if (stage != nullptr) {
+            const int ln = threadIdx.x & 63;
+            stage->piece[ln] = u32x4{out[0], out[1], 0u, 0u};
+            if (ql == 0) {
+                stage->par[ln >> 2] = s_bits | (z_bits << 16);
+                stage->cell[ln >> 2] = store ? (uint32_t)cell : 0xFFFFFFFFu;
+            }
+            return;
+        }
         if (store) {
             u32x2 *dst = reinterpret_cast<u32x2 *>(codes + cell * (kRowCodeBytes / 2)) + ql;
             store_row<NT>(dst, u32x2{out[0], out[1]});
@@ -203,6 +222,15 @@ __device__ __forceinline__ void encode_row(float (&x)[32], int32_t slot, uint8_t
             }
             out[k] = ev | (od << 4);
         }
+    }
+    if (stage != nullptr) {
+        const int ln = threadIdx.x & 63;
+        stage->piece[ln] = u32x4{out[0], out[1], out[2], out[3]};
+        if (ql == 0) {
+            stage->par[ln >> 2] = s_bits | (z_bits << 16);
+            stage->cell[ln >> 2] = store ? (uint32_t)cell : 0xFFFFFFFFu;
+        }
+        return;
     }
     if (store) {
         u32x4 *dst = reinterpret_cast<u32x4 *>(codes + cell * kRowCodeBytes) + ql;

@@ -19,6 +19,7 @@ constexpr int kWriteWavesPerSimd = 2;
 // persistent write grid: 256-lane workgroups per CU, one wave per SIMD each, so all of them
 // are resident at once (one more, waiting for a slot, measured 8% slower on 16k-token chunks)
 constexpr int kWriteWgsPerCu = kWriteWavesPerSimd;
+constexpr int kWriteStage = 8;      // tile pairs per wave staged in LDS by the staged write
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave
 constexpr int kDecodeWaves = 4;     // waves per decode workgroup, each on its own token range
 constexpr int kExtendBlocks = 2;    // extend: 16-column blocks per wave (query rows x heads)

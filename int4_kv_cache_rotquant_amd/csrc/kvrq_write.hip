@@ -65,7 +65,16 @@ __device__ __forceinline__ void load_row(RowLoad &R, const uint16_t *src_base, i
 // us; four tiles of one head: 35.9 and 46.7 us).  The loop is
 // unrolled over the two tensors, so each half is compiled for its own block size, and
 // K and V work is spread evenly over the waves.
-template <int BK, int BV, int KBITS, int VBITS>
+//
+// STAGED: the encoded tiles of up to kWriteStage pairs per wave wait in LDS (73.7 KB per
+// workgroup, two workgroups per CU: the chip's LDS holds a 32k-token chunk's whole output)
+// and are stored in one burst when the stage is full and at the end.  HBM does not overlap
+// reads and writes, and the stores interleaved with the loads cost more than the same
+// stores in a burst after them (measured on MI355X: the 32k chunk 33.7 -> 32.0 us, the
+// Qwen3-4B-like write 44.1 -> 41.8 us).  A wave with fewer pairs than a full stage stores
+// as it goes: a short write has too little reading left to hide the burst behind (the 16k
+// long-context chunk, four pairs per wave: 19.4 -> 21.3 us staged).
+template <int BK, int BV, int KBITS, int VBITS, bool STAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWriteWavesPerSimd)))
 void rotquant_write_kernel(WriteArgs a)
 {
@@ -88,6 +97,30 @@ void rotquant_write_kernel(WriteArgs a)
         load_row(R, src + h * kHeadDim, stride, a.slots, tt * kWriteTile + row, a.num_tokens, ql);
     };
 
+    // the stage: [wave][K, V][pair]; nothing when not STAGED
+    constexpr int NST = STAGED ? kWriteStage : 1;
+    __shared__ StageSlot stage[STAGED ? 4 : 1][2][NST];
+    int nst = 0;
+    auto flush_one = [&](const StageSlot &S, uint8_t *codes, uint32_t *params, int bits) {
+        const uint32_t cell = S.cell[row];
+        if (cell != 0xFFFFFFFFu) {
+            const u32x4 p = S.piece[lane];
+            if (bits == 4)
+                store_row<true>(reinterpret_cast<u32x4 *>(codes + (uint64_t)cell * kRowCodeBytes) + ql, p);
+            else
+                store_row<true>(reinterpret_cast<u32x2 *>(codes + (uint64_t)cell * (kRowCodeBytes / 2)) + ql,
+                                u32x2{p.x, p.y});
+            if (ql == 0)
+                params[cell] = S.par[row];
+        }
+    };
+    auto flush = [&]() {
+        for (int k = 0; k < nst; ++k) {
+            flush_one(stage[wave][0][k], a.k_codes, a.k_params, KBITS);
+            flush_one(stage[wave][1][k], a.v_codes, a.v_params, VBITS);
+        }
+        nst = 0;
+    };
     // Two register sets, K and V: each is refilled with the next pair's tile as soon as
     // its bf16 input is widened to fp32, so up to two tiles are in flight while one is
     // encoded.
@@ -106,7 +139,7 @@ void rotquant_write_kernel(WriteArgs a)
         int32_t slot = RK.valid ? RK.slot : -1;
         issue(RK, a.k, a.k_stride, pf);
         encode_row<BK, KBITS, true>(x, slot, a.k_codes, a.k_params, a.num_slots, a.num_kv_heads,
-                              a.page_log2, h, ql);
+                                    a.page_log2, h, ql, 4, STAGED ? &stage[wave][0][nst] : nullptr);
 
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -114,11 +147,15 @@ void rotquant_write_kernel(WriteArgs a)
         slot = RV.valid ? RV.slot : -1;
         issue(RV, a.v, a.v_stride, pf);
         encode_row<BV, VBITS, true>(x, slot, a.v_codes, a.v_params, a.num_slots, a.num_kv_heads,
-                              a.page_log2, h, ql);
+                                    a.page_log2, h, ql, 4, STAGED ? &stage[wave][1][nst] : nullptr);
+        if (STAGED && ++nst == NST)
+            flush();
         if (!more)
             break;
         pair = next;
     }
+    if constexpr (STAGED)
+        flush();
 }
 
 // bf16 paged copy: the same slot scatter with no quantisation.
@@ -202,14 +239,19 @@ hipError_t launch_bk_bv(const WriteArgs &a, hipStream_t s)
 {
     // the code widths are template arguments, so each kernel carries one encoder per tensor
     const dim3 grid(write_grid(a));
+    // staged when every wave has a full stage of pairs to encode (4-bit pools)
+    const int64_t pairs = (a.num_tokens + kWriteTile - 1) / kWriteTile * a.num_kv_heads;
+    const bool staged = pairs >= (int64_t)kWriteStage * 4 * grid.x;
     if (a.k_bits == 2 && a.v_bits == 2)
-        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 2, 2>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 2, 2, false>), grid, dim3(256), 0, s, a);
     else if (a.k_bits == 2)
-        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 2, 4>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 2, 4, false>), grid, dim3(256), 0, s, a);
     else if (a.v_bits == 2)
-        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 4, 2>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 4, 2, false>), grid, dim3(256), 0, s, a);
+    else if (staged)
+        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 4, 4, true>), grid, dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 4, 4>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 4, 4, false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
