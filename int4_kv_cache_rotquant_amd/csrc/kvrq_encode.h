@@ -101,7 +101,8 @@ __device__ __forceinline__ void store_row(T *p, const T &v)
 
 // One staged tile of 16 rows (the write kernel's LDS staging): each lane's code piece (16
 // bytes; 8 at 2 bits), and per row the parameter word and the destination cell
-// (0xFFFFFFFF: nothing to store).
+// (0xFFFFFFFF: nothing to store; no real cell has that index, since a pool of 2^32 cells
+// would need 256 GiB for one tensor's 4-bit codes alone).
 struct StageSlot {
     u32x4 piece[64];
     uint32_t par[16];

@@ -70,8 +70,8 @@ __device__ __forceinline__ void load_row(RowLoad &R, const uint16_t *src_base, i
 // workgroup, two workgroups per CU: the chip's LDS holds a 32k-token chunk's whole output)
 // and are stored in one burst when the stage is full and at the end.  HBM does not overlap
 // reads and writes, and the stores interleaved with the loads cost more than the same
-// stores in a burst after them (measured on MI355X: the 32k chunk 33.7 -> 32.0 us, the
-// Qwen3-4B-like write 44.1 -> 41.8 us).  A wave with fewer pairs than a full stage stores
+// stores in a burst after them (measured on MI355X, same box: the 32k chunk 33.8 -> 32.9
+// us, the Qwen3-4B-like write 44.1 -> 41.8 us).  A wave with fewer pairs than a full stage stores
 // as it goes: a short write has too little reading left to hide the burst behind (the 16k
 // long-context chunk, four pairs per wave: 19.4 -> 21.3 us staged).
 template <int BK, int BV, int KBITS, int VBITS, bool STAGED>
