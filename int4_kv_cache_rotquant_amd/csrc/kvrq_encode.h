@@ -7,7 +7,8 @@
 // Bit-exactness: every step runs in IEEE binary32 in a fixed order -- butterfly widths
 // 1, 2, 4, ... with (u+w, u-w), then * fp32(1/sqrt b); exact min/max; correctly rounded
 // (mx-mn)/15 and 1/scale; round-to-nearest-even binary16 parameters; codes from the
-// stored parameters.  No multiply-add is fused here.
+// stored parameters.  The compiler contracts nothing here; the explicit multiply-adds are
+// exact (a product by +-1 in the butterflies) or the correction step of the division.
 #pragma once
 
 #include <hip/hip_runtime.h>
