@@ -97,6 +97,10 @@ def parse_args(argv=None):
     ap.add_argument("--bdr-vs-plain", action="store_true",
                     help="also time the 32k prefill-chunk write with BDR-128 and plain INT4 "
                          "(always on for the default workload)")
+    ap.add_argument("--paged-ceiling", action="store_true",
+                    help="only measure the decode's pages read in the decode's order with no "
+                         "arithmetic (kvrq_paged_read), the decode alone and a streaming read of "
+                         "as many bytes, each after a cache-evicting read; print one JSON line")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the size-matched streaming-read and copy ceilings and print "
                          "them as one JSON line")
@@ -716,6 +720,63 @@ def measure_ceilings(torch, K, reps=20):
     return out
 
 
+# ------------------------------------------------------------------ page-gather ceiling
+def measure_paged_ceiling(s, torch, K, reps=20):
+    """The decode's own pages read in the decode's order (kvrq_paged_read: each sequence's
+    page-table entries in order, whole pages of K and V codes and parameters, nothing
+    computed) against the decode of the same lengths and a streaming read of as many bytes,
+    each timed alone after a 1 GiB read that evicts the Infinity Cache, median of `reps`."""
+    w = s.w
+    if w.name == "long_context":
+        lens = np.array([w.total_tokens], dtype=np.int64)
+        maxlen, lens_dev = int(w.total_tokens), s.lens
+    elif w.name in ("qwen3_32b_like_decode", "small_batch_decode"):
+        lens = w.seq_lens.astype(np.int64) + 1
+        maxlen, lens_dev = s.maxlen, s.step_lens[0]
+    else:
+        raise SystemExit("--paged-ceiling measures the decode workloads (qwen3_32b_like_decode, "
+                         "small_batch_decode, long_context)")
+    P = w.page_size
+    tab = w.paging.page_table()
+    pages = np.concatenate([tab[i, :(int(L) + P - 1) // P] for i, L in enumerate(lens)]).astype(np.int32)
+    pages_dev = s.dev_i32(pages)
+    page_bytes = w.num_kv_heads * P * 136
+    read_bytes = int(len(pages)) * page_bytes
+    dec_bytes = s.decode_bytes(lens, w.num_kv_heads, w.num_q_heads, P)
+    flush = torch.ones((1 << 30) // 4, dtype=torch.int32, device="cuda")
+    big = torch.ones(read_bytes // 4 + 1024, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            K.kvrq_device_read(flush, sink)
+            e0, e1 = HipEvent(torch), HipEvent(torch)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)) * 1e-3
+
+    out = {"workload": w.name, "pages": int(len(pages)), "page_bytes": page_bytes,
+           "read_bytes": read_bytes, "decode_algorithmic_bytes": int(dec_bytes), "reps": reps,
+           "statistic": "median", "paged_read": {}}
+    for wg in (1, 2, 3, 4):
+        t = timed(lambda: K.kvrq_paged_read(s.cache, pages_dev, sink, wgs_per_cu=wg))
+        out["paged_read"][f"{wg}_wgs_per_cu"] = {"us": round(t * 1e6, 2),
+                                                 "gbps": round(read_bytes / t / 1e9, 1)}
+    t = timed(lambda: K.kvrq_device_read(big, sink, nbytes=read_bytes // 16 * 16))
+    out["streaming_read"] = {"us": round(t * 1e6, 2), "gbps": round(read_bytes / t / 1e9, 1)}
+    t = timed(lambda: K.kv_int4_paged_decode(s.cache, s.q, s.tab, lens_dev, maxlen, out=s.out,
+                                             split_tokens=s.args.split_tokens, workspace=s.ws))
+    out["decode"] = {"us": round(t * 1e6, 2), "algorithmic_gbps": round(dec_bytes / t / 1e9, 1)}
+    best = min(v["us"] for v in out["paged_read"].values())
+    out["decode_vs_paged_read"] = round(best / out["decode"]["us"], 4)
+    return out
+
+
 # ------------------------------------------------------------------ BDR against plain INT4
 def measure_bdr_vs_plain(args, torch, K, steps=1000, warmup=1000):
     """The prefill-chunk workload's write (32768 tokens, 8 KV heads, page 64, permuted pages,
@@ -767,6 +828,9 @@ def main():
         return 0
     s = Setup(args, K, torch)
     torch.cuda.synchronize()
+    if args.paged_ceiling:
+        print(json.dumps(measure_paged_ceiling(s, torch, K)))
+        return 0
 
     copy_bytes = 1 << 30
     n_ev = 3

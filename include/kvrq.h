@@ -374,6 +374,21 @@ KVRQ_API kvrq_status kvrq_device_copy(void *dst, const void *src, size_t bytes, 
  * measured the same way on the same device. */
 KVRQ_API kvrq_status kvrq_device_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
+/* Page-gather read: every byte of the cache pages listed in `pages` (device int32
+ * [num_list]; ids outside [0, num_pages) read page 0) -- K codes, V codes and both
+ * parameter pools of all KV heads -- in list order, with non-temporal loads, nothing
+ * computed and nothing written but possibly one word at `sink` (a device uint32; in
+ * practice never).  A decode's page table walked in sequence order gives the decode's
+ * own bytes in the decode's order: the ceiling of a read-only kernel over a
+ * page-scattered cache (the pages are fixed-size and scattered by the allocator;
+ * wispaper.ai blog, section 1), next to kvrq_device_read's ceiling over contiguous
+ * memory.  Reads num_list * num_kv_heads * page_size * 136 bytes.  4-bit pools only,
+ * with num_kv_heads * page_size a multiple of 128 (KVRQ_EUNSUPPORTED otherwise);
+ * wgs_per_cu (1..4) workgroups of four waves per CU.  Asynchronous on `stream`. */
+KVRQ_API kvrq_status kvrq_paged_read(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
+                                     const int32_t *pages, int64_t num_list, int32_t wgs_per_cu,
+                                     uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     kvrq_cache_sizes,
     kvrq_device_copy,
     kvrq_device_read,
+    kvrq_paged_read,
     last_error,
     lib,
     status_str,

@@ -83,6 +83,7 @@ def lib() -> ctypes.CDLL:
         "kvrq_bf16_paged_write": (st, [P, P, P, P, P, i64, i64, i64, P, P]),
         "kvrq_device_copy": (st, [P, P, sz, P]),
         "kvrq_device_read": (st, [P, sz, P, P]),
+        "kvrq_paged_read": (st, [P, P, P, i64, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -324,6 +325,16 @@ def kvrq_device_copy(dst, src, nbytes: Optional[int] = None, stream=None) -> Non
 def kvrq_device_read(src, sink, nbytes: Optional[int] = None, stream=None) -> None:
     n = nbytes if nbytes is not None else src.numel() * src.element_size()
     _check(lib().kvrq_device_read(_ptr(src), n, _ptr(sink), _stream(stream)))
+
+
+def kvrq_paged_read(cache: PagedInt4Cache, pages, sink, wgs_per_cu: int = 2, stream=None) -> None:
+    """Page-gather read of the pages listed in the int32 device tensor ``pages`` (whole pages:
+    K and V codes and parameters of every KV head), in list order; nothing is written."""
+    import torch
+    if pages.dtype != torch.int32 or not pages.is_contiguous():
+        raise ValueError("pages must be a contiguous int32 tensor")
+    _check(lib().kvrq_paged_read(ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(pages),
+                                 int(pages.numel()), wgs_per_cu, _ptr(sink), _stream(stream)))
 
 
 # --------------------------------------------------------------------- host page pool

@@ -840,6 +840,41 @@ kvrq_status kvrq_device_read(const void *src, size_t bytes, uint32_t *sink, void
     return hip_status(kvrq::launch_device_read(src, bytes, sink, stream), "kvrq_device_read");
 }
 
+kvrq_status kvrq_paged_read(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, const int32_t *pages,
+                            int64_t num_list, int32_t wgs_per_cu, uint32_t *sink, void *stream)
+{
+    kvrq_status st = check_desc(d);
+    if (st != KVRQ_OK)
+        return st;
+    if ((st = check_buffers(b)) != KVRQ_OK)
+        return st;
+    if (code_bits(d->k_bits) != 4 || code_bits(d->v_bits) != 4)
+        return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read reads 4-bit pools only");
+    if (((int64_t)d->num_kv_heads * d->page_size) % 128 != 0)
+        return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read needs num_kv_heads * page_size to be a multiple "
+                                       "of 128 (got %d * %d)", d->num_kv_heads, d->page_size);
+    if (num_list < 0)
+        return fail(KVRQ_EINVAL, "num_list must be >= 0");
+    if (wgs_per_cu < 1 || wgs_per_cu > 4)
+        return fail(KVRQ_EINVAL, "wgs_per_cu must be 1..4 (got %d)", wgs_per_cu);
+    if (num_list == 0)
+        return KVRQ_OK;
+    if (!pages || !sink || !aligned(sink, 4))
+        return fail(KVRQ_EINVAL, "pages and a 4-byte aligned sink must be given");
+    kvrq::PagedReadArgs a{};
+    a.k_codes = b->k_codes;
+    a.v_codes = b->v_codes;
+    a.k_params = reinterpret_cast<const uint8_t *>(b->k_params);
+    a.v_params = reinterpret_cast<const uint8_t *>(b->v_params);
+    a.pages = pages;
+    a.num_list = num_list;
+    a.units_per_page = d->num_kv_heads * d->page_size / 128;
+    a.num_pages = d->num_pages;
+    a.sink = sink;
+    a.magic = 0x9E3779B9u;
+    return hip_status(kvrq::launch_paged_read(a, wgs_per_cu, stream), "kvrq_paged_read");
+}
+
 kvrq_status kvrq_device_copy(void *dst, const void *src, size_t bytes, void *stream)
 {
     if (bytes == 0)

@@ -74,6 +74,22 @@ struct CopyArgs {
     int32_t page_log2;
 };
 
+// Page-gather read (a measurement kernel): whole cache pages in list order.  A page is
+// units_per_page units of 17 lines of 1 KiB: 8 lines of K codes, 8 of V codes, and one of
+// parameters (512 bytes of K, 512 of V).
+struct PagedReadArgs {
+    const uint8_t *k_codes;
+    const uint8_t *v_codes;
+    const uint8_t *k_params;
+    const uint8_t *v_params;
+    const int32_t *pages;       // [num_list]; ids outside [0, num_pages) read page 0
+    int64_t num_list;
+    int32_t units_per_page;     // num_kv_heads * page_size / 128
+    int32_t num_pages;
+    uint32_t *sink;
+    uint32_t magic;
+};
+
 struct DecodePlan {
     int32_t split_tokens;       // tokens per workgroup, multiple of kTile * kDecodeWaves
     int32_t max_splits;         // ceil(max_seq_len / split_tokens), >= 1
@@ -150,6 +166,7 @@ int launch_rotquant_write(int k_block, int v_block, const WriteArgs &a, void *st
 int launch_bf16_paged_write(const CopyArgs &a, void *stream);
 int launch_device_copy(void *dst, const void *src, size_t bytes, void *stream);
 int launch_device_read(const void *src, size_t bytes, uint32_t *sink, void *stream);
+int launch_paged_read(const PagedReadArgs &a, int wgs_per_cu, void *stream);
 // decode, or extend when a.qo_start is set
 int launch_decode(int k_block, int v_block, const DecodeArgs &a, void *stream);
 // workgroups of one resident round of the balanced decode (kBalancedWavesF2 per CU; two for

@@ -222,6 +222,97 @@ __global__ __launch_bounds__(256) void device_read_kernel(const u32x4 *__restric
         *sink = acc;
 }
 
+// Page-gather read: the cache pages of a list, whole (K and V codes and parameters of every
+// KV head), in list order, with non-temporal loads; the words are folded as in the streaming
+// read and nothing is written.  These are the decode's bytes in the decode's page order with
+// no arithmetic: the ceiling of a read over a page-scattered cache, next to the streaming
+// read's ceiling over contiguous memory.  Each wave takes a contiguous share of the list's
+// units (17 lines of 1 KiB: 8 of K codes, 8 of V codes, one of parameters, 512 bytes of each
+// tensor) and keeps two units in flight: the next unit is issued before the current one is
+// folded, so the wait before each fold covers that unit only.
+struct ReadUnit {
+    u32x4 v[17];
+};
+
+// Issues the loads of unit q of page index pi (scheduling barriers keep the 17 loads
+// together: without them the compiler interleaves loads and folds and keeps only a few
+// loads in flight).
+__device__ __forceinline__ void issue_unit(ReadUnit &U, const PagedReadArgs &a, int64_t pi, int q,
+                                           int lane)
+{
+    __builtin_amdgcn_sched_barrier(0);
+    int p = a.pages[pi];
+    p = (unsigned)p < (unsigned)a.num_pages ? p : 0;
+    const uint64_t unit = (uint64_t)p * (uint64_t)a.units_per_page + (uint64_t)q;
+    const u32x4 *kc = reinterpret_cast<const u32x4 *>(a.k_codes + unit * 8192u) + lane;
+    const u32x4 *vc = reinterpret_cast<const u32x4 *>(a.v_codes + unit * 8192u) + lane;
+    const u32x4 *pr = reinterpret_cast<const u32x4 *>((lane < 32 ? a.k_params : a.v_params) +
+                                                      unit * 512u) + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        U.v[j] = __builtin_nontemporal_load(kc + 64 * j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        U.v[8 + j] = __builtin_nontemporal_load(vc + 64 * j);
+    U.v[16] = __builtin_nontemporal_load(pr);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Folds a unit into acc where it stands: the empty asm takes acc as an operand, so the
+// compiler cannot sink the folds past the next unit's loads (which would make it copy the
+// unit's registers, and wait for all of its loads, before reusing them).
+__device__ __forceinline__ void fold_unit(uint32_t &acc, const ReadUnit &U)
+{
+#pragma unroll
+    for (int j = 0; j < 17; ++j)
+        acc ^= U.v[j].x ^ U.v[j].y ^ U.v[j].z ^ U.v[j].w;
+    asm("" : "+v"(acc));
+}
+
+__global__ __launch_bounds__(256) void paged_read_kernel(PagedReadArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t W = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n_units = a.num_list * a.units_per_page;
+    const int64_t u0 = n_units * w / W, u1 = n_units * (w + 1) / W;
+    if (u0 >= u1)
+        return;
+    // unit u is unit q = u % units_per_page of page index pi = u / units_per_page; (pi, q)
+    // advance one unit per issue, on the scalar unit
+    const int upp = a.units_per_page;
+    int64_t pi = u0 / upp;
+    int q = (int)(u0 - pi * upp);
+    auto next = [&]() {
+        if (++q == upp) {
+            q = 0;
+            ++pi;
+        }
+    };
+    uint32_t acc = 0;
+    ReadUnit A, B;
+    issue_unit(A, a, pi, q, lane);
+    next();
+    int64_t u = u0;
+    for (; u + 2 < u1; u += 2) {
+        issue_unit(B, a, pi, q, lane);
+        next();
+        fold_unit(acc, A);
+        issue_unit(A, a, pi, q, lane);
+        next();
+        fold_unit(acc, B);
+    }
+    if (u + 1 < u1) {
+        issue_unit(B, a, pi, q, lane);
+        fold_unit(acc, A);
+        fold_unit(acc, B);
+    } else {
+        fold_unit(acc, A);
+    }
+    if (acc == a.magic)
+        *a.sink = acc;
+}
+
 // Persistent grid: enough workgroups for a few resident waves per SIMD, each wave
 // then walks several tiles so its next loads overlap its current arithmetic.
 unsigned write_grid(const WriteArgs &a)
@@ -334,6 +425,15 @@ int launch_device_read(const void *src, size_t bytes, uint32_t *sink, void *stre
     hipLaunchKernelGGL(device_read_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src), n, sink,
                        0x9E3779B9u);
+    return hipGetLastError();
+}
+
+int launch_paged_read(const PagedReadArgs &a, int wgs_per_cu, void *stream)
+{
+    if (a.num_list == 0)
+        return 0;
+    hipLaunchKernelGGL(paged_read_kernel, dim3((unsigned)(device_cus() * wgs_per_cu)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), a);
     return hipGetLastError();
 }
 

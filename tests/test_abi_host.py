@@ -226,6 +226,27 @@ def test_helper_validation(K):
                                    0x4000, None) == K.KVRQ_EINVAL
 
 
+def test_paged_read_validation(K):
+    """kvrq_paged_read checks its arguments on the host before any launch."""
+    L = K.lib()
+    d, b = _desc(K), _bufs(K)
+
+    def call(desc=d, bufs=b, pages=0x7000, n=4, wgs=2, sink=0x8000):
+        return L.kvrq_paged_read(ctypes.byref(desc), ctypes.byref(bufs), pages, n, wgs, sink, None)
+
+    assert call(n=0) == K.KVRQ_OK                       # nothing to read: no launch
+    assert call(n=-1) == K.KVRQ_EINVAL
+    assert call(wgs=0) == K.KVRQ_EINVAL
+    assert call(wgs=5) == K.KVRQ_EINVAL
+    assert call(pages=0) == K.KVRQ_EINVAL
+    assert call(sink=0) == K.KVRQ_EINVAL
+    assert call(sink=0x8002) == K.KVRQ_EINVAL
+    assert call(desc=_desc(K, page_size=8)) == K.KVRQ_EUNSUPPORTED      # 8 heads x 8 tokens
+    assert call(desc=_desc(K, k_bits=2)) == K.KVRQ_EUNSUPPORTED
+    assert call(bufs=K.CacheBuffers(0, 0x1000, 0x2000, 0x3000)) == K.KVRQ_EINVAL
+    assert call(desc=_desc(K, head_dim=64)) == K.KVRQ_EUNSUPPORTED
+
+
 def test_status_strings(K):
     for st, name in [(0, "KVRQ_OK"), (1, "KVRQ_EINVAL"), (2, "KVRQ_EUNSUPPORTED"), (3, "KVRQ_ENOPAGES"),
                      (4, "KVRQ_EHIP"), (5, "KVRQ_EWORKSPACE"), (99, "KVRQ_UNKNOWN")]:
