@@ -1003,9 +1003,10 @@ void decode_split_kernel(DecodeArgs a)
     // the first chunk's page ids are requested before the query prologue, so their latency
     // overlaps it
     const int32_t *ptab = a.page_table + (int64_t)s * a.max_pages;
+    // (page ids and tile addresses are clamped into the table and the pool, so the tile loads
+    // are in bounds for any range, an empty one included)
     PageIds pid;
-    if (t_begin < t_end)
-        pid.fill(a, ptab, t_begin >> a.page_log2, lane);
+    pid.fill(a, ptab, t_begin >> a.page_log2, lane);
 
     // the waves' partial states in the epilogue (F = 2: the two halves of each column are
     // merged inside the wave first, so one slot per query head and wave)
@@ -1024,37 +1025,41 @@ void decode_split_kernel(DecodeArgs a)
     const int seg = lane & 15;   // channels [8 seg, 8 seg + 8)
     float x[NB][8];
     float amax = 0.0f;
+    // The query rows are requested (unconditionally: a lane past the columns reads the
+    // first column's row, which every workgroup has, and zeroes it), then, for the decode, the wave's first two tiles, so
+    // that the tile loads overlap the query prologue, the query rows' latency included, and
+    // the walk starts on data already in registers (a load round trip at kernel start, ~3 us
+    // on the Qwen3-4B-like decode, is paid once).  Loads return in order, so the prologue's
+    // wait for the query rows does not wait for the tiles; a load issued under a branch
+    // would make the compiler wait for every load issued before it where the paths join, so
+    // the tiles are always issued.  (Decode only: the extend's long workgroups gain nothing
+    // from it.  The workgroup of a fused step that writes the new token's rows does not use
+    // them: its reads must all follow those stores, which the prologue's barriers order, so
+    // its walk issues them again.)
+    u32x4 qw[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int g = b * 16 + wave * 4 + (lane >> 4);
-        if (g < ncols) {
-            const int64_t qrow = EXT ? (row0 + g / G) * a.num_q_heads + h * G + g % G
-                                     : (int64_t)s * a.num_q_heads + h * G + g;
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(a.q + qrow * kHeadDim + 8 * seg);
-            const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                x[b][2 * m] = __uint_as_float(d[m] << 16);
-                x[b][2 * m + 1] = __uint_as_float(d[m] & 0xFFFF0000u);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                x[b][i] = 0.0f;
-        }
+        const int gc = g < ncols ? g : 0;
+        const int64_t qrow = EXT ? (row0 + gc / G) * a.num_q_heads + h * G + gc % G
+                                 : (int64_t)s * a.num_q_heads + h * G + gc;
+        qw[b] = *reinterpret_cast<const u32x4 *>(a.q + qrow * kHeadDim + 8 * seg);
     }
-    // With the query rows on their way, issue the wave's first two tiles, so that their
-    // loads overlap the query prologue and the walk starts on data already in registers
-    // (a load round trip at kernel start, ~3 us on the Qwen3-4B-like decode, is paid once).
-    // Loads return in order, so the prologue's wait for the query rows does not wait for
-    // the tiles.  (Decode only: the extend's long workgroups gain nothing from it.  Not in
-    // the workgroup of a fused step that writes the new token's rows: its reads must all
-    // follow those stores, which the prologue's barriers order.)
     Tile<CB> TA, TB;
     const bool writer = a.new_slots != nullptr && split == (L - 1) / a.split_tokens;
     const bool pre = !EXT && !writer && t_begin < t_end;
-    if (pre)
-        walk_first_tiles<CB, !EXT>(TA, TB, a, pid, ptab, h, t_begin, t_end, lane);
+    if constexpr (!EXT)
+        walk_first_tiles<CB, true>(TA, TB, a, pid, ptab, h, t_begin, t_end, lane);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int g = b * 16 + wave * 4 + (lane >> 4);
+        const uint32_t d[4] = {qw[b].x, qw[b].y, qw[b].z, qw[b].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            x[b][2 * m] = g < ncols ? __uint_as_float(d[m] << 16) : 0.0f;
+            x[b][2 * m + 1] = g < ncols ? __uint_as_float(d[m] & 0xFFFF0000u) : 0.0f;
+        }
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int g = b * 16 + wave * 4 + (lane >> 4);
@@ -1545,28 +1550,34 @@ void decode_balanced_kernel(DecodeArgs a)
         const int t_begin = seg_tok0 + (wave * n_tiles / kDecodeWaves) * kTile;
         const int t_end = min(seg_tok1, seg_tok0 + ((wave + 1) * n_tiles / kDecodeWaves) * kTile);
         const int32_t *ptab = a.page_table + (int64_t)s * a.max_pages;
+        // (page ids and tile addresses are clamped into the table and the pool, so the loads
+        // below are in bounds for any range, an empty one included)
         PageIds pid;
-        if (t_begin < t_end)
-            pid.fill(a, ptab, t_begin >> a.page_log2, lane);
+        pid.fill(a, ptab, t_begin >> a.page_log2, lane);
 
         // ---- a6: the query rows of (s, h): rotate, scale, round to one grid, cut into digits
         float x[8];
         float amax = 0.0f;
+        // The query row is requested, then the wave's first two tiles of the segment, so that
+        // the tile loads overlap the query prologue, the query row's latency included: both
+        // are unconditional (a lane past the G heads reads head 0's row and zeroes it), as a
+        // load issued under a branch would make the compiler wait for every load issued
+        // before it where the paths join.  The segment of a fused step that writes the new
+        // token's rows does not use these tiles: its reads must follow those stores, which
+        // the prologue's barriers order, so its walk issues them again.
+        Tile<CB> TA, TB;
+        const bool writer = k.new_slots != nullptr && (L - 1) / kTile >= t0 && (L - 1) / kTile < t1;
+        const bool pre = !writer && t_begin < t_end;
         {
             const int gq = wave * 4 + (lane >> 4);
-            if (gq < G) {
-                const int64_t qrow = (int64_t)s * k.num_q_heads + h * G + gq;
-                const u32x4 wq = *reinterpret_cast<const u32x4 *>(k.q + qrow * kHeadDim + 8 * seg);
-                const uint32_t d[4] = {wq.x, wq.y, wq.z, wq.w};
+            const int64_t qrow = (int64_t)s * k.num_q_heads + h * G + (gq < G ? gq : 0);
+            const u32x4 wq = *reinterpret_cast<const u32x4 *>(k.q + qrow * kHeadDim + 8 * seg);
+            walk_first_tiles<CB, true>(TA, TB, a, pid, ptab, h, t_begin, t_end, lane);
+            const uint32_t d[4] = {wq.x, wq.y, wq.z, wq.w};
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    x[2 * m] = __uint_as_float(d[m] << 16);
-                    x[2 * m + 1] = __uint_as_float(d[m] & 0xFFFF0000u);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    x[i] = 0.0f;
+            for (int m = 0; m < 4; ++m) {
+                x[2 * m] = gq < G ? __uint_as_float(d[m] << 16) : 0.0f;
+                x[2 * m + 1] = gq < G ? __uint_as_float(d[m] & 0xFFFF0000u) : 0.0f;
             }
             rotate_query_row<BK>(x, seg);
             float sum = 0.0f;
@@ -1640,9 +1651,8 @@ void decode_balanced_kernel(DecodeArgs a)
         st[0].qsum = lds_qsum[gl];
 
         // ---- a7..a9: the page walk
-        Tile<CB> TA, TB;
         walk_tiles<F, false, CB, 1, true>(st, a, pid, ptab, h, t_begin, t_end, lane, kscale, qop, pl,
-                                          col_len, 0, TA, TB);
+                                          col_len, 0, TA, TB, pre);
 
         // ---- the waves' (and for F = 2 the two halves') states of this segment
         WaveState &sb = st[0];
