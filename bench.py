@@ -767,6 +767,11 @@ def measure_paged_ceiling(s, torch, K, reps=20):
         t = timed(lambda: K.kvrq_paged_read(s.cache, pages_dev, sink, wgs_per_cu=wg))
         out["paged_read"][f"{wg}_wgs_per_cu"] = {"us": round(t * 1e6, 2),
                                                  "gbps": round(read_bytes / t / 1e9, 1)}
+    # the same bytes per (page, KV head) block as the decode reads them, two tiles in flight
+    # per wave, two workgroups per CU: with the decode's load shapes, and with whole-line V
+    for pat, name in ((1, "decode_shapes"), (2, "decode_blocks_full_line_v")):
+        t = timed(lambda: K.kvrq_paged_read(s.cache, pages_dev, sink, wgs_per_cu=2, pattern=pat))
+        out["paged_read"][name] = {"us": round(t * 1e6, 2), "gbps": round(read_bytes / t / 1e9, 1)}
     t = timed(lambda: K.kvrq_device_read(big, sink, nbytes=read_bytes // 16 * 16))
     out["streaming_read"] = {"us": round(t * 1e6, 2), "gbps": round(read_bytes / t / 1e9, 1)}
     t = timed(lambda: K.kv_int4_paged_decode(s.cache, s.q, s.tab, lens_dev, maxlen, out=s.out,
@@ -774,6 +779,7 @@ def measure_paged_ceiling(s, torch, K, reps=20):
     out["decode"] = {"us": round(t * 1e6, 2), "algorithmic_gbps": round(dec_bytes / t / 1e9, 1)}
     best = min(v["us"] for v in out["paged_read"].values())
     out["decode_vs_paged_read"] = round(best / out["decode"]["us"], 4)
+    out["decode_vs_decode_shapes"] = round(out["paged_read"]["decode_shapes"]["us"] / out["decode"]["us"], 4)
     return out
 
 

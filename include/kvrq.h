@@ -382,12 +382,18 @@ KVRQ_API kvrq_status kvrq_device_read(const void *src, size_t bytes, uint32_t *s
  * own bytes in the decode's order: the ceiling of a read-only kernel over a
  * page-scattered cache (the pages are fixed-size and scattered by the allocator;
  * wispaper.ai blog, section 1), next to kvrq_device_read's ceiling over contiguous
- * memory.  Reads num_list * num_kv_heads * page_size * 136 bytes.  4-bit pools only,
- * with num_kv_heads * page_size a multiple of 128 (KVRQ_EUNSUPPORTED otherwise);
- * wgs_per_cu (1..4) workgroups of four waves per CU.  Asynchronous on `stream`. */
+ * memory.  Reads num_list * num_kv_heads * page_size * 136 bytes.
+ *   pattern 0: whole pages per wave, 16-byte loads (num_kv_heads * page_size a
+ *              multiple of 128);
+ *   pattern 1: per (page, KV head) block of 16 tokens, one workgroup per KV head and
+ *              share of the list, two 32-token tiles in flight per wave, with the
+ *              decode's own load shapes (16-byte K loads, 4-byte V and parameter loads);
+ *   pattern 2: as 1 with 16-byte V loads (page_size a multiple of 16 for 1 and 2).
+ * 4-bit pools only (KVRQ_EUNSUPPORTED otherwise); wgs_per_cu (1..4) workgroups of four
+ * waves per CU.  Asynchronous on `stream`. */
 KVRQ_API kvrq_status kvrq_paged_read(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
-                                     const int32_t *pages, int64_t num_list, int32_t wgs_per_cu,
-                                     uint32_t *sink, void *stream);
+                                     const int32_t *pages, int64_t num_list, int32_t pattern,
+                                     int32_t wgs_per_cu, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

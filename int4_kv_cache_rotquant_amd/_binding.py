@@ -83,7 +83,7 @@ def lib() -> ctypes.CDLL:
         "kvrq_bf16_paged_write": (st, [P, P, P, P, P, i64, i64, i64, P, P]),
         "kvrq_device_copy": (st, [P, P, sz, P]),
         "kvrq_device_read": (st, [P, sz, P, P]),
-        "kvrq_paged_read": (st, [P, P, P, i64, i32, P, P]),
+        "kvrq_paged_read": (st, [P, P, P, i64, i32, i32, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -327,14 +327,17 @@ def kvrq_device_read(src, sink, nbytes: Optional[int] = None, stream=None) -> No
     _check(lib().kvrq_device_read(_ptr(src), n, _ptr(sink), _stream(stream)))
 
 
-def kvrq_paged_read(cache: PagedInt4Cache, pages, sink, wgs_per_cu: int = 2, stream=None) -> None:
-    """Page-gather read of the pages listed in the int32 device tensor ``pages`` (whole pages:
-    K and V codes and parameters of every KV head), in list order; nothing is written."""
+def kvrq_paged_read(cache: PagedInt4Cache, pages, sink, wgs_per_cu: int = 2, pattern: int = 0,
+                    stream=None) -> None:
+    """Page-gather read of the pages listed in the int32 device tensor ``pages`` (K and V codes
+    and parameters of every KV head), in list order; nothing is written.  ``pattern`` 0: whole
+    pages per wave; 1: per (page, KV head) block with the decode's load shapes; 2: as 1 with
+    16-byte V loads."""
     import torch
     if pages.dtype != torch.int32 or not pages.is_contiguous():
         raise ValueError("pages must be a contiguous int32 tensor")
     _check(lib().kvrq_paged_read(ctypes.byref(cache.desc), ctypes.byref(cache.buffers), _ptr(pages),
-                                 int(pages.numel()), wgs_per_cu, _ptr(sink), _stream(stream)))
+                                 int(pages.numel()), pattern, wgs_per_cu, _ptr(sink), _stream(stream)))
 
 
 # --------------------------------------------------------------------- host page pool

@@ -841,7 +841,8 @@ kvrq_status kvrq_device_read(const void *src, size_t bytes, uint32_t *sink, void
 }
 
 kvrq_status kvrq_paged_read(const kvrq_cache_desc *d, const kvrq_cache_buffers *b, const int32_t *pages,
-                            int64_t num_list, int32_t wgs_per_cu, uint32_t *sink, void *stream)
+                            int64_t num_list, int32_t pattern, int32_t wgs_per_cu, uint32_t *sink,
+                            void *stream)
 {
     kvrq_status st = check_desc(d);
     if (st != KVRQ_OK)
@@ -850,9 +851,14 @@ kvrq_status kvrq_paged_read(const kvrq_cache_desc *d, const kvrq_cache_buffers *
         return st;
     if (code_bits(d->k_bits) != 4 || code_bits(d->v_bits) != 4)
         return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read reads 4-bit pools only");
-    if (((int64_t)d->num_kv_heads * d->page_size) % 128 != 0)
-        return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read needs num_kv_heads * page_size to be a multiple "
-                                       "of 128 (got %d * %d)", d->num_kv_heads, d->page_size);
+    if (pattern < 0 || pattern > 2)
+        return fail(KVRQ_EINVAL, "pattern must be 0, 1 or 2 (got %d)", pattern);
+    if (pattern == 0 && ((int64_t)d->num_kv_heads * d->page_size) % 128 != 0)
+        return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read pattern 0 needs num_kv_heads * page_size to be a "
+                                       "multiple of 128 (got %d * %d)", d->num_kv_heads, d->page_size);
+    if (pattern != 0 && d->page_size % 16 != 0)
+        return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read patterns 1 and 2 need page_size to be a multiple "
+                                       "of 16 (got %d)", d->page_size);
     if (num_list < 0)
         return fail(KVRQ_EINVAL, "num_list must be >= 0");
     if (wgs_per_cu < 1 || wgs_per_cu > 4)
@@ -870,6 +876,9 @@ kvrq_status kvrq_paged_read(const kvrq_cache_desc *d, const kvrq_cache_buffers *
     a.num_list = num_list;
     a.units_per_page = d->num_kv_heads * d->page_size / 128;
     a.num_pages = d->num_pages;
+    a.num_kv_heads = d->num_kv_heads;
+    a.page_size = d->page_size;
+    a.pattern = pattern;
     a.sink = sink;
     a.magic = 0x9E3779B9u;
     return hip_status(kvrq::launch_paged_read(a, wgs_per_cu, stream), "kvrq_paged_read");

@@ -19,6 +19,10 @@ constexpr int kWriteWavesPerSimd = 2;
 // persistent write grid: 256-lane workgroups per CU, one wave per SIMD each, so all of them
 // are resident at once (one more, waiting for a slot, measured 8% slower on 16k-token chunks)
 constexpr int kWriteWgsPerCu = kWriteWavesPerSimd;
+// a write that stores as it goes (too few tile pairs per wave to stage them) runs three
+// workgroups per CU (its 104 VGPRs allow four): the 16k-token long-context chunk 19.67 ->
+// 19.34 us against two, four no faster (measured on MI355X, same box)
+constexpr int kWriteWgsPerCuUnstaged = 3;
 constexpr int kWriteStage = 8;      // tile pairs per wave staged in LDS by the staged write
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave
 constexpr int kDecodeWaves = 4;     // waves per decode workgroup, each on its own token range
@@ -74,9 +78,12 @@ struct CopyArgs {
     int32_t page_log2;
 };
 
-// Page-gather read (a measurement kernel): whole cache pages in list order.  A page is
-// units_per_page units of 17 lines of 1 KiB: 8 lines of K codes, 8 of V codes, and one of
-// parameters (512 bytes of K, 512 of V).
+// Page-gather read (a measurement kernel): the cache pages of a list, in list order.
+// Pattern 0 reads whole pages per wave, as units of 17 lines of 1 KiB (8 lines of K codes,
+// 8 of V codes, one of parameters: 512 bytes of K, 512 of V), units_per_page per page.
+// Patterns 1 and 2 read per (page, KV head) block of 16 tokens as the decode does (one
+// workgroup per KV head and share of the list); 1 with the decode's load shapes, 2 with
+// 16-byte V loads.
 struct PagedReadArgs {
     const uint8_t *k_codes;
     const uint8_t *v_codes;
@@ -84,8 +91,11 @@ struct PagedReadArgs {
     const uint8_t *v_params;
     const int32_t *pages;       // [num_list]; ids outside [0, num_pages) read page 0
     int64_t num_list;
-    int32_t units_per_page;     // num_kv_heads * page_size / 128
+    int32_t units_per_page;     // pattern 0: num_kv_heads * page_size / 128
     int32_t num_pages;
+    int32_t num_kv_heads;
+    int32_t page_size;
+    int32_t pattern;            // 0, 1 or 2
     uint32_t *sink;
     uint32_t magic;
 };

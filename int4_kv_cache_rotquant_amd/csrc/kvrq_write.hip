@@ -313,15 +313,105 @@ __global__ __launch_bounds__(256) void paged_read_kernel(PagedReadArgs a)
         *a.sink = acc;
 }
 
+// Page-gather read per (page, KV head) block, the decode's way: workgroup (h, j) of NG
+// groups reads KV head h of share j of the list, its four waves a quarter each, in blocks of
+// 16 tokens (a (page, head) block at page size 16, a quarter of one at 64), four blocks (two
+// of the decode's 32-token tiles) issued before the previous four are folded.  VW = 0: the
+// decode's load shapes (16 bytes of K per lane, four 4-byte V loads per lane at the PV
+// operand's offsets, one 4-byte parameter word per lane); VW = 1: V as one 16-byte load per
+// lane (whole lines).  The same bytes as the whole-page read, in units of 2,176 bytes.
+template <int VW>
+struct BlockUnit {
+    u32x4 k;
+    u32x4 v;
+    uint32_t par;
+};
+
+template <int VW>
+__device__ __forceinline__ void issue_block(BlockUnit<VW> &U, const PagedReadArgs &a, int64_t u,
+                                            int qpp, int h, int lane)
+{
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t pi = u / qpp;
+    int p = a.pages[pi];
+    p = (unsigned)p < (unsigned)a.num_pages ? p : 0;
+    const uint64_t cell = ((uint64_t)p * a.num_kv_heads + h) * a.page_size + 16 * (uint64_t)(u - pi * qpp);
+    const uint8_t *kb = a.k_codes + cell * kRowCodeBytes, *vb = a.v_codes + cell * kRowCodeBytes;
+    U.k = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kb) + lane);
+    if constexpr (VW == 1) {
+        U.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vb) + lane);
+    } else {
+        const uint32_t *v32 = reinterpret_cast<const uint32_t *>(vb + 256 * (lane >> 4) + 4 * (lane & 15));
+        U.v.x = __builtin_nontemporal_load(v32);
+        U.v.y = __builtin_nontemporal_load(v32 + 16);
+        U.v.z = __builtin_nontemporal_load(v32 + 32);
+        U.v.w = __builtin_nontemporal_load(v32 + 48);
+    }
+    const uint8_t *pb = lane < 32 ? a.k_params : a.v_params;
+    U.par = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(pb) + cell + (lane & 15));
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int VW>
+__device__ __forceinline__ void fold_block(uint32_t &acc, const BlockUnit<VW> &U)
+{
+    acc ^= U.k.x ^ U.k.y ^ U.k.z ^ U.k.w ^ U.v.x ^ U.v.y ^ U.v.z ^ U.v.w ^ U.par;
+    asm("" : "+v"(acc));
+}
+
+template <int VW>
+__global__ __launch_bounds__(256) void paged_read_blocks_kernel(PagedReadArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int NG = gridDim.x / a.num_kv_heads;
+    const int h = blockIdx.x / NG, j = blockIdx.x - h * NG;
+    if (h >= a.num_kv_heads)
+        return;
+    const int qpp = a.page_size / 16;
+    const int64_t n = a.num_list * qpp;
+    const int64_t g0 = n * j / NG, g1 = n * (j + 1) / NG;
+    const int64_t w0 = g0 + (g1 - g0) * wave / 4, w1 = g0 + (g1 - g0) * (wave + 1) / 4;
+    if (w0 >= w1)
+        return;
+    // past the share's end the last block is read again (in flight, not counted)
+    auto cl = [&](int64_t u) { return u < w1 ? u : w1 - 1; };
+    uint32_t acc = 0;
+    BlockUnit<VW> X[4], Y[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        issue_block(X[k], a, cl(w0 + k), qpp, h, lane);
+    int64_t u = w0;
+    for (; u + 4 < w1; u += 8) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            issue_block(Y[k], a, cl(u + 4 + k), qpp, h, lane);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            fold_block(acc, X[k]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            issue_block(X[k], a, cl(u + 8 + k), qpp, h, lane);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            fold_block(acc, Y[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        fold_block(acc, X[k]);
+    if (acc == a.magic)
+        *a.sink = acc;
+}
+
 // Persistent grid: enough workgroups for a few resident waves per SIMD, each wave
 // then walks several tiles so its next loads overlap its current arithmetic.
-unsigned write_grid(const WriteArgs &a)
+unsigned write_grid(const WriteArgs &a, int wgs_per_cu)
 {
     const int cus = device_cus();
     // one wave per (K, V) tile pair at most, four waves per workgroup
     const int64_t pairs = (a.num_tokens + kWriteTile - 1) / kWriteTile * a.num_kv_heads;
     const int64_t wgs = (pairs + 3) / 4;
-    const int64_t cap = (int64_t)cus * kWriteWgsPerCu;
+    const int64_t cap = (int64_t)cus * wgs_per_cu;
     return (unsigned)(wgs < cap ? wgs : cap);
 }
 
@@ -329,10 +419,12 @@ template <int BK, int BV>
 hipError_t launch_bk_bv(const WriteArgs &a, hipStream_t s)
 {
     // the code widths are template arguments, so each kernel carries one encoder per tensor
-    const dim3 grid(write_grid(a));
-    // staged when every wave has a full stage of pairs to encode (4-bit pools)
+    // staged when every wave of the two-workgroups-per-CU grid has a full stage of pairs to
+    // encode (4-bit pools); otherwise the grid takes three workgroups per CU
     const int64_t pairs = (a.num_tokens + kWriteTile - 1) / kWriteTile * a.num_kv_heads;
-    const bool staged = pairs >= (int64_t)kWriteStage * 4 * grid.x;
+    const unsigned grid2 = write_grid(a, kWriteWgsPerCu);
+    const bool staged = a.k_bits != 2 && a.v_bits != 2 && pairs >= (int64_t)kWriteStage * 4 * grid2;
+    const dim3 grid(staged ? grid2 : write_grid(a, kWriteWgsPerCuUnstaged));
     if (a.k_bits == 2 && a.v_bits == 2)
         hipLaunchKernelGGL((rotquant_write_kernel<BK, BV, 2, 2, false>), grid, dim3(256), 0, s, a);
     else if (a.k_bits == 2)
@@ -432,8 +524,18 @@ int launch_paged_read(const PagedReadArgs &a, int wgs_per_cu, void *stream)
 {
     if (a.num_list == 0)
         return 0;
-    hipLaunchKernelGGL(paged_read_kernel, dim3((unsigned)(device_cus() * wgs_per_cu)), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), a);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (a.pattern == 0) {
+        hipLaunchKernelGGL(paged_read_kernel, dim3((unsigned)(device_cus() * wgs_per_cu)), dim3(256), 0, s, a);
+    } else {
+        // whole groups of Hkv workgroups, as the balanced decode
+        const int groups = std::max(1, device_cus() * wgs_per_cu / a.num_kv_heads);
+        const dim3 grid((unsigned)(groups * a.num_kv_heads));
+        if (a.pattern == 1)
+            hipLaunchKernelGGL(paged_read_blocks_kernel<0>, grid, dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(paged_read_blocks_kernel<1>, grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

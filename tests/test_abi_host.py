@@ -231,8 +231,9 @@ def test_paged_read_validation(K):
     L = K.lib()
     d, b = _desc(K), _bufs(K)
 
-    def call(desc=d, bufs=b, pages=0x7000, n=4, wgs=2, sink=0x8000):
-        return L.kvrq_paged_read(ctypes.byref(desc), ctypes.byref(bufs), pages, n, wgs, sink, None)
+    def call(desc=d, bufs=b, pages=0x7000, n=4, wgs=2, sink=0x8000, pattern=0):
+        return L.kvrq_paged_read(ctypes.byref(desc), ctypes.byref(bufs), pages, n, pattern, wgs, sink,
+                                 None)
 
     assert call(n=0) == K.KVRQ_OK                       # nothing to read: no launch
     assert call(n=-1) == K.KVRQ_EINVAL
@@ -242,6 +243,9 @@ def test_paged_read_validation(K):
     assert call(sink=0) == K.KVRQ_EINVAL
     assert call(sink=0x8002) == K.KVRQ_EINVAL
     assert call(desc=_desc(K, page_size=8)) == K.KVRQ_EUNSUPPORTED      # 8 heads x 8 tokens
+    assert call(desc=_desc(K, page_size=8), pattern=1) == K.KVRQ_EUNSUPPORTED   # 16-token blocks
+    assert call(pattern=3) == K.KVRQ_EINVAL
+    assert call(pattern=-1) == K.KVRQ_EINVAL
     assert call(desc=_desc(K, k_bits=2)) == K.KVRQ_EUNSUPPORTED
     assert call(bufs=K.CacheBuffers(0, 0x1000, 0x2000, 0x3000)) == K.KVRQ_EINVAL
     assert call(desc=_desc(K, head_dim=64)) == K.KVRQ_EUNSUPPORTED
