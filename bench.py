@@ -767,9 +767,11 @@ def measure_paged_ceiling(s, torch, K, reps=20):
         t = timed(lambda: K.kvrq_paged_read(s.cache, pages_dev, sink, wgs_per_cu=wg))
         out["paged_read"][f"{wg}_wgs_per_cu"] = {"us": round(t * 1e6, 2),
                                                  "gbps": round(read_bytes / t / 1e9, 1)}
-    # the same bytes per (page, KV head) block as the decode reads them, two tiles in flight
-    # per wave, two workgroups per CU: with the decode's load shapes, and with whole-line V
-    for pat, name in ((1, "decode_shapes"), (2, "decode_blocks_full_line_v")):
+    # the same bytes per (page, KV head) block as the decode reads them, two workgroups per
+    # CU: with the decode's load shapes and two tiles in flight per wave, with whole-line V,
+    # and with the decode's shapes and four tiles in flight
+    for pat, name in ((1, "decode_shapes"), (2, "decode_blocks_full_line_v"),
+                      (3, "decode_shapes_four_tiles")):
         t = timed(lambda: K.kvrq_paged_read(s.cache, pages_dev, sink, wgs_per_cu=2, pattern=pat))
         out["paged_read"][name] = {"us": round(t * 1e6, 2), "gbps": round(read_bytes / t / 1e9, 1)}
     t = timed(lambda: K.kvrq_device_read(big, sink, nbytes=read_bytes // 16 * 16))

@@ -388,7 +388,9 @@ KVRQ_API kvrq_status kvrq_device_read(const void *src, size_t bytes, uint32_t *s
  *   pattern 1: per (page, KV head) block of 16 tokens, one workgroup per KV head and
  *              share of the list, two 32-token tiles in flight per wave, with the
  *              decode's own load shapes (16-byte K loads, 4-byte V and parameter loads);
- *   pattern 2: as 1 with 16-byte V loads (page_size a multiple of 16 for 1 and 2).
+ *   pattern 2: as 1 with 16-byte V loads;
+ *   pattern 3: as 1 with four 32-token tiles in flight per wave (page_size a
+ *              multiple of 16 for 1 to 3).
  * 4-bit pools only (KVRQ_EUNSUPPORTED otherwise); wgs_per_cu (1..4) workgroups of four
  * waves per CU.  Asynchronous on `stream`. */
 KVRQ_API kvrq_status kvrq_paged_read(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,

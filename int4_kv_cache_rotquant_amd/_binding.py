@@ -331,8 +331,8 @@ def kvrq_paged_read(cache: PagedInt4Cache, pages, sink, wgs_per_cu: int = 2, pat
                     stream=None) -> None:
     """Page-gather read of the pages listed in the int32 device tensor ``pages`` (K and V codes
     and parameters of every KV head), in list order; nothing is written.  ``pattern`` 0: whole
-    pages per wave; 1: per (page, KV head) block with the decode's load shapes; 2: as 1 with
-    16-byte V loads."""
+    pages per wave; 1: per (page, KV head) block with the decode's load shapes and depth; 2: as 1
+    with 16-byte V loads; 3: as 1 with four tiles in flight."""
     import torch
     if pages.dtype != torch.int32 or not pages.is_contiguous():
         raise ValueError("pages must be a contiguous int32 tensor")

@@ -851,13 +851,13 @@ kvrq_status kvrq_paged_read(const kvrq_cache_desc *d, const kvrq_cache_buffers *
         return st;
     if (code_bits(d->k_bits) != 4 || code_bits(d->v_bits) != 4)
         return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read reads 4-bit pools only");
-    if (pattern < 0 || pattern > 2)
-        return fail(KVRQ_EINVAL, "pattern must be 0, 1 or 2 (got %d)", pattern);
+    if (pattern < 0 || pattern > 3)
+        return fail(KVRQ_EINVAL, "pattern must be 0, 1, 2 or 3 (got %d)", pattern);
     if (pattern == 0 && ((int64_t)d->num_kv_heads * d->page_size) % 128 != 0)
         return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read pattern 0 needs num_kv_heads * page_size to be a "
                                        "multiple of 128 (got %d * %d)", d->num_kv_heads, d->page_size);
     if (pattern != 0 && d->page_size % 16 != 0)
-        return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read patterns 1 and 2 need page_size to be a multiple "
+        return fail(KVRQ_EUNSUPPORTED, "kvrq_paged_read patterns 1 to 3 need page_size to be a multiple "
                                        "of 16 (got %d)", d->page_size);
     if (num_list < 0)
         return fail(KVRQ_EINVAL, "num_list must be >= 0");

@@ -81,9 +81,10 @@ struct CopyArgs {
 // Page-gather read (a measurement kernel): the cache pages of a list, in list order.
 // Pattern 0 reads whole pages per wave, as units of 17 lines of 1 KiB (8 lines of K codes,
 // 8 of V codes, one of parameters: 512 bytes of K, 512 of V), units_per_page per page.
-// Patterns 1 and 2 read per (page, KV head) block of 16 tokens as the decode does (one
-// workgroup per KV head and share of the list); 1 with the decode's load shapes, 2 with
-// 16-byte V loads.
+// Patterns 1 to 3 read per (page, KV head) block of 16 tokens as the decode does (one
+// workgroup per KV head and share of the list); 1 with the decode's load shapes and depth
+// (two 32-token tiles in flight per wave), 2 with 16-byte V loads, 3 with the decode's
+// shapes and four tiles in flight.
 struct PagedReadArgs {
     const uint8_t *k_codes;
     const uint8_t *v_codes;
@@ -95,7 +96,7 @@ struct PagedReadArgs {
     int32_t num_pages;
     int32_t num_kv_heads;
     int32_t page_size;
-    int32_t pattern;            // 0, 1 or 2
+    int32_t pattern;            // 0 .. 3
     uint32_t *sink;
     uint32_t magic;
 };

@@ -315,8 +315,8 @@ __global__ __launch_bounds__(256) void paged_read_kernel(PagedReadArgs a)
 
 // Page-gather read per (page, KV head) block, the decode's way: workgroup (h, j) of NG
 // groups reads KV head h of share j of the list, its four waves a quarter each, in blocks of
-// 16 tokens (a (page, head) block at page size 16, a quarter of one at 64), four blocks (two
-// of the decode's 32-token tiles) issued before the previous four are folded.  VW = 0: the
+// 16 tokens (a (page, head) block at page size 16, a quarter of one at 64), NU blocks (NU / 2
+// of the decode's 32-token tiles) issued before the previous NU are folded.  VW = 0: the
 // decode's load shapes (16 bytes of K per lane, four 4-byte V loads per lane at the PV
 // operand's offsets, one 4-byte parameter word per lane); VW = 1: V as one 16-byte load per
 // lane (whole lines).  The same bytes as the whole-page read, in units of 2,176 bytes.
@@ -359,7 +359,7 @@ __device__ __forceinline__ void fold_block(uint32_t &acc, const BlockUnit<VW> &U
     asm("" : "+v"(acc));
 }
 
-template <int VW>
+template <int VW, int NU>
 __global__ __launch_bounds__(256) void paged_read_blocks_kernel(PagedReadArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -377,27 +377,27 @@ __global__ __launch_bounds__(256) void paged_read_blocks_kernel(PagedReadArgs a)
     // past the share's end the last block is read again (in flight, not counted)
     auto cl = [&](int64_t u) { return u < w1 ? u : w1 - 1; };
     uint32_t acc = 0;
-    BlockUnit<VW> X[4], Y[4];
+    BlockUnit<VW> X[NU], Y[NU];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < NU; ++k)
         issue_block(X[k], a, cl(w0 + k), qpp, h, lane);
     int64_t u = w0;
-    for (; u + 4 < w1; u += 8) {
+    for (; u + NU < w1; u += 2 * NU) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            issue_block(Y[k], a, cl(u + 4 + k), qpp, h, lane);
+        for (int k = 0; k < NU; ++k)
+            issue_block(Y[k], a, cl(u + NU + k), qpp, h, lane);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < NU; ++k)
             fold_block(acc, X[k]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            issue_block(X[k], a, cl(u + 8 + k), qpp, h, lane);
+        for (int k = 0; k < NU; ++k)
+            issue_block(X[k], a, cl(u + 2 * NU + k), qpp, h, lane);
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < NU; ++k)
             fold_block(acc, Y[k]);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < NU; ++k)
         fold_block(acc, X[k]);
     if (acc == a.magic)
         *a.sink = acc;
@@ -532,9 +532,11 @@ int launch_paged_read(const PagedReadArgs &a, int wgs_per_cu, void *stream)
         const int groups = std::max(1, device_cus() * wgs_per_cu / a.num_kv_heads);
         const dim3 grid((unsigned)(groups * a.num_kv_heads));
         if (a.pattern == 1)
-            hipLaunchKernelGGL(paged_read_blocks_kernel<0>, grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL((paged_read_blocks_kernel<0, 4>), grid, dim3(256), 0, s, a);
+        else if (a.pattern == 2)
+            hipLaunchKernelGGL((paged_read_blocks_kernel<1, 4>), grid, dim3(256), 0, s, a);
         else
-            hipLaunchKernelGGL(paged_read_blocks_kernel<1>, grid, dim3(256), 0, s, a);
+            hipLaunchKernelGGL((paged_read_blocks_kernel<0, 8>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -244,7 +244,7 @@ def test_paged_read_validation(K):
     assert call(sink=0x8002) == K.KVRQ_EINVAL
     assert call(desc=_desc(K, page_size=8)) == K.KVRQ_EUNSUPPORTED      # 8 heads x 8 tokens
     assert call(desc=_desc(K, page_size=8), pattern=1) == K.KVRQ_EUNSUPPORTED   # 16-token blocks
-    assert call(pattern=3) == K.KVRQ_EINVAL
+    assert call(pattern=4) == K.KVRQ_EINVAL
     assert call(pattern=-1) == K.KVRQ_EINVAL
     assert call(desc=_desc(K, k_bits=2)) == K.KVRQ_EUNSUPPORTED
     assert call(bufs=K.CacheBuffers(0, 0x1000, 0x2000, 0x3000)) == K.KVRQ_EINVAL
