@@ -1026,16 +1026,16 @@ void decode_split_kernel(DecodeArgs a)
     float x[NB][8];
     float amax = 0.0f;
     // The query rows are requested (unconditionally: a lane past the columns reads the
-    // first column's row, which every workgroup has, and zeroes it), then, for the decode, the wave's first two tiles, so
-    // that the tile loads overlap the query prologue, the query rows' latency included, and
-    // the walk starts on data already in registers (a load round trip at kernel start, ~3 us
-    // on the Qwen3-4B-like decode, is paid once).  Loads return in order, so the prologue's
-    // wait for the query rows does not wait for the tiles; a load issued under a branch
-    // would make the compiler wait for every load issued before it where the paths join, so
-    // the tiles are always issued.  (Decode only: the extend's long workgroups gain nothing
-    // from it.  The workgroup of a fused step that writes the new token's rows does not use
-    // them: its reads must all follow those stores, which the prologue's barriers order, so
-    // its walk issues them again.)
+    // first column's row, which every workgroup has, and zeroes it), then, for the decode,
+    // the wave's first two tiles, so that the tile loads overlap the query prologue, the
+    // query rows' latency included, and the walk starts on data already in registers (a
+    // load round trip at kernel start, ~3 us on the Qwen3-4B-like decode, is paid once).
+    // Loads return in order, so the prologue's wait for the query rows does not wait for the
+    // tiles; a load issued under a branch would make the compiler wait for every load issued
+    // before it where the paths join, so the tiles are always issued.  (Decode only: the
+    // extend's long workgroups gain nothing from it.  The workgroup of a fused step that
+    // writes the new token's rows does not use them: its reads must all follow those stores,
+    // which the prologue's barriers order, so its walk issues them again.)
     u32x4 qw[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
