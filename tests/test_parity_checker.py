@@ -159,3 +159,28 @@ def test_param_at_midpoint_is_excused_and_codes_rederived():
     gpu[0][0, 0, 0] = codes
     rep = compare_write(tuple(gpu), orc, {"k": k, "v": v}, slots, (128, 0))
     assert rep["param_excused"] == 1 and rep["code_mismatch"] > 0
+
+
+def test_decode_compare_bounds():
+    """gpu_harness.decode_compare: 2e-3 absolute per element, and per output row
+    ||err|| <= 1e-3 ||ref|| + 1e-4; planted errors beyond either bound fail."""
+    from gpu_harness import decode_compare
+    rng = np.random.default_rng(5)
+    ref = rng.standard_normal((3, 4, D)) * 0.5
+    ok = ref + rng.uniform(-1e-5, 1e-5, ref.shape)
+    decode_compare(ok.astype(np.float32), ref, "noise")
+    one = ok.copy()
+    one[1, 2, 7] += 3e-3                                   # one element past 2e-3
+    with pytest.raises(AssertionError):
+        decode_compare(one.astype(np.float32), ref, "element")
+    row = ok.copy()
+    # every channel of one row 1.5e-3 off: each element within 2e-3, the row norm not
+    row[2, 1] += 1.5e-3 * np.sign(rng.standard_normal(D))
+    assert np.abs(row - ref).max() < 2e-3
+    assert np.linalg.norm(row[2, 1] - ref[2, 1]) > 1e-3 * np.linalg.norm(ref[2, 1]) + 1e-4
+    with pytest.raises(AssertionError):
+        decode_compare(row.astype(np.float32), ref, "row")
+    bad = ok.copy()
+    bad[0, 0, 0] = np.nan
+    with pytest.raises(AssertionError):
+        decode_compare(bad.astype(np.float32), ref, "nan")
