@@ -1053,9 +1053,10 @@ void decode_split_kernel(DecodeArgs a)
     // Loads return in order, so the prologue's wait for the query rows does not wait for the
     // tiles; a load issued under a branch would make the compiler wait for every load issued
     // before it where the paths join, so the tiles are always issued.  (Decode only: the
-    // extend's long workgroups gain nothing from it.  The workgroup of a fused step that
-    // writes the new token's rows does not use them: its reads must all follow those stores,
-    // which the prologue's barriers order, so its walk issues them again.)
+    // extend's long workgroups gain nothing from it.  In the workgroup of a fused step that
+    // writes the new token's rows, the wave whose first two tiles hold that token does not use
+    // them: its reads of it must follow those stores, which the prologue's barriers order, so
+    // its walk issues them again.)
     u32x4 qw[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -1066,7 +1067,10 @@ void decode_split_kernel(DecodeArgs a)
         qw[b] = *reinterpret_cast<const u32x4 *>(a.q + qrow * kHeadDim + 8 * seg);
     }
     Tile<CB> TA, TB;
-    const bool writer = a.new_slots != nullptr && split == (L - 1) / a.split_tokens;
+    // only a wave whose first two tiles hold the new token (position L - 1) must wait for its
+    // write; the other waves of the writing workgroup keep their early tiles
+    const bool writer = a.new_slots != nullptr && split == (L - 1) / a.split_tokens &&
+                        L - 1 >= t_begin && L - 1 < t_begin + 2 * kTile;
     const bool pre = !EXT && !writer && t_begin < t_end;
     if constexpr (!EXT)
         walk_first_tiles<CB, true>(TA, TB, a, pid, ptab, h, t_begin, t_end, lane);
@@ -1590,11 +1594,15 @@ void decode_balanced_kernel(DecodeArgs a)
         // the tile loads overlap the query prologue, the query row's latency included: both
         // are unconditional (a lane past the G heads reads head 0's row and zeroes it), as a
         // load issued under a branch would make the compiler wait for every load issued
-        // before it where the paths join.  The segment of a fused step that writes the new
-        // token's rows does not use these tiles: its reads must follow those stores, which
-        // the prologue's barriers order, so its walk issues them again.
+        // before it where the paths join.  In the segment of a fused step that writes the new
+        // token's rows, the wave whose first two tiles hold that token does not use these
+        // tiles: its reads of it must follow those stores, which the prologue's barriers
+        // order, so its walk issues them again.
         Tile<CB> TA, TB;
-        const bool writer = k.new_slots != nullptr && (L - 1) / kTile >= t0 && (L - 1) / kTile < t1;
+        // only a wave whose first two tiles hold the new token (position L - 1) must wait for
+        // its write; the other waves of the segment keep their early tiles
+        const bool writer = k.new_slots != nullptr && (L - 1) / kTile >= t0 && (L - 1) / kTile < t1 &&
+                            L - 1 >= t_begin && L - 1 < t_begin + 2 * kTile;
         const bool pre = !writer && t_begin < t_end;
         {
             const int gq = wave * 4 + (lane >> 4);
