@@ -1007,8 +1007,9 @@ void decode_split_kernel(DecodeArgs a)
     // scalar so the page-table lookups and the loop control stay on the scalar unit
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // fused decode step: the workgroup holding position L - 1 writes that token's rows
-    // first; the barrier after the query prologue orders those stores before the tile
-    // loads of all four waves, and no other workgroup reads that position
+    // first; the barrier after the query prologue orders those stores before every load of
+    // that position (only the wave whose first two tiles hold it waits for them to load), and
+    // no other workgroup reads that position
     if constexpr (!EXT) {
         if (a.new_slots != nullptr && wave == 1 && split == (L - 1) / a.split_tokens && lane < 8)
             write_new_rows<BK>(a, s, h, lane);
@@ -1571,8 +1572,9 @@ void decode_balanced_kernel(DecodeArgs a)
         const int G = k.group;
         const int L = min(k.seq_lens[s], k.max_seq_len);
         // fused decode step: the segment holding position L - 1 writes that token's rows
-        // first; the prologue's barriers order those stores before every tile load of this
-        // workgroup, and no other workgroup reads that position
+        // first; the prologue's barriers order those stores before every load of that
+        // position (only the wave whose first two tiles hold it waits for them to load), and
+        // no other workgroup reads that position
         if (k.new_slots != nullptr && wave == 1 && lane < 8 && (L - 1) / kTile >= t0 &&
             (L - 1) / kTile < t1)
             write_new_rows<BK>(k, s, h, lane);
