@@ -391,8 +391,11 @@ KVRQ_API kvrq_status kvrq_device_read(const void *src, size_t bytes, uint32_t *s
  *   pattern 2: as 1 with 16-byte V loads;
  *   pattern 3: as 1 with four 32-token tiles in flight per wave (page_size a
  *              multiple of 16 for 1 to 3).
- * 4-bit pools only (KVRQ_EUNSUPPORTED otherwise); wgs_per_cu (1..4) workgroups of four
- * waves per CU.  Asynchronous on `stream`. */
+ * Patterns 1 to 3 may read a wave's last blocks again past the end of its share (in
+ * flight only).  4-bit pools only (KVRQ_EUNSUPPORTED otherwise); wgs_per_cu (1..4)
+ * workgroups of four waves per CU; a bad pattern, grid size, NULL `pages` or `sink`, or a
+ * sink not 4-byte aligned is KVRQ_EINVAL, checked before any launch.  Asynchronous on
+ * `stream`. */
 KVRQ_API kvrq_status kvrq_paged_read(const kvrq_cache_desc *d, const kvrq_cache_buffers *b,
                                      const int32_t *pages, int64_t num_list, int32_t pattern,
                                      int32_t wgs_per_cu, uint32_t *sink, void *stream);
