@@ -115,6 +115,18 @@ def test_page_sizes(K, P):
     decode_compare(out, _ref(orc, q, tab, L, 1, P, 64, 64), f"P{P}")
 
 
+@pytest.mark.parametrize("split", [16384, 32768])
+def test_long_walks_split_grid(K, split):
+    """Splits of 16k and 32k tokens: each wave walks up to 8k tokens, 500 pages of 16, so its
+    window of 128 page ids (and the ids it requests one move ahead) moves several times on
+    the split grid (the large automatic decodes take the balanced grid instead)."""
+    lens = [32000, 17001, 5003]
+    Hkv, G, P = 2, 4, 16
+    cache, orc, q, tab, L = _build(K, lens, Hkv, Hkv * G, P, 128, 0, seed=44)
+    out = _run(K, cache, q, tab, L, split=split)
+    decode_compare(out, _ref(orc, q, tab, L, Hkv, P, 128, 0), f"long walks split{split}")
+
+
 def test_split_sweep_consistent(K):
     lens = [2049, 700, 33]
     cache, orc, q, tab, L = _build(K, lens, 2, 16, 16, 128, 128, seed=11)

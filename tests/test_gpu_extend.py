@@ -69,6 +69,17 @@ def test_blocks_and_pages(K, kb, vb, P):
     decode_compare(out, _ref(orc, q, qo, tab, L, 2, P, kb, vb), f"extend kb={kb} vb={vb} P={P}")
 
 
+def test_long_prefix_one_split(K):
+    """A 20k-token prefix walked in one split: each wave of a row block walks ~5k tokens, 300
+    pages of 16, so its window of page ids (and the ids requested one move ahead) moves
+    several times."""
+    lens, news = [20000, 9000], [40, 33]
+    Hkv, G = 2, 4
+    cache, orc, q, qo, tab, L = _build(K, lens, news, Hkv, Hkv * G, 16, 64, 0, seed=61)
+    out = _run(K, cache, q, qo, tab, L, news, split=32768)
+    decode_compare(out, _ref(orc, q, qo, tab, L, Hkv, 16, 64, 0), "extend long prefix")
+
+
 def test_split_counts_agree(K):
     lens, news = [1500, 700], [96, 31]
     cache, orc, q, qo, tab, L = _build(K, lens, news, 1, 8, 16, 128, 0, seed=50)
