@@ -35,7 +35,10 @@ stream: the write's tokens written / write time and the decode's tokens
 attended / decode time.  The ``roofline`` object covers the kernel with the
 largest share of the step time: algorithmic bytes per launch / its mean launch
 time.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload in the same unit (rank 0, N=1 only).
+workload in the same unit (rank 0, N=1 only).  ``--graph`` (decode-step
+workloads) adds a ``graph`` object: the workload's distinct steps recorded once
+into a HIP graph and replayed, i.e. the step without the host's per-call launch
+overhead, which a small batch's kernels are shorter than.
 """
 from __future__ import annotations
 
@@ -90,6 +93,8 @@ def parse_args(argv=None):
     ap.add_argument("--k-bits", type=int, default=4, choices=[4, 2], help="K code width")
     ap.add_argument("--v-bits", type=int, default=4, choices=[4, 2], help="V code width")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="decode-step workloads: also time the steps replayed from a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle sample time")
     ap.add_argument("--cpu-threads", type=int, default=0,
@@ -131,6 +136,8 @@ def workload_tag(args) -> str:
         tag += "." + args.variant
     elif args.k_block is not None:
         tag += f".k{args.k_block}"
+    if (args.k_bits, args.v_bits) != (4, 4):
+        tag += f".k{args.k_bits}v{args.v_bits}bit"
     return tag
 
 
@@ -350,6 +357,7 @@ class Setup:
                             "kv_int4_paged_decode": round(dec_bytes)}
             self.rate_tokens = {"kv_rotquant_write": S, "kv_int4_paged_decode": attended}
         self.tokens_per_step = attended
+        self.tokens_by_step = [int(w.seq_lens.sum()) + S * (j + 1) for j in range(n_steps)]
         self.n_steps_max = n_steps
         self.config = {"workload": w.name, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
                        "num_seqs": S, "tokens_written": S, "tokens_attended_mean": round(attended),
@@ -499,6 +507,49 @@ class Setup:
 
     def step(self, i, ev):
         getattr(self, "step_" + self.args.workload)(i, ev)
+
+
+class _NoEvent:
+    def record(self):
+        pass
+
+
+def measure_graph(s, args, torch):
+    """The decode step replayed from a HIP graph: the workload's distinct steps (write +
+    decode, or the fused step) recorded once into one torch.cuda.CUDAGraph on the current
+    stream, after an eager warm-up, then replayed until about ``args.steps`` steps have run;
+    wall clock between two device synchronisations.  Each step's kernels are the eager
+    ones; what the graph removes is the host's per-call launch overhead."""
+    if not hasattr(s, "tokens_by_step"):
+        return {"skipped": "graph replay covers the decode-step workloads"}
+    n = s.n_steps_max
+    noev = [_NoEvent()] * 3
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for j in range(n):
+            s.step(j, noev)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for j in range(n):
+            s.step(j, noev)
+    torch.cuda.synchronize()
+    reps = max(1, round(args.steps / n))
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    steps = reps * n
+    tokens = float(np.mean(s.tokens_by_step))
+    return {"recorded_steps": n, "replays": reps, "steps": steps,
+            "ms_per_step": round(el / steps * 1e3, 4),
+            "value": round(tokens * steps / el, 1), "unit": "KV tokens/s"}
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -853,6 +904,7 @@ def main():
         s.step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    graph = measure_graph(s, args, torch) if args.graph else None
 
     # the measured copy ceiling, after the timed steps (clocks settled): a plain 1 GiB device
     # copy, median of five; its counter figures also calibrate the HBM byte counters
@@ -962,6 +1014,8 @@ def main():
         "read_probe_gbps": round(read_gbps, 1),
         "kernel_hash": kernel_source_hash(),
     }
+    if graph is not None:
+        result["graph"] = graph
     if args.workload == "qwen3_32b_like_decode" or args.bdr_vs_plain:
         # the write-side claim, next to the headline decode step
         result["bdr_vs_plain"] = measure_bdr_vs_plain(args, torch, K)
