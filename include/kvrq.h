@@ -37,6 +37,11 @@
  *     caller.  The library never allocates or frees device memory and never
  *     synchronises the device; hot-path calls are asynchronous on the HIP
  *     stream passed as `stream` (a hipStream_t; NULL = the null stream).
+ *   - The hot-path calls put only kernel launches on that stream (no memset,
+ *     copy, event or host wait), so a caller may record them into a HIP
+ *     graph during stream capture and replay it; the buffers recorded (and,
+ *     for the workspace calls, the zero state of the workspace's counters,
+ *     which every call restores) must stay valid for the replays.
  *   - A launch failure is reported as KVRQ_EHIP with the HIP error string.
  *   - head_dim must be 128.  Rotation blocks are 0 (no rotation, plain INT4)
  *     or 16, 32, 64, 128.  Page sizes are powers of two; the decode needs a
