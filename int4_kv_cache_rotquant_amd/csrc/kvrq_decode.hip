@@ -667,8 +667,12 @@ __device__ __forceinline__ void consume_tile(WaveState (&st)[NB], const Tile<CB>
             }
         }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            sc[0][r] = (float)((((dg[0][r] << 8) + dg[1][r]) << 8) + dg[2][r]);
+        for (int r = 0; r < 4; ++r) {
+            // two shift-adds; kept apart, the compiler reassociates them into three steps
+            int32_t t = (dg[0][r] << 8) + dg[1][r];
+            asm("" : "+v"(t));
+            sc[0][r] = (float)((t << 8) + dg[2][r]);
+        }
     }
 
     f16x8 bh[NB], bl[NB];
