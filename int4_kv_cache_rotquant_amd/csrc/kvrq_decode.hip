@@ -280,7 +280,7 @@ __device__ __forceinline__ u32x4 k_nibbles(const u32x2 &k)
 // the window are requested one move ahead, raw: a load whose value is used right away (the
 // range checks) makes the wave wait for every load in flight, its tiles included, while these
 // are only checked and moved into the window at the next move, 64 pages later, by which time
-// the tile waits in between have retired them (measured on MI355X, same box: the extend
+// the tile waits in between have retired them (measured on MI355X, same machine: the extend
 // 1,255 -> 1,251 us; the decodes, whose tile in flight is mostly back by a move, unchanged
 // within 0.1%).
 struct PageIds {
@@ -401,7 +401,7 @@ __device__ __forceinline__ void load_tile(Tile<CB> &T, const DecodeArgs &a, cons
     // unable to tell the two tiles in flight apart, and the wait before each tile would then
     // wait for both (measured: the page walk streamed ~10% slower).  The wave issues them at a
     // raised priority, so they are not held behind the other waves' arithmetic (measured on
-    // MI355X, same box: the Qwen3-32B-like decode 573.2 -> 571.5 us, the 1M-token decode
+    // MI355X, same machine: the Qwen3-32B-like decode 573.2 -> 571.5 us, the 1M-token decode
     // 196.8 -> 196.1 us, the Qwen3-4B-like decode 19.94 -> 19.83 us).
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(2);
@@ -418,7 +418,7 @@ __device__ __forceinline__ void load_tile(Tile<CB> &T, const DecodeArgs &a, cons
     // the parameter word of the lane: K (lanes 0..31) or V, first or second half.  Requested
     // ahead of the V codes (loads complete in order), so the tile's consumer converts the
     // parameters while the V codes are still arriving (the Qwen3-32B-like decode 568.8 ->
-    // 567.8 us, same box)
+    // 567.8 us, same machine)
     const bool ph = (la.lane & 16) != 0;
     const uint32_t *kp0 = a.k_params + cell[0], *kp1 = a.k_params + cell[1];
     const uint32_t *vp0 = a.v_params + cell[0], *vp1 = a.v_params + cell[1];

@@ -21,7 +21,7 @@ constexpr int kWriteWavesPerSimd = 2;
 constexpr int kWriteWgsPerCu = kWriteWavesPerSimd;
 // a write that stores as it goes (too few tile pairs per wave to stage them) runs three
 // workgroups per CU (its 104 VGPRs allow four): the 16k-token long-context chunk 19.67 ->
-// 19.34 us against two, four no faster (measured on MI355X, same box)
+// 19.34 us against two, four no faster (measured on MI355X, same machine)
 constexpr int kWriteWgsPerCuUnstaged = 3;
 constexpr int kWriteStage = 8;      // tile pairs per wave staged in LDS by the staged write
 constexpr int kMaxGroup = 16;       // query heads per KV head handled by one decode wave

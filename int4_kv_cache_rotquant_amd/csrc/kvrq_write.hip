@@ -70,7 +70,7 @@ __device__ __forceinline__ void load_row(RowLoad &R, const uint16_t *src_base, i
 // workgroup, two workgroups per CU: the chip's LDS holds a 32k-token chunk's whole output)
 // and are stored in one burst when the stage is full and at the end.  HBM does not overlap
 // reads and writes, and the stores interleaved with the loads cost more than the same
-// stores in a burst after them (measured on MI355X, same box: the 32k chunk 33.8 -> 32.9
+// stores in a burst after them (measured on MI355X, same machine: the 32k chunk 33.8 -> 32.9
 // us, the Qwen3-4B-like write 44.1 -> 41.8 us).  A wave with fewer pairs than a full stage stores
 // as it goes: a short write has too little reading left to hide the burst behind (the 16k
 // long-context chunk, four pairs per wave: 19.4 -> 21.3 us staged).
@@ -95,7 +95,7 @@ void rotquant_write_kernel(WriteArgs a)
         const int64_t tt = 2 * g2 + (r2 & 1);
         const int64_t h = r2 >> 1;
         // the staged write issues its loads at a raised priority, so they are not held
-        // behind the other waves' encoding (measured on MI355X, same box: the 32k chunk 31.9
+        // behind the other waves' encoding (measured on MI355X, same machine: the 32k chunk 31.9
         // -> 31.4 us, the Qwen3-4B-like write 41.7 -> 41.4 us; the unstaged 16k-token chunk,
         // whose stores go out between the loads, 19.07 -> 19.63 us, so it keeps one priority)
         if constexpr (STAGED)

@@ -70,8 +70,8 @@ COPY = "kvrq::(anonymous namespace)::device_copy_kernel(HIP_vector_type<unsigned
 
 
 def _counter_dir(path, counter, rows):
-    os.makedirs(os.path.join(path, "box", "1234"))
-    with open(os.path.join(path, "box", "1234", "run_counter_collection.csv"), "w", newline="") as f:
+    os.makedirs(os.path.join(path, "host", "1234"))
+    with open(os.path.join(path, "host", "1234", "run_counter_collection.csv"), "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
         w.writeheader()
         for name, value in rows:
