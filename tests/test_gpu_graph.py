@@ -11,7 +11,8 @@ step itself matches the oracle (its write, then its fp64 decode) within 2e-3.
 
 Cases: a new token's write followed by the decode, the fused decode step, and the decode
 that allocates nothing; each on the split grid (automatic and 128-token splits, the
-in-kernel combine) and on the balanced grid with its combine launch.
+in-kernel combine) and on the balanced grid with its combine launch.  And a chunk's write
+followed by its causal extend, in one split and in forced 128-token splits.
 """
 import numpy as np
 import pytest
@@ -168,3 +169,59 @@ def test_noalloc_decode(K, split):
                                                                split_tokens=split),
                         f"noalloc split={split}")
     _oracle_check(orc, paging, news[0], slots, L, out_e, f"graph noalloc split={split}")
+
+
+@pytest.mark.parametrize("split", [0, 128])
+def test_chunk_write_then_extend(K, split):
+    """A chunk of new tokens per sequence written, then its causal extend over prefix + chunk."""
+    import torch
+    import workloads as W
+    lens, news = [300, 129, 64, 1000], [100, 129, 33, 7]
+    rng = np.random.default_rng(4400 + split)
+    paging = W.assign_pages(np.random.default_rng(4401 + split), lens, P)
+    T = int(sum(lens))
+    k = W.make_rows(rng, T, HKV, W.OutlierSpec.random(rng, HKV))
+    v = W.make_rows(rng, T, HKV)
+    slots = np.concatenate([paging.slots(s, 0, int(L)) for s, L in enumerate(lens)]).astype(np.int32)
+    chunk = np.concatenate([np.arange(int(L) - n, int(L)) + off for L, n, off in
+                            zip(lens, news, np.concatenate([[0], np.cumsum(lens)[:-1]]))])
+    prefix = np.setdiff1d(np.arange(T), chunk)
+    caches = [K.PagedInt4Cache(paging.num_pages, HKV, P, KB, VB, fill=0) for _ in range(2)]
+    for c in caches:
+        K.kv_rotquant_write(c, bf16_dev(k[prefix]), bf16_dev(v[prefix]), to_dev(slots[prefix]))
+    gc, ec = caches
+    qo = np.concatenate([[0], np.cumsum(news)]).astype(np.int32)
+    q = W.f32_to_bf16_bits(rng.standard_normal((int(qo[-1]), HQ, 128)).astype(np.float32))
+    L = np.array(lens, np.int32)
+    d = dict(kc=bf16_dev(k[chunk]), vc=bf16_dev(v[chunk]), sc=to_dev(slots[chunk]), q=bf16_dev(q),
+             qo=to_dev(qo), tab=to_dev(paging.page_table()), L=to_dev(L))
+    maxlen, maxq = int(L.max()), int(max(news))
+
+    def ws():
+        n = K.kv_int4_paged_extend_workspace(gc, len(lens), HQ, int(qo[-1]), maxq, maxlen, split)
+        return torch.zeros(max(n, 16), dtype=torch.uint8, device="cuda")
+
+    ws_g, ws_e = ws(), ws()
+    K.kv_rotquant_write(ec, d["kc"], d["vc"], d["sc"])
+    out_e = K.kv_int4_paged_extend(ec, d["q"], d["qo"], d["tab"], d["L"], maxlen, maxq,
+                                   split_tokens=split, workspace=ws_e)
+    torch.cuda.synchronize()
+    out_g = torch.empty_like(out_e)
+    other = torch.empty_like(out_e)
+    q2 = torch.flip(d["q"], dims=[1]).contiguous()
+
+    def body():
+        K.kv_rotquant_write(gc, d["kc"], d["vc"], d["sc"])
+        K.kv_int4_paged_extend(gc, d["q"], d["qo"], d["tab"], d["L"], maxlen, maxq, out=out_g,
+                               split_tokens=split, workspace=ws_g)
+
+    g = _record(body)
+    _replay_and_compare(g, out_g, out_e, gc, ec,
+                        lambda: K.kv_int4_paged_extend(ec, q2, d["qo"], d["tab"], d["L"], maxlen, maxq,
+                                                       out=other, split_tokens=split, workspace=ws_e),
+                        f"chunk write+extend split={split}")
+    orc = oracle.Cache(paging.num_pages, HKV, P, fill=0)
+    oracle.write(orc, k, v, slots, KB, VB)
+    arrays = (orc.k_codes, orc.v_codes, orc.k_params, orc.v_params)
+    decode_compare(out_e.cpu().numpy(), oracle.extend(q, arrays, qo, paging.page_table(), L, HKV, P, KB, VB),
+                   f"graph chunk write+extend split={split}")
